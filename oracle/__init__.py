@@ -1,0 +1,150 @@
+"""CPU oracle for decode paged attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never loads it and
+it imports nothing from the product package: the two share no code.
+
+Contents
+--------
+``attention`` / ``attention_pairs``
+    ctypes front end of ``pa_oracle.c``: the plain fp64 definition (gather every
+    token through the block table, dense softmax with a max shift, weighted sum
+    of V) -- page 1 of the source pages, issue "ROCm gfx1200: PagedAttnOnline is
+    8.1x slower per call", section "Where to look"; page 2, PR "head_dim=128
+    decode arm", section "Correctness" (a CPU oracle at bf16, GQA 2, d=128).
+``brute``
+    an independent NumPy dense implementation and a ``decimal`` high-precision
+    one for tiny inputs; both pin the C oracle.
+``compare``
+    the NMSE / max-abs / bitwise comparator and its self-test (page 3, PR
+    "head_dim-128 arm for the warp-split-KV decode kernel", comparator
+    self-test paragraph).
+
+All arrays use bf16 *bits* (``uint16``) for bf16 data, so nothing here depends
+on a bf16 dtype in NumPy.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libpa_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``pa_oracle.c`` with gcc into ``libpa_oracle.so`` (in place)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(LIB_PATH)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    i32 = ctypes.c_int
+    common = [p, i64, i64, p, p, i64, i64, i64, i64, p, i64, p,
+              i32, i32, i32, i32, i32, ctypes.c_float]
+    lib.pa_oracle_f64.argtypes = common + [p, i32]
+    lib.pa_oracle_f64.restype = i32
+    lib.pa_oracle_f64_pairs.argtypes = common + [p, i64, p, i32]
+    lib.pa_oracle_f64_pairs.restype = i32
+    lib.pa_oracle_f64_mutant.argtypes = common + [p, i32, i32]
+    lib.pa_oracle_f64_mutant.restype = i32
+    lib.pa_oracle_num_mutants.argtypes = []
+    lib.pa_oracle_num_mutants.restype = i32
+    _lib = lib
+    return lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
+
+
+def _prep(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads):
+    q = np.asarray(q)
+    if q.dtype != np.uint16 or q.ndim != 3 or q.strides[2] != 2:
+        raise OracleError("q must be uint16 bf16 bits [B, Hq, D] with contiguous D")
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if c.dtype != np.uint16 or c.ndim != 4 or c.strides[3] != 2:
+            raise OracleError(f"{name} must be uint16 bf16 bits [NP, P, Hkv, D], D contiguous")
+    if k_cache.shape != v_cache.shape or k_cache.strides != v_cache.strides:
+        raise OracleError("k_cache and v_cache must share shape and strides")
+    B, Hq, D = q.shape
+    NP, P, Hkv, D2 = k_cache.shape
+    if D2 != D or Hkv != num_kv_heads or Hq % Hkv:
+        raise OracleError("inconsistent head geometry")
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.ndim != 2 or bt.shape[0] != B or ctx.shape != (B,):
+        raise OracleError("block_tables must be [B, MaxBlk] and context_lens [B]")
+    st = [s // 2 for s in k_cache.strides[:3]]
+    qst = [s // 2 for s in q.strides[:2]]
+    return q, bt, ctx, (B, Hq, D, NP, P, Hkv), st, qst
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def attention(q, k_cache, v_cache, block_tables, context_lens, scale,
+              num_kv_heads, threads: int | None = None, mutant: int = 0):
+    """fp64 output [B, Hq, D] of the plain definition.  ``scale`` is taken as
+    the fp32 value a caller would pass to the GPU and widened exactly."""
+    lib = _load()
+    q, bt, ctx, (B, Hq, D, NP, P, Hkv), st, qst = _prep(
+        q, k_cache, v_cache, block_tables, context_lens, num_kv_heads)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    n = threads or default_threads()
+    args = [_ptr(q), qst[0], qst[1], _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], NP,
+            _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale),
+            _ptr(out), n]
+    if mutant:
+        rc = lib.pa_oracle_f64_mutant(*args, mutant)
+    else:
+        rc = lib.pa_oracle_f64(*args)
+    if rc != 0:
+        raise OracleError(f"oracle returned {rc}")
+    return out
+
+
+def attention_pairs(q, k_cache, v_cache, block_tables, context_lens, scale,
+                    num_kv_heads, pairs, threads: int | None = None):
+    """fp64 rows [n, D] for the selected (b, h) pairs (an int array [n, 2])."""
+    lib = _load()
+    q, bt, ctx, (B, Hq, D, NP, P, Hkv), st, qst = _prep(
+        q, k_cache, v_cache, block_tables, context_lens, num_kv_heads)
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    out = np.zeros((pairs.shape[0], D), dtype=np.float64)
+    n = threads or default_threads()
+    rc = lib.pa_oracle_f64_pairs(
+        _ptr(q), qst[0], qst[1], _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], NP,
+        _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale),
+        _ptr(pairs), pairs.shape[0], _ptr(out), n)
+    if rc != 0:
+        raise OracleError(f"oracle returned {rc}")
+    return out
+
+
+def num_mutants() -> int:
+    return _load().pa_oracle_num_mutants()

@@ -1,0 +1,115 @@
+"""Comparator for bf16 outputs against an fp64 (or bf16) reference.
+
+Test infrastructure.  Reports, over one whole output tensor:
+
+* ``nmse``     = sum((y - r)^2) / sum(r^2) in fp64 (the pages' parity gate is
+                 NMSE <= 5e-4 against the CPU oracle -- page 2, PR
+                 "head_dim=128 decode arm", section "Correctness"; the pages do
+                 not define NMSE, this is the plain reading);
+* ``max_abs``  = max |y - r|;
+* ``bitwise``  = percentage of elements whose bf16 bits equal the reference
+                 rounded to bf16 (round to nearest, ties to even);
+* ``n_big``    = count of |r| >= 4, where the bf16 half-ULP (2^-6 = 0.0156)
+                 alone exceeds a 1e-2 max-abs bound;
+* ``worst``    = flat index of the largest |y - r|.
+
+``self_test`` repeats the pages' comparator self-test (page 3, PR
+"head_dim-128 arm for the warp-split-KV decode kernel", comparator self-test
+paragraph): a 1-ULP change in 3 of 2048 elements (offsets 5, 1024, 2047) must
+move bitwise agreement from 100% to 2045/2048 = 99.8535%.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+NMSE_TOL = 5e-4
+MAX_ABS_TOL = 1e-2
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round fp64 to the nearest bf16 (ties to even) in one rounding step.
+
+    bf16 keeps 8 significant bits: with x = m * 2^e, 0.5 <= |m| < 1, the
+    result is rint(m * 256) / 256 * 2^e (numpy's rint rounds ties to even).
+    Normal-range values only; zeros, infinities and NaN are passed through.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.rint(m * 256.0) / 256.0, e)
+    f = r.astype(np.float32)          # exact: r has 8 significant bits
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@dataclass
+class Report:
+    nmse: float
+    max_abs: float
+    bitwise: float
+    n_big: int
+    worst: int
+    n: int
+
+    def ok(self, nmse_tol=NMSE_TOL, max_abs_tol=MAX_ABS_TOL) -> bool:
+        return bool(np.isfinite(self.nmse) and self.nmse <= nmse_tol
+                    and self.max_abs <= max_abs_tol)
+
+    def __str__(self):
+        return (f"nmse={self.nmse:.3e} max_abs={self.max_abs:.3e} "
+                f"bitwise={self.bitwise:.4f}% n_big={self.n_big} worst={self.worst} n={self.n}")
+
+
+def compare(y_bits, ref) -> Report:
+    """``y_bits``: bf16 bits of the output under test.  ``ref``: fp64 values,
+    or bf16 bits (uint16) of another bf16 output."""
+    y_bits = np.asarray(y_bits, dtype=np.uint16).ravel()
+    ref = np.asarray(ref)
+    if ref.dtype == np.uint16:
+        r_bits = ref.ravel()
+        r = bf16_bits_to_f64(r_bits)
+    else:
+        r = ref.astype(np.float64).ravel()
+        r_bits = f64_to_bf16_bits(r)
+    if r.shape != y_bits.shape:
+        raise ValueError(f"shape mismatch {y_bits.shape} vs {r.shape}")
+    y = bf16_bits_to_f64(y_bits)
+    n = y.size
+    if n == 0:
+        return Report(0.0, 0.0, 100.0, 0, -1, 0)
+    d = y - r
+    den = float(np.sum(r * r))
+    num = float(np.sum(d * d))
+    nmse = num / den if den > 0 else (0.0 if num == 0 else float("inf"))
+    ad = np.abs(d)
+    if not np.all(np.isfinite(ad)):
+        worst = int(np.argmax(~np.isfinite(ad)))
+        return Report(float("inf"), float("inf"), float(np.mean(y_bits == r_bits) * 100),
+                      int(np.sum(np.abs(r) >= 4)), worst, n)
+    worst = int(np.argmax(ad))
+    return Report(nmse, float(ad[worst]), float(np.mean(y_bits == r_bits) * 100.0),
+                  int(np.sum(np.abs(r) >= 4.0)), worst, n)
+
+
+def bump_ulp(bits, offsets, ulps: int = 1) -> np.ndarray:
+    """Return a copy of bf16 bits with the given flat offsets moved by ``ulps``
+    units in the last place (away from zero)."""
+    out = np.array(bits, dtype=np.uint16, copy=True).ravel()
+    for o in offsets:
+        out[o] = np.uint16(int(out[o]) + ulps)
+    return out.reshape(np.shape(bits))
+
+
+def self_test(reference_bits) -> tuple[Report, Report]:
+    """The pages' comparator self-test on a 2048-element bf16 row set.
+    Returns (clean report, corrupted report)."""
+    ref = np.asarray(reference_bits, dtype=np.uint16).ravel()
+    assert ref.size == 2048
+    clean = compare(ref, ref)
+    bad = compare(bump_ulp(ref, (5, 1024, 2047)), ref)
+    return clean, bad

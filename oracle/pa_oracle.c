@@ -1,0 +1,264 @@
+/*
+ * pa_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * The plain, slow, fp64 CPU definition of single-query (decode) paged
+ * attention.  Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library; the product path never does.  It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * What it computes (page 1 of the source pages, issue "ROCm gfx1200:
+ * PagedAttnOnline is 8.1x slower per call...", section "Where to look": an
+ * online-softmax decode kernel reading an NHD KV cache through strides, with
+ * a device-side request lookup, i.e. a block table; page 2, PR "head_dim=128
+ * decode arm", section "Correctness": the CPU oracle at Qwen3 geometry, bf16,
+ * GQA 2, head_dim 128).  Online softmax and split-KV only reorder the sums of
+ * ordinary softmax attention, so the oracle is that plain definition:
+ *
+ *   for sequence b with L = context_lens[b] tokens and query head h,
+ *   g = floor(h / (Hq / Hkv))                    (grouped-query sharing)
+ *   token t lives in physical page  block_tables[b][floor(t / P)],
+ *                     slot          t mod P
+ *   x_t   = s * sum_i q[b][h][i] * K[page][slot][g][i]      (s = fp32 scale)
+ *   m     = max_t x_t
+ *   w_t   = exp(x_t - m),  Z = sum_t w_t
+ *   o[i]  = (sum_t w_t * V[page][slot][g][i]) / Z
+ *
+ * Readings where the pages are silent: L == 0 gives an all-zero row; the
+ * scale is the fp32 value the caller passes, widened exactly; there is no
+ * mask, window, soft-cap or positional term.  Sums run in ascending t and
+ * ascending i inside one (b, h) pair, so the result does not depend on the
+ * number of threads.
+ *
+ * Every input is read as exact bf16 bits widened to fp64.  Block-table
+ * entries of used pages are range-checked; bad input returns an error code.
+ *
+ * The "mutant" argument exists only so that a test can plant a known mistake
+ * in the oracle and show that the pins catch it.  0 is the definition.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL -1
+#define ORC_EPAGE -2
+#define ORC_ENOMEM -3
+
+typedef struct {
+    const uint16_t* q;
+    int64_t q_sb, q_sh;                 /* element strides of q [B][Hq][D]   */
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t s_page, s_slot, s_head;     /* element strides of the NHD pools  */
+    int64_t num_pages;
+    const int32_t* bt;
+    int64_t max_blk;
+    const int32_t* ctx;
+    int B, Hq, Hkv, D, P;
+    double scale;
+    int mutant;
+    /* work list */
+    const int32_t* pairs;               /* (b, h) pairs, or NULL = all       */
+    int64_t n_items;
+    double* out;                        /* [n_items][D]                      */
+    int status;
+} orc_args;
+
+typedef struct {
+    orc_args* a;
+    int64_t begin, end;
+    int status;
+} orc_slice;
+
+static double bf16_bits_to_f64(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* One output row o[b][h][0..D) following the definition above. */
+static int attend_row(const orc_args* a, int b, int h, double* o)
+{
+    const int D = a->D;
+    int64_t L = a->ctx[b];
+    for (int i = 0; i < D; ++i) o[i] = 0.0;
+    if (L <= 0) return ORC_OK;
+    if (L > a->max_blk * a->P) return ORC_EINVAL;
+
+    const int qg = a->Hq / a->Hkv;
+    int g = h / qg;
+    if (a->mutant == 1) g = h % a->Hkv;            /* wrong head map          */
+
+    const uint16_t* qrow = a->q + (int64_t)b * a->q_sb + (int64_t)h * a->q_sh;
+    double* x = (double*)malloc((size_t)L * sizeof(double));
+    const uint16_t** vrows = (const uint16_t**)malloc((size_t)L * sizeof(void*));
+    if (!x || !vrows) { free(x); free(vrows); return ORC_ENOMEM; }
+
+    for (int64_t t = 0; t < L; ++t) {
+        int64_t lp = t / a->P, slot = t % a->P;
+        if (a->mutant == 2) slot = (t + 1) % a->P;        /* off-by-one slot */
+        if (lp >= a->max_blk) { free(x); free(vrows); return ORC_EPAGE; }
+        int64_t page = a->bt[(int64_t)b * a->max_blk + lp];
+        if (a->mutant == 8) page = a->bt[lp];             /* batch row lost  */
+        if (page < 0 || page >= a->num_pages) { free(x); free(vrows); return ORC_EPAGE; }
+        int64_t off = page * a->s_page + slot * a->s_slot + (int64_t)g * a->s_head;
+        const uint16_t* krow = a->k + off;
+        vrows[t] = a->v + off;
+        if (a->mutant == 5) vrows[t] = a->k + off; /* K used in place of V    */
+        double dot = 0.0;
+        for (int i = 0; i < D; ++i) {
+            double qi = bf16_bits_to_f64(qrow[i]);
+            double ki = bf16_bits_to_f64(krow[i]);
+            if (a->mutant == 6 && i == D - 1) ki = 0.0;   /* dropped term    */
+            dot += qi * ki;
+        }
+        x[t] = a->scale * dot;
+        if (a->mutant == 3) x[t] = dot;                   /* scale ignored   */
+        if (a->mutant == 4) x[t] = -a->scale * dot;       /* wrong sign      */
+    }
+
+    double m = x[0];
+    for (int64_t t = 1; t < L; ++t) if (x[t] > m) m = x[t];
+    double Z = 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        x[t] = exp(x[t] - m);                             /* x now holds w_t */
+        Z += x[t];
+    }
+    int64_t t_end = L;
+    if (a->mutant == 7) t_end = L - 1;                    /* last token lost */
+    for (int64_t t = 0; t < t_end; ++t) {
+        const uint16_t* vrow = vrows[t];
+        for (int i = 0; i < D; ++i) o[i] += x[t] * bf16_bits_to_f64(vrow[i]);
+    }
+    for (int i = 0; i < D; ++i) o[i] /= Z;
+
+    free(x);
+    free(vrows);
+    return ORC_OK;
+}
+
+static void* run_slice(void* p)
+{
+    orc_slice* s = (orc_slice*)p;
+    const orc_args* a = s->a;
+    s->status = ORC_OK;
+    for (int64_t it = s->begin; it < s->end; ++it) {
+        int b, h;
+        if (a->pairs) { b = a->pairs[2 * it]; h = a->pairs[2 * it + 1]; }
+        else { b = (int)(it / a->Hq); h = (int)(it % a->Hq); }
+        if (b < 0 || b >= a->B || h < 0 || h >= a->Hq) { s->status = ORC_EINVAL; return NULL; }
+        int rc = attend_row(a, b, h, a->out + it * a->D);
+        if (rc != ORC_OK) { s->status = rc; return NULL; }
+    }
+    return NULL;
+}
+
+static int run(orc_args* a, int n_threads)
+{
+    if (!a->q || !a->k || !a->v || !a->bt || !a->ctx || !a->out) return ORC_EINVAL;
+    if (a->B < 0 || a->Hq <= 0 || a->Hkv <= 0 || a->D <= 0 || a->P <= 0) return ORC_EINVAL;
+    if (a->Hq % a->Hkv != 0) return ORC_EINVAL;
+    if (a->n_items == 0) return ORC_OK;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > a->n_items) n_threads = (int)a->n_items;
+
+    orc_slice* sl = (orc_slice*)calloc((size_t)n_threads, sizeof *sl);
+    pthread_t* th = (pthread_t*)calloc((size_t)n_threads, sizeof *th);
+    if (!sl || !th) { free(sl); free(th); return ORC_ENOMEM; }
+    int64_t per = (a->n_items + n_threads - 1) / n_threads;
+    int started = 0;
+    for (int i = 0; i < n_threads; ++i) {
+        sl[i].a = a;
+        sl[i].begin = (int64_t)i * per;
+        sl[i].end = sl[i].begin + per < a->n_items ? sl[i].begin + per : a->n_items;
+        if (sl[i].begin >= sl[i].end) continue;
+        if (i == n_threads - 1 || pthread_create(&th[i], NULL, run_slice, &sl[i]) != 0) {
+            run_slice(&sl[i]);          /* last slice (or a failed spawn) inline */
+            sl[i].begin = -1;
+        } else {
+            ++started;
+        }
+    }
+    int rc = ORC_OK;
+    for (int i = 0; i < n_threads; ++i) {
+        if (sl[i].begin >= 0 && sl[i].begin < sl[i].end) pthread_join(th[i], NULL);
+        if (sl[i].status != ORC_OK && rc == ORC_OK) rc = sl[i].status;
+    }
+    (void)started;
+    free(sl);
+    free(th);
+    return rc;
+}
+
+static void fill(orc_args* a,
+                 const uint16_t* q, int64_t q_sb, int64_t q_sh,
+                 const uint16_t* k, const uint16_t* v,
+                 int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                 const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                 int B, int Hq, int Hkv, int D, int P, float scale)
+{
+    memset(a, 0, sizeof *a);
+    a->q = q; a->q_sb = q_sb; a->q_sh = q_sh;
+    a->k = k; a->v = v;
+    a->s_page = s_page; a->s_slot = s_slot; a->s_head = s_head;
+    a->num_pages = num_pages;
+    a->bt = bt; a->max_blk = max_blk; a->ctx = ctx;
+    a->B = B; a->Hq = Hq; a->Hkv = Hkv; a->D = D; a->P = P;
+    a->scale = (double)scale;
+}
+
+/* Every (b, h) row: out is [B][Hq][D] fp64. */
+int pa_oracle_f64(const uint16_t* q, int64_t q_sb, int64_t q_sh,
+                  const uint16_t* k, const uint16_t* v,
+                  int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                  const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                  int B, int Hq, int Hkv, int D, int P, float scale,
+                  double* out, int n_threads)
+{
+    orc_args a;
+    fill(&a, q, q_sb, q_sh, k, v, s_page, s_slot, s_head, num_pages, bt, max_blk, ctx,
+         B, Hq, Hkv, D, P, scale);
+    a.out = out;
+    a.n_items = (int64_t)B * Hq;
+    return run(&a, n_threads);
+}
+
+/* Selected rows: pairs holds n_pairs (b, h) int32 pairs; out is [n_pairs][D]. */
+int pa_oracle_f64_pairs(const uint16_t* q, int64_t q_sb, int64_t q_sh,
+                        const uint16_t* k, const uint16_t* v,
+                        int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                        const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                        int B, int Hq, int Hkv, int D, int P, float scale,
+                        const int32_t* pairs, int64_t n_pairs, double* out, int n_threads)
+{
+    orc_args a;
+    fill(&a, q, q_sb, q_sh, k, v, s_page, s_slot, s_head, num_pages, bt, max_blk, ctx,
+         B, Hq, Hkv, D, P, scale);
+    a.out = out;
+    a.pairs = pairs;
+    a.n_items = n_pairs;
+    return run(&a, n_threads);
+}
+
+/* As pa_oracle_f64 with a planted mistake (tests of the pins only). */
+int pa_oracle_f64_mutant(const uint16_t* q, int64_t q_sb, int64_t q_sh,
+                         const uint16_t* k, const uint16_t* v,
+                         int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                         const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                         int B, int Hq, int Hkv, int D, int P, float scale,
+                         double* out, int n_threads, int mutant)
+{
+    orc_args a;
+    fill(&a, q, q_sb, q_sh, k, v, s_page, s_slot, s_head, num_pages, bt, max_blk, ctx,
+         B, Hq, Hkv, D, P, scale);
+    a.out = out;
+    a.n_items = (int64_t)B * Hq;
+    a.mutant = mutant;
+    return run(&a, n_threads);
+}
+
+int pa_oracle_num_mutants(void) { return 8; }

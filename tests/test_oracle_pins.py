@@ -1,0 +1,302 @@
+"""Pins of the CPU oracle against things other than itself (no GPU).
+
+Each pin follows something the source pages or plain mathematics fix:
+
+* brute force: an independent NumPy dense evaluation (library softmax, page
+  gather by fancy indexing) and a 50-digit ``decimal`` evaluation;
+* physical-page relabelling leaves the result bit-identical (the block table
+  is the only link between logical tokens and pages -- page 1, issue "ROCm
+  gfx1200: PagedAttnOnline is 8.1x slower per call", section "Where to look");
+* ctx = 1 returns the V row exactly; uniform keys, or scale 0, give the mean
+  of the V rows; L = 2 has the closed form sigma(x0 - x1) v0 + sigma(x1 - x0) v1;
+* grouped-query attention equals multi-head attention over KV heads copied
+  qg times (the head map g = floor(h / qg));
+* reordering the logical tokens (K and V rows together) changes nothing
+  beyond rounding: softmax attention has no positional term here;
+* context lengths straddling the page boundary, 1/31/32/33/64/100/685/1000
+  at page 32 (page 3, PR "head_dim-128 arm for the warp-split-KV decode
+  kernel", numerics table) and 15/16/17 at page 16;
+* every planted mistake in the oracle (wrong head map, off-by-one slot, lost
+  scale, flipped sign, K read for V, dropped term, lost token, lost batch
+  row) is caught by the brute-force pin.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from workloads import round_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(rng, shape, scale=1.0):
+    return round_bf16(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+def random_case(rng, B, Hq, Hkv, D, P, lens, extra_pages=3):
+    lens = np.asarray(lens, dtype=np.int32)
+    n_b = (lens + P - 1) // P
+    NP = int(n_b.sum()) + extra_pages
+    perm = rng.permutation(NP)
+    mb = max(int(n_b.max()), 1)
+    bt = np.full((B, mb), -1, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        bt[b, :n_b[b]] = perm[pos:pos + n_b[b]]
+        pos += n_b[b]
+    q = bf16(rng, (B, Hq, D))
+    k = bf16(rng, (NP, P, Hkv, D))
+    v = bf16(rng, (NP, P, Hkv, D))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    return dict(q=q, k_cache=k, v_cache=v, block_tables=bt, context_lens=lens,
+                scale=scale, num_kv_heads=Hkv)
+
+
+def run_oracle(c, **kw):
+    return oracle.attention(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                            c["context_lens"], c["scale"], c["num_kv_heads"], **kw)
+
+
+def run_dense(c):
+    return brute.dense(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                       c["context_lens"], c["scale"], c["num_kv_heads"])
+
+
+def rel_err(a, b):
+    den = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+# --------------------------------------------------------------------------
+# brute force
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (4, 2), (8, 2), (8, 8), (4, 1)])
+@pytest.mark.parametrize("P", [1, 3, 16, 32])
+def test_matches_dense_bruteforce(Hq, Hkv, P):
+    rng = np.random.default_rng(1000 * Hq + 10 * Hkv + P)
+    lens = rng.integers(1, 101, 4)
+    c = random_case(rng, 4, Hq, Hkv, 32, P, lens)
+    assert rel_err(run_oracle(c), run_dense(c)) <= 1e-12
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_matches_dense_bruteforce_full_head_dim(D):
+    rng = np.random.default_rng(D)
+    c = random_case(rng, 3, 8, 2, D, 16, [5, 40, 77])
+    assert rel_err(run_oracle(c), run_dense(c)) <= 1e-12
+
+
+def test_matches_decimal_exact():
+    rng = np.random.default_rng(7)
+    c = random_case(rng, 2, 4, 2, 8, 2, [3, 5])
+    ref = brute.exact(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                      c["context_lens"], c["scale"], c["num_kv_heads"])
+    # fp64 evaluation of a short sum: error is a few ulps of the largest term
+    assert rel_err(run_oracle(c), ref) <= 1e-14
+
+
+def test_golden_exact_fixture():
+    """Stored 50-digit decimal results written by tests/golden/make_golden.py
+    (which calls only oracle.brute.exact)."""
+    with open(os.path.join(GOLDEN, "tiny_exact.json")) as f:
+        g = json.load(f)
+    c = dict(q=np.array(g["q"], dtype=np.uint16),
+             k_cache=np.array(g["k_cache"], dtype=np.uint16),
+             v_cache=np.array(g["v_cache"], dtype=np.uint16),
+             block_tables=np.array(g["block_tables"], dtype=np.int32),
+             context_lens=np.array(g["context_lens"], dtype=np.int32),
+             scale=g["scale"], num_kv_heads=g["num_kv_heads"])
+    expect = np.array(g["expected"], dtype=np.float64)
+    assert rel_err(run_oracle(c), expect) <= 1e-14
+
+
+# --------------------------------------------------------------------------
+# invariants and special cases
+# --------------------------------------------------------------------------
+def test_page_relabelling_bitwise():
+    rng = np.random.default_rng(11)
+    c = random_case(rng, 3, 8, 4, 64, 16, [17, 50, 33], extra_pages=5)
+    base = run_oracle(c)
+    NP = c["k_cache"].shape[0]
+    pi = rng.permutation(NP)               # old page p moves to pi[p]
+    k2 = np.empty_like(c["k_cache"]); k2[pi] = c["k_cache"]
+    v2 = np.empty_like(c["v_cache"]); v2[pi] = c["v_cache"]
+    bt = c["block_tables"]
+    bt2 = np.where(bt >= 0, pi[np.maximum(bt, 0)], -1).astype(np.int32)
+    c2 = dict(c, k_cache=k2, v_cache=v2, block_tables=bt2)
+    assert np.array_equal(run_oracle(c2), base)
+
+
+def test_ctx1_returns_v_row():
+    rng = np.random.default_rng(12)
+    c = random_case(rng, 4, 8, 2, 128, 32, [1, 1, 1, 1])
+    out = run_oracle(c)
+    vf = brute.bf16_bits_to_f64(c["v_cache"])
+    for b in range(4):
+        for h in range(8):
+            assert np.array_equal(out[b, h], vf[c["block_tables"][b, 0], 0, h // 4])
+
+
+def test_uniform_keys_give_mean_of_v():
+    rng = np.random.default_rng(13)
+    c = random_case(rng, 2, 4, 2, 32, 8, [37, 64])
+    k = c["k_cache"].copy()
+    k[:] = k[0, 0]                           # every K row identical
+    c = dict(c, k_cache=k)
+    out = run_oracle(c)
+    vf = brute.bf16_bits_to_f64(c["v_cache"])
+    for b, L in enumerate(c["context_lens"]):
+        rows = np.array([vf[c["block_tables"][b, t // 8], t % 8] for t in range(L)])
+        for h in range(4):
+            assert rel_err(out[b, h], rows[:, h // 2].mean(axis=0)) <= 1e-12
+
+
+def test_zero_scale_gives_mean_of_v():
+    rng = np.random.default_rng(14)
+    c = random_case(rng, 2, 2, 1, 16, 4, [9, 3])
+    c["scale"] = 0.0
+    out = run_oracle(c)
+    vf = brute.bf16_bits_to_f64(c["v_cache"])
+    for b, L in enumerate(c["context_lens"]):
+        rows = np.array([vf[c["block_tables"][b, t // 4], t % 4, 0] for t in range(L)])
+        assert rel_err(out[b, 0], rows.mean(axis=0)) <= 1e-12
+
+
+def test_closed_form_two_tokens():
+    rng = np.random.default_rng(15)
+    c = random_case(rng, 1, 1, 1, 16, 1, [2])
+    out = run_oracle(c)[0, 0]
+    qf = brute.bf16_bits_to_f64(c["q"])[0, 0]
+    kf = brute.bf16_bits_to_f64(c["k_cache"])
+    vf = brute.bf16_bits_to_f64(c["v_cache"])
+    p0, p1 = c["block_tables"][0]
+    x0 = float(np.dot(qf, kf[p0, 0, 0])) * c["scale"]
+    x1 = float(np.dot(qf, kf[p1, 0, 0])) * c["scale"]
+    sig = lambda z: 1.0 / (1.0 + np.exp(-z))
+    expect = sig(x0 - x1) * vf[p0, 0, 0] + sig(x1 - x0) * vf[p1, 0, 0]
+    assert rel_err(out, expect) <= 1e-13
+
+
+def test_gqa_equals_mha_with_copied_heads():
+    rng = np.random.default_rng(16)
+    Hq, Hkv = 8, 2
+    c = random_case(rng, 2, Hq, Hkv, 32, 8, [19, 40])
+    qg = Hq // Hkv
+    k_mha = np.repeat(c["k_cache"], qg, axis=2)      # KV head g copied to g*qg..g*qg+qg-1
+    v_mha = np.repeat(c["v_cache"], qg, axis=2)
+    c_mha = dict(c, k_cache=np.ascontiguousarray(k_mha),
+                 v_cache=np.ascontiguousarray(v_mha), num_kv_heads=Hq)
+    assert np.array_equal(run_oracle(c_mha), run_oracle(c))
+
+
+def test_logical_token_permutation():
+    rng = np.random.default_rng(17)
+    P = 4
+    c = random_case(rng, 1, 4, 2, 32, P, [23], extra_pages=0)
+    L = 23
+    sigma = rng.permutation(L)
+    k, v = c["k_cache"].copy(), c["v_cache"].copy()
+    bt = c["block_tables"][0]
+    for t in range(L):
+        s = sigma[t]
+        k[bt[t // P], t % P] = c["k_cache"][bt[s // P], s % P]
+        v[bt[t // P], t % P] = c["v_cache"][bt[s // P], s % P]
+    assert rel_err(run_oracle(dict(c, k_cache=k, v_cache=v)), run_oracle(c)) <= 1e-12
+
+
+@pytest.mark.parametrize("P,lens", [(32, [1, 31, 32, 33, 64, 100, 685, 1000]),
+                                    (16, [15, 16, 17])])
+def test_page_boundary_sweep(P, lens):
+    rng = np.random.default_rng(P)
+    c = random_case(rng, len(lens), 16, 8, 128, P, lens)
+    assert rel_err(run_oracle(c), run_dense(c)) <= 1e-12
+
+
+def test_empty_sequence_gives_zeros():
+    rng = np.random.default_rng(18)
+    c = random_case(rng, 3, 4, 2, 16, 4, [5, 0, 9])
+    out = run_oracle(c)
+    assert np.all(out[1] == 0.0)
+    assert rel_err(out, run_dense(c)) <= 1e-12
+
+
+def test_thread_count_does_not_change_bits():
+    rng = np.random.default_rng(19)
+    c = random_case(rng, 5, 8, 2, 64, 16, [100, 3, 64, 77, 1])
+    assert np.array_equal(run_oracle(c, threads=1), run_oracle(c, threads=7))
+
+
+def test_pairs_entry_matches_full():
+    rng = np.random.default_rng(20)
+    c = random_case(rng, 3, 8, 2, 32, 16, [40, 1, 17])
+    full = run_oracle(c)
+    pairs = np.array([[2, 7], [0, 0], [1, 3]], dtype=np.int32)
+    rows = oracle.attention_pairs(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                                  c["context_lens"], c["scale"], 2, pairs)
+    for i, (b, h) in enumerate(pairs):
+        assert np.array_equal(rows[i], full[b, h])
+
+
+def test_bad_page_id_is_an_error_not_a_crash():
+    rng = np.random.default_rng(21)
+    c = random_case(rng, 1, 2, 1, 16, 4, [6])
+    bt = c["block_tables"].copy()
+    bt[0, 1] = 10_000
+    with pytest.raises(oracle.OracleError):
+        run_oracle(dict(c, block_tables=bt))
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: every mutant must be caught
+# --------------------------------------------------------------------------
+def test_every_planted_mistake_is_caught():
+    rng = np.random.default_rng(22)
+    c = random_case(rng, 3, 8, 2, 16, 4, [1, 7, 13])
+    ref = run_dense(c)
+    assert rel_err(run_oracle(c), ref) <= 1e-12
+    for m in range(1, oracle.num_mutants() + 1):
+        try:
+            out = run_oracle(c, mutant=m)
+        except oracle.OracleError:
+            continue                        # an error is also a catch
+        assert rel_err(out, ref) > 1e-6, f"mutant {m} slipped through"
+
+
+# --------------------------------------------------------------------------
+# comparator
+# --------------------------------------------------------------------------
+def test_comparator_selftest_matches_pages():
+    """1-ULP corruption of 3 of 2048 elements -> 99.8535% bitwise (the pages'
+    figure), and a gross corruption fails the NMSE gate."""
+    from oracle import compare
+    with open(os.path.join(GOLDEN, "comparator_selftest.json")) as f:
+        g = json.load(f)
+    rng = np.random.default_rng(23)
+    ref = round_bf16(rng.standard_normal(2048).astype(np.float32) * 0.3)
+    clean, bad = compare.self_test(ref)
+    assert clean.bitwise == 100.0 and clean.max_abs == 0.0
+    assert round(bad.bitwise, 4) == g["bitwise_after_percent"]
+    assert bad.worst in g["offsets"]
+    gross = compare.compare(round_bf16(rng.standard_normal(2048).astype(np.float32)), ref)
+    assert not gross.ok()
+
+
+def test_bf16_rounding_helpers_agree_with_torch():
+    import torch
+    from oracle import compare
+    rng = np.random.default_rng(24)
+    x = (rng.standard_normal(100_000) * np.exp(rng.uniform(-20, 20, 100_000))).astype(np.float32)
+    x[:4] = [1.0 + 2**-8, 1.0 + 3 * 2**-8, -(1.0 + 2**-8), 0.0]   # exact ties
+    t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(round_bf16(x), t)
+    assert np.array_equal(compare.f64_to_bf16_bits(x.astype(np.float64)), t)
