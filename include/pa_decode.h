@@ -1,0 +1,218 @@
+/*
+ * pa_decode.h -- C ABI of the MI355X (gfx950) decode paged-attention library.
+ *
+ * One operation: single-query (decode) attention of every sequence's newest
+ * query over that sequence's keys and values, read page by page from an NHD
+ * paged KV cache through a block table.
+ *
+ *   Source: page 1 of the source pages, issue "ROCm gfx1200: PagedAttnOnline
+ *   is 8.1x slower per call than vLLM's paged-attention kernel", section
+ *   "Where to look" (online softmax, NHD KV addressed through strides,
+ *   device-side request lookup); page 2, PR "head_dim=128 decode arm", section
+ *   "Correctness" (bf16, grouped-query attention, head_dim 128); page 3, PR
+ *   "head_dim-128 arm for the warp-split-KV decode kernel" (split-KV decode,
+ *   the numerics table's 32-token pages).
+ *
+ * For sequence b (L = context_lens[b] tokens) and query head h, with
+ * qg = num_q_heads / num_kv_heads and g = h / qg:
+ *
+ *   token t is stored at  page = block_tables[b][t / page_size],
+ *                         slot = t % page_size,
+ *   x_t  = scale * dot(q[b][h][:], k_cache[page][slot][g][:])
+ *   out[b][h][:] = sum_t softmax(x)_t * v_cache[page][slot][g][:]
+ *
+ * computed with fp32 arithmetic (online softmax, fp32 accumulation) and
+ * written as bf16 rounded to nearest even.  L == 0 writes zeros.  There is no
+ * mask, window or positional term.
+ *
+ * All functions are plain C, never throw, and make no HIP call before their
+ * arguments have been validated.  Calls are asynchronous on the given stream:
+ * a PA_OK return means the work was enqueued; device faults surface at the
+ * caller's next synchronisation.  The library keeps no reference to caller
+ * memory after a call returns, but the caller must keep every tensor alive
+ * until the enqueued work has finished.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- errors */
+#define PA_OK       0  /* success                                                  */
+#define PA_EINVAL   1  /* null pointer, bad shape/dtype/stride, Hq % Hkv != 0,
+                          non-finite scale, page_size < 1                          */
+#define PA_ENOTSUP  2  /* head_dim not 128/256, or Hq/Hkv not 1, 2, 4, 8 or 16      */
+#define PA_EALIGN   3  /* a base pointer or a row stride not 16-byte aligned       */
+#define PA_ENODEV   4  /* no HIP device available                                  */
+#define PA_ENOMEM   5  /* workspace could not be allocated, or is too small        */
+#define PA_EHIP     6  /* a HIP runtime call failed; text in pa_last_error()        */
+
+/* ---------------------------------------------------------------- tensors */
+#define PA_DTYPE_BF16  1
+#define PA_DTYPE_INT32 2
+#define PA_DTYPE_FP32  3
+
+/*
+ * A strided view of device memory.  shape[] and stride[] are in elements;
+ * entries at index >= ndim are ignored.  The library only reads the
+ * descriptor during the call.
+ */
+typedef struct pa_tensor {
+    void*   data;       /* device pointer                                    */
+    int32_t dtype;      /* PA_DTYPE_*                                        */
+    int32_t ndim;
+    int64_t shape[4];
+    int64_t stride[4];
+} pa_tensor;
+
+/*
+ * pa_decode -- enqueue one decode paged-attention call.
+ *
+ *  q             [B, Hq, D]        bf16; stride[2] == 1; stride[0], stride[1]
+ *                                  multiples of 8 (16 bytes).
+ *  k_cache       [NP, P, Hkv, D]   bf16 NHD pool: page, slot, KV head, dim;
+ *                                  stride[3] == 1, other strides multiples of
+ *                                  8 elements.  Pages may lie anywhere in the
+ *                                  pool: block_tables gives the order.
+ *  v_cache       same shape as k_cache (its own strides, same rules).
+ *  block_tables  [B, MaxBlk]       int32, stride[1] == 1.  Entry j of row b is
+ *                                  the physical page of tokens
+ *                                  [j*P, (j+1)*P) of sequence b.  Entries at
+ *                                  or past ceil(L_b / P) are never read and
+ *                                  may hold anything (e.g. -1).
+ *  context_lens  [B]               int32, stride[0] == 1.  L_b tokens.
+ *  scale         fp32 multiplier of the logits (normally 1/sqrt(D)).
+ *  num_q_heads, num_kv_heads, head_dim, page_size
+ *                must equal q.shape[1], k_cache.shape[2], q.shape[2] and
+ *                k_cache.shape[1].
+ *  out           [B, Hq, D]        bf16, stride[2] == 1, 16-byte aligned rows.
+ *  stream        hipStream_t to enqueue on; NULL is the null stream.
+ *
+ * Device-side preconditions, not checked on the host (the host never reads
+ * device memory): 0 <= L_b <= MaxBlk * P and every used block-table entry is
+ * in [0, NP).  The kernels clamp L_b into [0, MaxBlk * P] and page ids into
+ * [0, NP), so a violation gives unspecified output, never an out-of-range
+ * access.
+ *
+ * Long contexts are split into partitions whose partial results are merged
+ * by a second kernel (log-sum-exp merge); the library keeps a per-device
+ * workspace for those partials, grown on demand with hipMalloc and freed by
+ * pa_release().  Returns PA_OK or an error code above.
+ */
+int pa_decode(const pa_tensor* q,
+              const pa_tensor* k_cache,
+              const pa_tensor* v_cache,
+              const pa_tensor* block_tables,
+              const pa_tensor* context_lens,
+              float scale,
+              int num_q_heads,
+              int num_kv_heads,
+              int head_dim,
+              int page_size,
+              const pa_tensor* out,
+              void* stream);
+
+/* ---------------------------------------------------------------- options */
+#define PA_VARIANT_AUTO  0   /* the library picks                              */
+#define PA_VARIANT_VALU  1   /* vector-ALU kernel (any supported qg)            */
+#define PA_VARIANT_MFMA  2   /* matrix-core kernel (bf16 MFMA for Q.K and P.V)  */
+
+typedef struct pa_opts {
+    int32_t variant;            /* PA_VARIANT_*                                */
+    int32_t partition_tokens;   /* 0 = automatic; else tokens per split-KV
+                                   partition, a multiple of 64 (rounded up).
+                                   A value >= MaxBlk * P disables the split.   */
+    int32_t reserved[6];        /* must be zero                                */
+} pa_opts;
+
+/*
+ * Bytes of workspace pa_decode_ex needs for a call with these sizes and
+ * options (0 when the call does not split).  max_blocks_per_seq is
+ * block_tables.shape[1].  Returns 0 on bad arguments as well.
+ */
+size_t pa_decode_workspace_bytes(int64_t num_seqs, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int64_t max_blocks_per_seq, int page_size,
+                                 const pa_opts* opts);
+
+/*
+ * pa_decode_ex -- pa_decode with options and caller-owned workspace.
+ * opts may be NULL (automatic).  workspace is a device buffer of at least
+ * pa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the caller
+ * and in use until the enqueued work finishes; if workspace is NULL the
+ * library's own per-device workspace is used (as in pa_decode).  Returns
+ * PA_ENOMEM if the given workspace is too small.
+ */
+int pa_decode_ex(const pa_tensor* q,
+                 const pa_tensor* k_cache,
+                 const pa_tensor* v_cache,
+                 const pa_tensor* block_tables,
+                 const pa_tensor* context_lens,
+                 float scale,
+                 int num_q_heads,
+                 int num_kv_heads,
+                 int head_dim,
+                 int page_size,
+                 const pa_tensor* out,
+                 void* stream,
+                 const pa_opts* opts,
+                 void* workspace,
+                 size_t workspace_bytes);
+
+/*
+ * pa_check_args -- run only the host-side validation of pa_decode_ex and
+ * return the code it would return before touching the GPU (PA_OK if the
+ * arguments are acceptable).  Makes no HIP call.
+ */
+int pa_check_args(const pa_tensor* q,
+                  const pa_tensor* k_cache,
+                  const pa_tensor* v_cache,
+                  const pa_tensor* block_tables,
+                  const pa_tensor* context_lens,
+                  float scale,
+                  int num_q_heads,
+                  int num_kv_heads,
+                  int head_dim,
+                  int page_size,
+                  const pa_tensor* out,
+                  const pa_opts* opts);
+
+/* ----------------------------------------------------- introspection */
+/* Launch counters since load or the last pa_reset_stats (process-wide). */
+typedef struct pa_stats {
+    uint64_t calls;             /* successful pa_decode / pa_decode_ex calls   */
+    uint64_t valu_launches;     /* decode-kernel launches, vector-ALU variant  */
+    uint64_t mfma_launches;     /* decode-kernel launches, MFMA variant        */
+    uint64_t split_calls;       /* calls that split the context                */
+    uint64_t merge_launches;    /* log-sum-exp merge kernel launches           */
+    uint64_t last_partition_tokens; /* partition size of the last call         */
+    uint64_t last_num_partitions;   /* partitions of the last call (grid x)    */
+    uint64_t last_variant;          /* PA_VARIANT_* of the last call           */
+} pa_stats;
+
+int  pa_get_stats(pa_stats* stats);   /* PA_EINVAL if stats is NULL            */
+void pa_reset_stats(void);
+
+/* Static text for an error code; never NULL. */
+const char* pa_strerror(int code);
+
+/* Detail of the calling thread's last error ("" if none); valid until the
+ * thread's next call into the library. */
+const char* pa_last_error(void);
+
+/* Free the library-owned workspaces of all devices.  Synchronises each device
+ * that has one.  Returns PA_OK or PA_EHIP. */
+int pa_release(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,232 @@
+"""ctypes binding of ``libpa_decode.so`` (the C ABI in ``include/pa_decode.h``).
+
+Argument marshalling only: torch tensors become ``pa_tensor`` descriptors
+(data pointer, dtype, shape, strides) and the current HIP stream is passed
+through.  Every step of the computation runs in the library's gfx950 kernels;
+there is no fallback of any kind.  If the library is missing, importing the
+package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
+
+PA_OK, PA_EINVAL, PA_ENOTSUP, PA_EALIGN, PA_ENODEV, PA_ENOMEM, PA_EHIP = range(7)
+PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32 = 1, 2, 3
+PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
+VARIANTS = {"auto": PA_VARIANT_AUTO, "valu": PA_VARIANT_VALU, "mfma": PA_VARIANT_MFMA}
+
+
+class PaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class PaOpts(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+class PaStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
+        "last_partition_tokens", "last_num_partitions", "last_variant")]
+
+
+class PaError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code}): {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_attention_decode_04_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    T = ctypes.POINTER(PaTensor)
+    args12 = [T, T, T, T, T, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+              ctypes.c_int, T]
+    lib.pa_decode.argtypes = args12 + [ctypes.c_void_p]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_ex.argtypes = args12 + [ctypes.c_void_p, ctypes.POINTER(PaOpts),
+                                          ctypes.c_void_p, ctypes.c_size_t]
+    lib.pa_decode_ex.restype = ctypes.c_int
+    lib.pa_check_args.argtypes = args12 + [ctypes.POINTER(PaOpts)]
+    lib.pa_check_args.restype = ctypes.c_int
+    lib.pa_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.POINTER(PaOpts)]
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_get_stats.argtypes = [ctypes.POINTER(PaStats)]
+    lib.pa_get_stats.restype = ctypes.c_int
+    lib.pa_reset_stats.argtypes = []
+    lib.pa_reset_stats.restype = None
+    lib.pa_strerror.argtypes = [ctypes.c_int]
+    lib.pa_strerror.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_release.argtypes = []
+    lib.pa_release.restype = ctypes.c_int
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def strerror(code: int) -> str:
+    return LIB.pa_strerror(code).decode()
+
+
+def last_error() -> str:
+    return LIB.pa_last_error().decode()
+
+
+def version() -> str:
+    return LIB.pa_version().decode()
+
+
+def _check(rc: int, where: str):
+    if rc != PA_OK:
+        raise PaError(rc, where, last_error())
+
+
+# ------------------------------------------------------------------ marshalling
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.bfloat16: PA_DTYPE_BF16, torch.int32: PA_DTYPE_INT32,
+            torch.float32: PA_DTYPE_FP32}.get(t.dtype, 0)
+
+
+def tensor_desc(t) -> PaTensor:
+    """pa_tensor describing a torch tensor (no copy; shape/strides in elements)."""
+    d = PaTensor()
+    d.data = t.data_ptr()
+    d.dtype = _dtype_code(t)
+    d.ndim = t.dim()
+    for i, (n, s) in enumerate(zip(t.shape, t.stride())):
+        if i < 4:
+            d.shape[i] = n
+            d.stride[i] = s
+    return d
+
+
+def _require_device(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must live on the same GPU device")
+
+
+def make_opts(variant="auto", partition_tokens: int = 0) -> PaOpts:
+    o = PaOpts()
+    o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    o.partition_tokens = int(partition_tokens)
+    return o
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ------------------------------------------------------------------ C-ABI mirror
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+              num_kv_heads, head_dim, page_size, out, stream=None):
+    """Same arguments as the C function; tensors are torch tensors on one GPU.
+    Uses the library's own split-KV workspace."""
+    import torch
+    _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
+    with torch.cuda.device(q.device):
+        rc = LIB.pa_decode(tensor_desc(q), tensor_desc(k_cache), tensor_desc(v_cache),
+                           tensor_desc(block_tables), tensor_desc(context_lens), float(scale),
+                           num_q_heads, num_kv_heads, head_dim, page_size, tensor_desc(out),
+                           _stream_handle(stream, q.device))
+    _check(rc, "pa_decode")
+    return out
+
+
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              max_blocks_per_seq, page_size, opts: PaOpts | None = None) -> int:
+    return int(LIB.pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_blocks_per_seq, page_size,
+                                             ctypes.byref(opts) if opts else None))
+
+
+def pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+                 num_kv_heads, head_dim, page_size, out, stream=None, opts: PaOpts | None = None,
+                 workspace=None):
+    """C ``pa_decode_ex``; ``workspace`` is a torch uint8 tensor or None."""
+    import torch
+    _require_device(q, k_cache, v_cache, block_tables, context_lens, out,
+                    *([workspace] if workspace is not None else []))
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else None)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(q.device):
+        rc = LIB.pa_decode_ex(tensor_desc(q), tensor_desc(k_cache), tensor_desc(v_cache),
+                              tensor_desc(block_tables), tensor_desc(context_lens), float(scale),
+                              num_q_heads, num_kv_heads, head_dim, page_size, tensor_desc(out),
+                              _stream_handle(stream, q.device),
+                              ctypes.byref(opts) if opts else None, ws_ptr, ws_len)
+    _check(rc, "pa_decode_ex")
+    return out
+
+
+def pa_check_args(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+                  num_kv_heads, head_dim, page_size, out, opts: PaOpts | None = None) -> int:
+    """Host-side validation only (no HIP call); returns the error code."""
+    return LIB.pa_check_args(tensor_desc(q), tensor_desc(k_cache), tensor_desc(v_cache),
+                             tensor_desc(block_tables), tensor_desc(context_lens), float(scale),
+                             num_q_heads, num_kv_heads, head_dim, page_size, tensor_desc(out),
+                             ctypes.byref(opts) if opts else None)
+
+
+def pa_get_stats() -> dict:
+    s = PaStats()
+    _check(LIB.pa_get_stats(ctypes.byref(s)), "pa_get_stats")
+    return {name: int(getattr(s, name)) for name, _ in PaStats._fields_}
+
+
+def pa_reset_stats() -> None:
+    LIB.pa_reset_stats()
+
+
+def pa_release() -> None:
+    _check(LIB.pa_release(), "pa_release")
+
+
+# ------------------------------------------------------------------ convenience
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None, *,
+           variant="auto", partition_tokens: int = 0, workspace=None, stream=None):
+    """Decode paged attention on torch tensors.
+
+    q [B, Hq, D] bf16; k_cache/v_cache [NP, P, Hkv, D] bf16 (NHD pool);
+    block_tables [B, MaxBlk] int32; context_lens [B] int32; scale defaults to
+    1/sqrt(D).  Returns out [B, Hq, D] bf16.  The split-KV workspace comes from
+    torch's caching allocator unless one is given.
+    """
+    import torch
+    B, Hq, D = q.shape
+    NP, P, Hkv, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    opts = make_opts(variant, partition_tokens)
+    if workspace is None:
+        n = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], P, opts)
+        if n:
+            workspace = torch.empty(n + 256, dtype=torch.uint8, device=q.device)
+            off = (-workspace.data_ptr()) % 256
+            workspace = workspace[off:off + n]
+    return pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, Hq, Hkv, D, P,
+                        out, stream, opts, workspace)

@@ -1,0 +1,410 @@
+// pa_api.hip -- the C ABI (include/pa_decode.h): host-side validation,
+// planning of the split-KV partitioning, workspace management, launch and
+// counters.  No C++ exception crosses the ABI and no HIP call happens before
+// the arguments have been validated.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pa_decode.h"
+#include "pa_launch.h"
+
+namespace {
+
+thread_local std::string t_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    t_err = buf;
+    return code;
+}
+
+struct Counters {
+    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0};
+    std::atomic<uint64_t> last_t{0}, last_np{0}, last_variant{0};
+} g_stats;
+
+// Validated call geometry.
+struct Geometry {
+    int64_t B, Hq, Hkv, D, P, NP, max_blk;
+    int qg;
+};
+
+struct Plan {
+    int variant;        // PA_VARIANT_VALU / PA_VARIANT_MFMA
+    int qw;             // query heads per workgroup
+    int part_tokens;
+    int n_part;
+    bool split;
+    size_t ws_bytes;
+    size_t lse_offset;  // byte offset of the lse array inside the workspace
+};
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_tensor(const pa_tensor* t, const char* name, int32_t dtype, int ndim) {
+    if (!t) return fail(PA_EINVAL, "%s: descriptor is NULL", name);
+    if (t->dtype != dtype) return fail(PA_EINVAL, "%s: dtype %d, expected %d", name, t->dtype, dtype);
+    if (t->ndim != ndim) return fail(PA_EINVAL, "%s: ndim %d, expected %d", name, t->ndim, ndim);
+    for (int i = 0; i < ndim; ++i) {
+        if (t->shape[i] < 0) return fail(PA_EINVAL, "%s: negative shape[%d]", name, i);
+        if (t->stride[i] < 0) return fail(PA_EINVAL, "%s: negative stride[%d]", name, i);
+    }
+    if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
+        return fail(PA_EINVAL, "%s: innermost stride must be 1", name);
+    bool empty = false;
+    for (int i = 0; i < ndim; ++i) empty = empty || t->shape[i] == 0;
+    if (!t->data && !empty) return fail(PA_EINVAL, "%s: data pointer is NULL", name);
+    return PA_OK;
+}
+
+int check_rows16(const pa_tensor* t, const char* name, int n_outer) {
+    if (!t->data) return PA_OK;   // empty tensor (checked by check_tensor)
+    if (!aligned16(t->data)) return fail(PA_EALIGN, "%s: base pointer not 16-byte aligned", name);
+    for (int i = 0; i < n_outer; ++i)
+        if (t->shape[i] > 1 && (t->stride[i] % 8) != 0)
+            return fail(PA_EALIGN, "%s: stride[%d]=%lld is not a multiple of 8 elements", name, i,
+                        (long long)t->stride[i]);
+    return PA_OK;
+}
+
+int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* bt,
+             const pa_tensor* ctx, float scale, int num_q_heads, int num_kv_heads, int head_dim,
+             int page_size, const pa_tensor* out, const pa_opts* opts, Geometry& geo) {
+    int rc;
+    if ((rc = check_tensor(q, "q", PA_DTYPE_BF16, 3))) return rc;
+    if ((rc = check_tensor(k, "k_cache", PA_DTYPE_BF16, 4))) return rc;
+    if ((rc = check_tensor(v, "v_cache", PA_DTYPE_BF16, 4))) return rc;
+    if ((rc = check_tensor(bt, "block_tables", PA_DTYPE_INT32, 2))) return rc;
+    if ((rc = check_tensor(ctx, "context_lens", PA_DTYPE_INT32, 1))) return rc;
+    if ((rc = check_tensor(out, "out", PA_DTYPE_BF16, 3))) return rc;
+    if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+    if (page_size < 1) return fail(PA_EINVAL, "page_size %d < 1", page_size);
+    if (num_q_heads < 1 || num_kv_heads < 1) return fail(PA_EINVAL, "head counts must be >= 1");
+    if (num_q_heads % num_kv_heads) return fail(PA_EINVAL, "num_q_heads %d not a multiple of num_kv_heads %d",
+                                                num_q_heads, num_kv_heads);
+    const int64_t B = q->shape[0];
+    if (q->shape[1] != num_q_heads || q->shape[2] != head_dim)
+        return fail(PA_EINVAL, "q shape [%lld,%lld,%lld] does not match Hq=%d, D=%d", (long long)B,
+                    (long long)q->shape[1], (long long)q->shape[2], num_q_heads, head_dim);
+    for (int i = 0; i < 4; ++i)
+        if (k->shape[i] != v->shape[i]) return fail(PA_EINVAL, "k_cache and v_cache shapes differ");
+    if (k->shape[1] != page_size || k->shape[2] != num_kv_heads || k->shape[3] != head_dim)
+        return fail(PA_EINVAL, "k_cache shape [%lld,%lld,%lld,%lld] does not match P=%d, Hkv=%d, D=%d",
+                    (long long)k->shape[0], (long long)k->shape[1], (long long)k->shape[2],
+                    (long long)k->shape[3], page_size, num_kv_heads, head_dim);
+    if (bt->shape[0] != B) return fail(PA_EINVAL, "block_tables has %lld rows, batch is %lld",
+                                       (long long)bt->shape[0], (long long)B);
+    if (ctx->shape[0] != B) return fail(PA_EINVAL, "context_lens has %lld entries, batch is %lld",
+                                        (long long)ctx->shape[0], (long long)B);
+    if (out->shape[0] != B || out->shape[1] != num_q_heads || out->shape[2] != head_dim)
+        return fail(PA_EINVAL, "out shape does not match q");
+    if (opts) {
+        for (int i = 0; i < 6; ++i)
+            if (opts->reserved[i]) return fail(PA_EINVAL, "pa_opts.reserved must be zero");
+        if (opts->variant < PA_VARIANT_AUTO || opts->variant > PA_VARIANT_MFMA)
+            return fail(PA_EINVAL, "unknown variant %d", opts->variant);
+        if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
+    }
+    if (head_dim != 128 && head_dim != 256) return fail(PA_ENOTSUP, "head_dim %d (supported: 128, 256)", head_dim);
+    const int qg = num_q_heads / num_kv_heads;
+    if (qg != 1 && qg != 2 && qg != 4 && qg != 8 && qg != 16)
+        return fail(PA_ENOTSUP, "Hq/Hkv = %d (supported: 1, 2, 4, 8, 16)", qg);
+    if (B > 65535) return fail(PA_ENOTSUP, "batch %lld > 65535", (long long)B);
+    if (bt->shape[1] > (int64_t)1 << 24 || (int64_t)bt->shape[1] * page_size > INT32_MAX / 2)
+        return fail(PA_ENOTSUP, "block table too wide");
+    if (k->shape[0] > INT32_MAX) return fail(PA_ENOTSUP, "pool too large");
+    if ((rc = check_rows16(q, "q", 2))) return rc;
+    if ((rc = check_rows16(k, "k_cache", 3))) return rc;
+    if ((rc = check_rows16(v, "v_cache", 3))) return rc;
+    if ((rc = check_rows16(out, "out", 2))) return rc;
+    if ((reinterpret_cast<uintptr_t>(bt->data) & 3u) || (reinterpret_cast<uintptr_t>(ctx->data) & 3u))
+        return fail(PA_EALIGN, "block_tables/context_lens not 4-byte aligned");
+    geo = Geometry{B, num_q_heads, num_kv_heads, head_dim, page_size, k->shape[0], bt->shape[1], qg};
+    return PA_OK;
+}
+
+Plan make_plan(const Geometry& g, const pa_opts* opts) {
+    Plan pl{};
+    pl.variant = (opts && opts->variant) ? opts->variant : PA_VARIANT_VALU;
+    pl.qw = g.qg < 8 ? g.qg : 8;
+    const int64_t max_ctx = std::max<int64_t>(g.max_blk * g.P, 1);
+    const int64_t groups = g.B * (g.Hq / pl.qw);
+    int64_t T;
+    if (opts && opts->partition_tokens > 0) {
+        T = (int64_t)opts->partition_tokens;
+    } else {
+        // Aim for ~1024 workgroups; partitions of 64..1024 tokens.
+        T = (max_ctx * groups + 1023) / 1024;
+        T = std::max<int64_t>(64, std::min<int64_t>(T, 1024));
+    }
+    T = (T + 63) / 64 * 64;
+    T = std::min<int64_t>(T, 8192 * g.P);   // page-id LDS stays <= ~32 KB
+    if (T >= max_ctx) T = max_ctx;
+    pl.part_tokens = (int)T;
+    pl.n_part = (int)((max_ctx + T - 1) / T);
+    pl.split = pl.n_part > 1;
+    if (pl.split) {
+        const size_t n = (size_t)g.B * g.Hq * pl.n_part;
+        pl.lse_offset = align_up(n * g.D * sizeof(float), kAlign);
+        pl.ws_bytes = pl.lse_offset + align_up(n * sizeof(float), kAlign);
+    }
+    return pl;
+}
+
+// Library-owned per-device workspace.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::vector<Workspace> g_ws;
+
+int library_workspace(int dev, size_t need, void** out) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+    Workspace& w = g_ws[dev];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            hipError_t e = hipDeviceSynchronize();   // old buffer may still be in use
+            if (e != hipSuccess) return fail(PA_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t sz = align_up(need + need / 2, 1 << 20);
+        hipError_t e = hipMalloc(&w.ptr, sz);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return fail(PA_ENOMEM, "hipMalloc(%zu): %s", sz, hipGetErrorString(e));
+        }
+        w.bytes = sz;
+    }
+    *out = w.ptr;
+    return PA_OK;
+}
+
+int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* bt,
+           const pa_tensor* ctx, float scale, const pa_tensor* out, void* stream,
+           const Geometry& g, const Plan& pl, void* ws) {
+    pa::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q->data);
+    p.q_sb = q->stride[0];
+    p.q_sh = q->stride[1];
+    p.k = static_cast<const uint16_t*>(k->data);
+    p.k_sp = k->stride[0];
+    p.k_ss = k->stride[1];
+    p.k_sh = k->stride[2];
+    p.v = static_cast<const uint16_t*>(v->data);
+    p.v_sp = v->stride[0];
+    p.v_ss = v->stride[1];
+    p.v_sh = v->stride[2];
+    p.bt = static_cast<const int32_t*>(bt->data);
+    p.bt_sb = bt->stride[0];
+    p.ctx = static_cast<const int32_t*>(ctx->data);
+    p.out = static_cast<uint16_t*>(out->data);
+    p.o_sb = out->stride[0];
+    p.o_sh = out->stride[1];
+    p.part_o = pl.split ? static_cast<float*>(ws) : nullptr;
+    p.part_lse = pl.split ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.lse_offset) : nullptr;
+    p.B = (int)g.B;
+    p.Hq = (int)g.Hq;
+    p.Hkv = (int)g.Hkv;
+    p.P = (int)g.P;
+    p.p_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((int64_t)1 << sh == g.P) p.p_shift = sh;
+    p.max_blk = (int)g.max_blk;
+    p.num_pages = (int)std::max<int64_t>(g.NP, 1);
+    p.part_tokens = pl.part_tokens;
+    p.n_part = pl.n_part;
+    p.scale_log2 = scale * pa::kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    hipError_t e;
+    if (pl.variant == PA_VARIANT_MFMA) {
+        e = pa::launch_mfma(p, (int)g.D, pl.qw, pl.split, s);
+        if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma) launch: %s", hipGetErrorString(e));
+        g_stats.mfma++;
+    } else {
+        e = pa::launch_valu(p, (int)g.D, pl.qw, pl.split, s);
+        if (e != hipSuccess) return fail(PA_EHIP, "decode (valu) launch: %s", hipGetErrorString(e));
+        g_stats.valu++;
+    }
+    if (pl.split) {
+        e = pa::launch_merge(p, (int)g.D, s);
+        if (e != hipSuccess) return fail(PA_EHIP, "merge launch: %s", hipGetErrorString(e));
+        g_stats.merge++;
+        g_stats.split++;
+    }
+    g_stats.calls++;
+    g_stats.last_t = (uint64_t)pl.part_tokens;
+    g_stats.last_np = (uint64_t)pl.n_part;
+    g_stats.last_variant = (uint64_t)pl.variant;
+    return PA_OK;
+}
+
+int decode_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* bt,
+                const pa_tensor* ctx, float scale, int num_q_heads, int num_kv_heads, int head_dim,
+                int page_size, const pa_tensor* out, void* stream, const pa_opts* opts,
+                void* workspace, size_t workspace_bytes) {
+    t_err.clear();
+    Geometry g;
+    int rc = validate(q, k, v, bt, ctx, scale, num_q_heads, num_kv_heads, head_dim, page_size, out,
+                      opts, g);
+    if (rc) return rc;
+    Plan pl = make_plan(g, opts);
+    if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw))
+        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
+    if (g.B == 0) return PA_OK;
+    int dev = 0;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(PA_ENODEV, "no HIP device");
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ENODEV, "hipGetDevice: %s", hipGetErrorString(e));
+    void* ws = nullptr;
+    if (pl.split) {
+        if (workspace) {
+            if (workspace_bytes < pl.ws_bytes)
+                return fail(PA_ENOMEM, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.ws_bytes);
+            if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+                return fail(PA_EALIGN, "workspace not %zu-byte aligned", kAlign);
+            ws = workspace;
+        } else {
+            rc = library_workspace(dev, pl.ws_bytes, &ws);
+            if (rc) return rc;
+        }
+    }
+    try {
+        return launch(q, k, v, bt, ctx, scale, out, stream, g, pl, ws);
+    } catch (const std::bad_alloc&) {
+        return fail(PA_ENOMEM, "host allocation failed");
+    } catch (...) {
+        return fail(PA_EHIP, "unexpected exception");
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+              const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+              int num_q_heads, int num_kv_heads, int head_dim, int page_size, const pa_tensor* out,
+              void* stream) {
+    return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+                       num_kv_heads, head_dim, page_size, out, stream, nullptr, nullptr, 0);
+}
+
+int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                 const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                 int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                 const pa_tensor* out, void* stream, const pa_opts* opts, void* workspace,
+                 size_t workspace_bytes) {
+    return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+                       num_kv_heads, head_dim, page_size, out, stream, opts, workspace,
+                       workspace_bytes);
+}
+
+int pa_check_args(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                  const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                  int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                  const pa_tensor* out, const pa_opts* opts) {
+    t_err.clear();
+    Geometry g;
+    int rc = validate(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+                      num_kv_heads, head_dim, page_size, out, opts, g);
+    if (rc) return rc;
+    Plan pl = make_plan(g, opts);
+    if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw))
+        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
+    return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int64_t max_blocks_per_seq, int page_size, const pa_opts* opts) {
+    if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads ||
+        head_dim < 1 || max_blocks_per_seq < 0 || page_size < 1)
+        return 0;
+    if (opts && opts->partition_tokens < 0) return 0;
+    Geometry g{num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, 1, max_blocks_per_seq,
+               num_q_heads / num_kv_heads};
+    return make_plan(g, opts).ws_bytes;
+}
+
+int pa_get_stats(pa_stats* s) {
+    if (!s) return PA_EINVAL;
+    s->calls = g_stats.calls;
+    s->valu_launches = g_stats.valu;
+    s->mfma_launches = g_stats.mfma;
+    s->split_calls = g_stats.split;
+    s->merge_launches = g_stats.merge;
+    s->last_partition_tokens = g_stats.last_t;
+    s->last_num_partitions = g_stats.last_np;
+    s->last_variant = g_stats.last_variant;
+    return PA_OK;
+}
+
+void pa_reset_stats(void) {
+    g_stats.calls = 0;
+    g_stats.valu = 0;
+    g_stats.mfma = 0;
+    g_stats.split = 0;
+    g_stats.merge = 0;
+    g_stats.last_t = 0;
+    g_stats.last_np = 0;
+    g_stats.last_variant = 0;
+}
+
+const char* pa_strerror(int code) {
+    switch (code) {
+        case PA_OK: return "success";
+        case PA_EINVAL: return "invalid argument";
+        case PA_ENOTSUP: return "unsupported configuration";
+        case PA_EALIGN: return "misaligned pointer or stride";
+        case PA_ENODEV: return "no HIP device";
+        case PA_ENOMEM: return "out of memory or workspace too small";
+        case PA_EHIP: return "HIP runtime error";
+        default: return "unknown error code";
+    }
+}
+
+const char* pa_last_error(void) { return t_err.c_str(); }
+
+int pa_release(void) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int rc = PA_OK;
+    int cur = -1;
+    bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (size_t d = 0; d < g_ws.size(); ++d) {
+        if (!g_ws[d].ptr) continue;
+        if (hipSetDevice((int)d) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipFree(g_ws[d].ptr) != hipSuccess)
+            rc = fail(PA_EHIP, "releasing workspace of device %zu failed", d);
+        g_ws[d].ptr = nullptr;
+        g_ws[d].bytes = 0;
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+    return rc;
+}
+
+const char* pa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,26 @@
+// pa_launch.h -- host-side launch entry points of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "pa_device.h"
+
+namespace pa {
+
+// Dynamic LDS holding one partition's page ids: a partition of T tokens spans
+// at most ceil(T / P) + 1 pages.
+inline size_t pages_lds_bytes(const DecodeParams& p) {
+    return sizeof(int) * (size_t)((p.part_tokens + p.P - 1) / p.P + 1);
+}
+
+// Vector-ALU decode kernel; qw = query heads per workgroup (1, 2, 4 or 8).
+hipError_t launch_valu(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s);
+
+// Matrix-core decode kernel (16 query rows per MFMA tile).
+hipError_t launch_mfma(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s);
+bool mfma_supported(int head_dim, int qw);
+
+// Log-sum-exp merge of split partials into bf16 output.
+hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s);
+
+}  // namespace pa
