@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of decode paged attention on one MI355X.
+
+Metric: paged-attention decode microseconds per call and the achieved KV-read
+bandwidth, i.e. algorithmic KV bytes (sum_b L_b * Hkv * D * 2 tensors * 2 B)
+divided by the time per call, also as a fraction of the MI355X HBM3E peak
+(8 TB/s).  A step is one decode call over the whole batch (decode kernel plus,
+when the context is split, the log-sum-exp merge kernel), with every input
+already resident in HBM.
+
+Default workload: the long-context, high-GQA batch (64 sequences, ctx
+U[8192, 32768], Hq 64 / Hkv 8, head_dim 128, page 16; about 5.4 GB of KV per
+call).  The same JSON line also carries every other workload's time per call
+(``per_config``), the bandwidth roofline of the dominant kernel and the CPU
+oracle timed on the host cores as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+METRIC = "paged-attn decode µs/call + achieved KV-read GB/s (% of MI355X HBM peak)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_ctx_gqa8")
+    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="timed steps only (no per-config sweep, no CPU baseline): for rocprofv3 runs")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also time a plain device copy of this many MiB (HBM reference and the "
+                         "calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+def make_call(pa, d, call, variant, partition_tokens):
+    """A closure issuing one decode call on the current stream."""
+    import torch
+    q, k, v = d.call(call)
+    out = torch.empty_like(q)
+    B, Hq, D = q.shape
+    NP, P, Hkv, _ = k.shape
+    opts = pa.make_opts(variant, partition_tokens)
+    n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, opts)
+    ws = None
+    if n:
+        raw = torch.empty(n + 256, dtype=torch.uint8, device=q.device)
+        off = (-raw.data_ptr()) % 256
+        ws = raw[off:off + n]
+    scale = d.w.scale
+
+    def run():
+        pa.pa_decode_ex(q, k, v, d.block_tables, d.context_lens, scale, Hq, Hkv, D, P, out,
+                        None, opts, ws)
+    return run, out
+
+
+def event_time_ms(fn, n, torch):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e)
+
+
+def graph_time_us(calls, reps, torch):
+    """Capture the list of calls into one HIP graph, replay it, and return
+    the event-timed microseconds per call."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for c in calls:          # warm outside the graph
+            c()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = event_time_ms(g.replay, reps, torch)
+    return 1e3 * ms / (reps * len(calls))
+
+
+# ----------------------------------------------------------------------------
+def per_config(pa, variant, partition_tokens, torch, workloads_mod):
+    """Time every workload: warm (inputs reused, MALL may hold them) and, for
+    footprints that fit the 256 MB MALL, cold (calls rotate over replicas of
+    the KV pools totalling >= 1 GB)."""
+    import numpy as np
+    res = {}
+    for name in workloads_mod.ORDER:
+        w = workloads_mod.WORKLOADS[name]
+        if name == "long_ctx_gqa8":
+            d = workloads_mod.device_inputs(w, seed=0)
+        else:
+            d = workloads_mod.to_device(workloads_mod.make_inputs(w, seed=0))
+        lens = d.layout.context_lens
+        kvb = workloads_mod.kv_bytes(w, lens)
+        n_calls = w.calls if w.calls > 1 else 1
+        calls = [make_call(pa, d, i, variant, partition_tokens)[0] for i in range(n_calls)]
+        st = pa.pa_get_stats()
+        entry = {"kv_bytes_per_call": kvb, "calls": n_calls}
+        if name == "long_ctx_gqa8":
+            ms = event_time_ms(calls[0], 3, torch)
+            ms = event_time_ms(calls[0], 10, torch) / 10
+            entry["us_per_call"] = round(1e3 * ms, 2)
+        else:
+            reps = max(3, int(20000 // max(1, n_calls)))
+            entry["us_per_call"] = round(graph_time_us(calls, min(reps, 200), torch), 3)
+            footprint = kvb * (w.layers if w.layers > 1 else 1)
+            R = min(int(np.ceil(1.0e9 / max(footprint, 1))), 64)
+            if R > 1:
+                reps_k = []
+                for r in range(R):
+                    k2 = d.k.clone()
+                    v2 = d.v.clone()
+                    d2 = workloads_mod.DeviceInputs(w, d.q, k2, v2, d.block_tables, d.context_lens,
+                                                    d.layout)
+                    reps_k.append(d2)
+                cold_calls = []
+                for i in range(n_calls):
+                    for d2 in reps_k:
+                        cold_calls.append(make_call(pa, d2, i, variant, partition_tokens)[0])
+                cold_calls = cold_calls[:min(len(cold_calls), max(R, 2048))]
+                entry["us_per_call_cold"] = round(graph_time_us(cold_calls, 5, torch), 3)
+                entry["cold_replicas"] = R
+                del reps_k
+        st2 = pa.pa_get_stats()
+        entry["partition_tokens"] = int(st2["last_partition_tokens"])
+        entry["partitions"] = int(st2["last_num_partitions"])
+        entry["variant"] = {1: "valu", 2: "mfma"}.get(int(st2["last_variant"]), "?")
+        for key in ("us_per_call", "us_per_call_cold"):
+            if key in entry:
+                gbs = kvb / (entry[key] * 1e-6) / 1e9
+                entry[key.replace("us_per_call", "kv_GBps")] = round(gbs, 1)
+                entry[key.replace("us_per_call", "hbm_frac")] = round(gbs / HBM_PEAK_GBS, 4)
+        res[name] = entry
+        log(f"[per_config] {name}: {entry}")
+        del d, calls
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(d, w, target_s, workloads_mod):
+    """The oracle as it stands, on the host cores, over whole sequences of the
+    same workload (all query heads) until about target_s seconds."""
+    import numpy as np
+    import oracle
+    host = workloads_mod.host_copy(d)
+    threads = oracle.default_threads()
+    t_total, b_done, bytes_done, tok = 0.0, 0, 0, 0
+    lens = host.context_lens
+    for b in range(w.batch):
+        pairs = np.array([(b, h) for h in range(w.num_q_heads)], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.attention_pairs(host.q[0], host.k[0], host.v[0], host.block_tables, lens, w.scale,
+                               w.num_kv_heads, pairs, threads=threads)
+        t_total += time.perf_counter() - t0
+        b_done += 1
+        tok += int(lens[b])
+        bytes_done += int(lens[b]) * w.num_kv_heads * w.head_dim * 4
+        if t_total >= target_s:
+            break
+    gbs = bytes_done / t_total / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t_total, 2),
+            "us_per_call_equiv": round(1e6 * t_total * w.batch / b_done, 1),
+            "sample": f"{b_done} of {w.batch} sequences of {w.name} ({tok} tokens, all "
+                      f"{w.num_q_heads} query heads), fp64, {threads} threads"}
+
+
+def copy_probe(mib, torch):
+    """A plain elementwise kernel that reads and writes mib MiB once each
+    (torch.neg on fp32): the HBM reference and the kernel whose rocprofv3
+    FETCH_SIZE / WRITE_SIZE calibrate the counters."""
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    reps = 20
+    ms = event_time_ms(lambda: torch.neg(src, out=dst), reps, torch) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": n, "bytes_written": n, "us": round(ms * 1e3, 2),
+            "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "decode paged attention here is a single-GPU kernel; no multi-GPU path exists.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_attention_decode_04_amd as pa
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    if w.name == "long_ctx_gqa8":
+        d = wl.device_inputs(w, seed=args.seed)
+    else:
+        d = wl.to_device(wl.make_inputs(w, seed=args.seed))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs for {w.name} ready in {time.perf_counter() - t_gen:.1f}s")
+    kvb_per_call = wl.kv_bytes(w, d.layout.context_lens)
+    n_calls = w.calls
+    calls = [make_call(pa, d, i, args.variant, args.partition_tokens)[0] for i in range(n_calls)]
+
+    def step():                       # one pass of the whole path over the batch
+        for c in calls:
+            c()
+
+    pa.pa_reset_stats()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = pa.pa_get_stats()
+    ev_s, ev_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_s.record()
+    for _ in range(args.steps):
+        step()
+    ev_e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev_s.elapsed_time(ev_e)
+    ms_per_step = 1e3 * wall / args.steps
+    us_per_call_ev = 1e3 * gpu_ms / (args.steps * n_calls)
+    kv_per_step = kvb_per_call * n_calls
+    value = kv_per_step / (ms_per_step * 1e-3) / 1e9
+    achieved = kvb_per_call / (us_per_call_ev * 1e-6) / 1e9
+    variant = {1: "valu", 2: "mfma"}.get(int(st["last_variant"]), "?")
+    log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step wall, {us_per_call_ev:.2f} us/call (events), "
+        f"{achieved:.0f} GB/s KV, variant {variant}, T={st['last_partition_tokens']} "
+        f"x {st['last_num_partitions']}")
+
+    kernel = ("pa_decode_valu_kernel" if variant == "valu" else "pa_decode_mfma_kernel")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if variant == "mfma" else "f32",
+        "storage_dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled block tables)",
+        "config": {
+            "workload": w.name, "desc": w.desc, "batch": w.batch,
+            "sum_ctx": int(d.layout.context_lens.sum()), "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+            "calls_per_step": n_calls, "kv_bytes_per_call": kvb_per_call, "variant": variant,
+            "partition_tokens": int(st["last_partition_tokens"]),
+            "partitions": int(st["last_num_partitions"]),
+        },
+        "us_per_call": round(us_per_call_ev, 3),
+        "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": kernel + (" + pa_lse_merge_kernel" if st["merge_launches"] else ""),
+            "duration_us": round(us_per_call_ev, 3),
+            "note": "achieved = algorithmic KV bytes per call / HIP-event time per call over the "
+                    "timed region (decode kernel plus merge kernel, on the launch stream)",
+        },
+    }
+    if args.copy_probe_mib:
+        result["copy_probe"] = copy_probe(args.copy_probe_mib, torch)
+        log(f"[bench] copy probe: {result['copy_probe']}")
+    if not args.profile and not args.no_per_config:
+        result["per_config"] = per_config(pa, args.variant, args.partition_tokens, torch, wl)
+    if not args.profile and not args.no_cpu_baseline:
+        t = time.perf_counter()
+        result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds, wl)
+        log(f"[bench] cpu baseline in {time.perf_counter() - t:.1f}s: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

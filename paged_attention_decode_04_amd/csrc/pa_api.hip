@@ -144,7 +144,10 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
 Plan make_plan(const Geometry& g, const pa_opts* opts) {
     Plan pl{};
     pl.variant = (opts && opts->variant) ? opts->variant : PA_VARIANT_VALU;
-    pl.qw = g.qg < 8 ? g.qg : 8;
+    if (pl.variant == PA_VARIANT_MFMA)
+        pl.qw = g.qg < 16 ? g.qg : 16;          // one 16-column MFMA tile of queries
+    else
+        pl.qw = g.qg < 8 ? g.qg : 8;
     const int64_t max_ctx = std::max<int64_t>(g.max_blk * g.P, 1);
     const int64_t groups = g.B * (g.Hq / pl.qw);
     int64_t T;
@@ -235,6 +238,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     p.num_pages = (int)std::max<int64_t>(g.NP, 1);
     p.part_tokens = pl.part_tokens;
     p.n_part = pl.n_part;
+    p.qw = pl.qw;
     p.scale_log2 = scale * pa::kLog2e;
     hipStream_t s = static_cast<hipStream_t>(stream);
 

@@ -22,6 +22,7 @@ struct DecodeParams {
     int   p_shift;                                          // log2(P) if P is a power of 2, else -1
     int   part_tokens;                                      // tokens per partition
     int   n_part;                                           // grid partitions
+    int   qw;                                               // query heads per workgroup
     float scale_log2;                                       // scale * log2(e)
 };
 

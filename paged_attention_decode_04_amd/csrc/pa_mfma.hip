@@ -1,12 +1,375 @@
-// pa_mfma.hip -- matrix-core decode kernel (placeholder until implemented).
+// pa_mfma.hip -- matrix-core decode paged-attention kernel for gfx950.
+//
+// One workgroup (4 waves) handles one sequence, the (up to 16) query heads
+// of one KV head, and one partition of the tokens.  Each wave walks 16-token
+// tiles of the partition (tile j goes to wave j mod 4) and keeps its own
+// online-softmax state.  Per tile:
+//
+//   S^T (16 tokens x 16 queries) = K_tile (16 x D) . Q^T (D x 16)
+//       v_mfma_f32_16x16x32_bf16, D/32 steps.  The K rows go straight from
+//       global memory into the A operand: lane l supplies token l%16 and the
+//       16 bytes [64 kk + 16 (l/16), +16) of its row, i.e. 16 rows x 64
+//       contiguous bytes per load instruction.  Q^T (bf16, unscaled) is the
+//       B operand, loaded once; query columns past the group are zero.
+//   The C tile gives lane l the logits of query l%16 for tokens
+//   4 (l/16) + r, r = 0..3.  Scale (times log2 e), mask the tail, take the
+//   tile max across the four 16-lane rows (permlane16/32 swaps), update the
+//   running max m and sum l, rescale the accumulators, p = 2^(s - m).
+//   O^T (D x 16) += V^T_tile (D x 16 tokens) . P^T (16 x 16)
+//       v_mfma_f32_16x16x16_bf16, D/16 steps.  P^T is exactly the C tile
+//       held as bf16 (lane l: query l%16, tokens 4 (l/16) + jj).  V^T: lane l
+//       loads the 16-byte chunk l%16 of the four rows 4 (l/16) + jj (whole
+//       256-byte rows per 16 lanes) and transposes the 4 x 8 bf16 block in
+//       registers, so MFMA mm of a 128-dim half covers dims 8 (l%16) + mm.
+//
+// Every accumulator element of a lane belongs to the lane's own query, so the
+// online-softmax rescale needs no data movement.  Waves merge through LDS with
+// the log-sum-exp algebra of the split-KV merge; split mode writes
+// (o_p, lse_p) partials.  This is the online-softmax decode over an NHD cache
+// of page 1 of the source pages (issue "PagedAttnOnline is 8.1x slower per
+// call", section "Where to look"), with the query heads of a KV group fused
+// into one tile (page 2, PR "head_dim=128 decode arm": qg=2 fusion; here up
+// to 16) and the matrix-core arm the pages leave as future work, re-designed
+// for CDNA4 MFMA.
+#include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
-bool mfma_supported(int, int) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-hipError_t launch_mfma(const DecodeParams&, int, int, bool, hipStream_t) {
-    return hipErrorInvalidValue;
+constexpr int kMBlock = 256;
+constexpr int kMWaves = kMBlock / 64;
+constexpr int kTile = 16;                       // tokens per MFMA tile
+constexpr float kRescaleSlack = 8.f;            // log2 units, see tile_step
+
+template <int D>
+struct TileFrag {
+    static constexpr int KK = D / 32;           // Q.K MFMA steps
+    static constexpr int VH = D / 128;          // 128-dim halves of a V row
+    u32x4 k[KK];
+    u32x4 v[4][VH];
+};
+
+// Element offset of token t's row (KV head g) in a pool with strides sp, ss, sh.
+__device__ __forceinline__ int64_t row_offset(const DecodeParams& p, const int* s_pages, int pg0,
+                                              int t, int64_t sp, int64_t ss, int64_t gsh) {
+    int lp, slot;
+    page_slot(p, t, lp, slot);
+    return (int64_t)s_pages[lp - pg0] * sp + (int64_t)slot * ss + gsh;
+}
+
+// Per-lane 32-bit element offsets inside one page, fixed for the whole
+// kernel: K row n (chunk q) and the four V rows 4q + jj (chunk n).
+struct LaneOffsets {
+    int k;
+    int v[4];
+};
+
+// Issue the loads of the 16-token tile starting at tb.  K: token tb + n
+// (A operand rows); V: tokens tb + 4q + jj (16 lanes per row).  Tokens at or
+// past te are clamped to te - 1, a real row, and masked out of the softmax.
+// PAGE16: the page size is a power of two >= 16, so the tile lies in one page;
+// the page base is wave-uniform and each lane adds a fixed 32-bit offset.
+template <int D, bool PAGE16>
+__device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pages, int pg0, int g,
+                                          int n, int q, const LaneOffsets& lo, int tb, int te,
+                                          TileFrag<D>& f) {
+    if constexpr (PAGE16) {
+        const int lp = tb >> p.p_shift;
+        const int page = __builtin_amdgcn_readfirstlane(s_pages[lp - pg0]);
+        const int slot0 = tb - (lp << p.p_shift);
+        const uint16_t* kt = p.k + (int64_t)page * p.k_sp + (int64_t)g * p.k_sh + (int64_t)slot0 * p.k_ss;
+        const uint16_t* vt = p.v + (int64_t)page * p.v_sp + (int64_t)g * p.v_sh + (int64_t)slot0 * p.v_ss;
+        if (tb + kTile <= te) {                 // full tile (wave-uniform)
+#pragma unroll
+            for (int kk = 0; kk < TileFrag<D>::KK; ++kk) f.k[kk] = load16_nt(kt + lo.k + 32 * kk);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int hh = 0; hh < TileFrag<D>::VH; ++hh)
+                    f.v[jj][hh] = load16_nt(vt + lo.v[jj] + 128 * hh);
+        } else {                                // tail tile: clamp rows to te - 1
+            const int last = te - 1 - tb;
+            const int ks = (int)p.k_ss, vs = (int)p.v_ss;
+            const int ko = min(n, last) * ks + 8 * q;
+#pragma unroll
+            for (int kk = 0; kk < TileFrag<D>::KK; ++kk) f.k[kk] = load16_nt(kt + ko + 32 * kk);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int vo = min(4 * q + jj, last) * vs + 8 * n;
+#pragma unroll
+                for (int hh = 0; hh < TileFrag<D>::VH; ++hh) f.v[jj][hh] = load16_nt(vt + vo + 128 * hh);
+            }
+        }
+    } else {
+        const int64_t gk = (int64_t)g * p.k_sh, gv = (int64_t)g * p.v_sh;
+        const int tk = min(tb + n, te - 1);
+        const uint16_t* kr = p.k + row_offset(p, s_pages, pg0, tk, p.k_sp, p.k_ss, gk) + 8 * q;
+#pragma unroll
+        for (int kk = 0; kk < TileFrag<D>::KK; ++kk) f.k[kk] = load16_nt(kr + 32 * kk);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int tv = min(tb + 4 * q + jj, te - 1);
+            const uint16_t* vr = p.v + row_offset(p, s_pages, pg0, tv, p.v_sp, p.v_ss, gv) + 8 * n;
+#pragma unroll
+            for (int hh = 0; hh < TileFrag<D>::VH; ++hh) f.v[jj][hh] = load16_nt(vr + 128 * hh);
+        }
+    }
+}
+
+__device__ __forceinline__ float xmax16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One 16-token tile: logits on MFMA, online-softmax update, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<D>& cur,
+                                          const u32x4 (&qop)[D / 32], int tb, int te, int q,
+                                          f32x4 (&o)[D / 16], float& m_run, float& l_run) {
+    constexpr int KK = TileFrag<D>::KK;
+    constexpr int VH = TileFrag<D>::VH;
+    constexpr int NO = D / 16;
+    // logits S^T: lane -> query n, tokens tb + 4q + r
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[kk]),
+                                                    __builtin_bit_cast(bf16x8, qop[kk]), s, 0, 0, 0);
+    float sv[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        sv[r] = (tb + 4 * q + r < te) ? s[r] * p.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, sv[r]);
+    }
+    mt = xmax32(xmax16(mt));
+    // The reference max only moves when the tile max exceeds it by more than
+    // kRescaleSlack (log2 units): p = 2^(s - m) then stays <= 2^kRescaleSlack,
+    // exact in fp32 and bf16 alike, and the accumulator rescale (a
+    // wave-uniform branch) runs only a handful of times per partition.
+    if (__any(mt > m_run + kRescaleSlack)) {
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - mn);
+        m_run = mn;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NO; ++i) o[i] *= alpha;
+    }
+    float pr[4], psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        pr[r] = fast_exp2(sv[r] - m_run);
+        psum += pr[r];
+    }
+    l_run += psum;
+    const u32x2 pb = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+
+    // O^T += V^T . P^T, V transposed in registers (4 tokens x 8 dims per lane)
+#pragma unroll
+    for (int hh = 0; hh < VH; ++hh)
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+            // (token 0, token 1) and (token 2, token 3) of dim 8n + mm: the low
+            // (even mm) or high (odd mm) halves of dword mm/2 of two rows.
+            const int x = mm >> 1;
+            const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+            const u32x2 va = {__builtin_amdgcn_perm(cur.v[1][hh][x], cur.v[0][hh][x], sel),
+                              __builtin_amdgcn_perm(cur.v[3][hh][x], cur.v[2][hh][x], sel)};
+            o[hh * 8 + mm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(bf16x4, va), __builtin_bit_cast(bf16x4, pb), o[hh * 8 + mm], 0, 0, 0);
+        }
+}
+
+template <int D, bool SPLIT, bool PAGE16>
+__global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p) {
+    constexpr int KK = TileFrag<D>::KK;
+    constexpr int VH = TileFrag<D>::VH;
+    constexpr int NO = D / 16;                  // O^T accumulator tiles
+    // Flat grid, query block fastest and partition slowest: consecutive
+    // workgroups (dealt round-robin to the XCDs) cover different heads and
+    // sequences of the same partition index, so every XCD gets an even share
+    // of each sequence's work, and partitions past a sequence's end (which
+    // exit at once) come last.
+    const int n_qb = p.Hq / p.qw;
+    const int qb = blockIdx.x % n_qb;
+    const int rest = blockIdx.x / n_qb;
+    const int b = rest % p.B;
+    const int part = rest / p.B;
+    const int qw = p.qw;                        // query heads of this workgroup (<= 16)
+    const int h0 = qb * qw;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, q = lane >> 4;
+    const int g = h0 / (p.Hq / p.Hkv);
+
+    const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+    const int ts = part * p.part_tokens;
+    if (ts >= L && part > 0) return;
+    const int te = min(L, ts + p.part_tokens);
+    const int n_tok = max(te - ts, 0);
+
+    extern __shared__ int s_pages[];
+    int pg0 = 0;
+    if (n_tok > 0) {
+        int lp_last, unused;
+        page_slot(p, ts, pg0, unused);
+        page_slot(p, te - 1, lp_last, unused);
+        const int32_t* btrow = p.bt + (int64_t)b * p.bt_sb;
+        for (int i = tid; i <= lp_last - pg0; i += kMBlock)
+            s_pages[i] = clampi(btrow[pg0 + i], 0, p.num_pages - 1);
+    }
+
+    // Q^T as the B operand: column n = query h0 + n, 8 dims per lane per step.
+    u32x4 qop[KK];
+    {
+        const bool live = n < qw;
+        const uint16_t* qr = p.q + (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? n : 0)) * p.q_sh + 8 * q;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            u32x4 w = load16(qr + 32 * kk);
+            qop[kk] = live ? w : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __syncthreads();
+
+    f32x4 o[NO];
+#pragma unroll
+    for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kEmptyMax, l_run = 0.f;
+
+    const int n_tiles = (n_tok + kTile - 1) / kTile;
+    LaneOffsets lo;
+    lo.k = n * (int)p.k_ss + 8 * q;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
+    // Ping-pong between two register buffers: the next tile's loads are
+    // always issued before the current tile is consumed, with no copies
+    // between buffers (so the waits cover only the current tile).
+    int j = wave;
+    if (j < n_tiles) {
+        TileFrag<D> fa, fb;
+        load_tile<D, PAGE16>(p, s_pages, pg0, g, n, q, lo, ts + j * kTile, te, fa);
+        while (true) {
+            if (j + kMWaves >= n_tiles) {
+                tile_step<D>(p, fa, qop, ts + j * kTile, te, q, o, m_run, l_run);
+                break;
+            }
+            load_tile<D, PAGE16>(p, s_pages, pg0, g, n, q, lo, ts + (j + kMWaves) * kTile, te, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_step<D>(p, fa, qop, ts + j * kTile, te, q, o, m_run, l_run);
+            j += kMWaves;
+            if (j + kMWaves >= n_tiles) {
+                tile_step<D>(p, fb, qop, ts + j * kTile, te, q, o, m_run, l_run);
+                break;
+            }
+            load_tile<D, PAGE16>(p, s_pages, pg0, g, n, q, lo, ts + (j + kMWaves) * kTile, te, fa);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_step<D>(p, fb, qop, ts + j * kTile, te, q, o, m_run, l_run);
+            j += kMWaves;
+        }
+    }
+
+    // Row sums over the four 16-lane rows (each saw different tokens).
+    l_run = xsum32(xsum16(l_run));
+
+    // Merge the waves through LDS.  O^T tile (hh, mm), element r of lane
+    // (n, q) holds query n, dim 128 hh + 32 q + 8 r + mm.
+    __shared__ float s_o[kMWaves][16][D + 4];   // +4: spread the 16 query rows over banks
+    __shared__ float s_m[kMWaves][16], s_l[kMWaves][16];
+    if (n < qw) {
+#pragma unroll
+        for (int hh = 0; hh < VH; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm)
+                    s_o[wave][n][128 * hh + 32 * q + 8 * r + mm] = o[hh * 8 + mm][r];
+        if (q == 0) {
+            s_m[wave][n] = m_run;
+            s_l[wave][n] = l_run;
+        }
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < qw * (D / 8); idx += kMBlock) {
+        const int jq = idx / (D / 8);
+        const int d0 = (idx % (D / 8)) * 8;
+        float M = s_m[0][jq];
+#pragma unroll
+        for (int w = 1; w < kMWaves; ++w) M = fmaxf(M, s_m[w][jq]);
+        float wt[kMWaves], lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kMWaves; ++w) {
+            wt[w] = fast_exp2(s_m[w][jq] - M);
+            lsum += s_l[w][jq] * wt[w];
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        float ov[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int w = 0; w < kMWaves; ++w) a = fmaf(s_o[w][jq][d0 + i], wt[w], a);
+            ov[i] = a * inv;
+        }
+        const int h = h0 + jq;
+        if constexpr (!SPLIT) {
+            u32x4 pk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
+            *reinterpret_cast<u32x4*>(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0) = pk;
+        } else {
+            const int64_t slot = ((int64_t)b * p.Hq + h) * p.n_part + part;
+            float* op = p.part_o + slot * D + d0;
+            *reinterpret_cast<float4*>(op) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+            *reinterpret_cast<float4*>(op + 4) = make_float4(ov[4], ov[5], ov[6], ov[7]);
+            if (d0 == 0) p.part_lse[slot] = lsum > 0.f ? M + __log2f(lsum) : -INFINITY;
+        }
+    }
+}
+
+bool mfma_supported(int head_dim, int qw) {
+    return (head_dim == 128 || head_dim == 256) && qw >= 1 && qw <= 16;
+}
+
+template <int D, bool SPLIT, bool PAGE16>
+static hipError_t launch_mfma_t(const DecodeParams& p, int qw, hipStream_t s) {
+    dim3 grid((uint32_t)((int64_t)p.n_part * (p.Hq / qw) * p.B));
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16>), grid, dim3(kMBlock),
+                       pages_lds_bytes(p), s, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_mfma_d(const DecodeParams& p, int qw, bool split, hipStream_t s) {
+    // Tiles start at multiples of 16 tokens (partitions at multiples of 64);
+    // in-page offsets must fit 32 bits.
+    const bool page16 = p.p_shift >= 4 && (int64_t)p.P * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) < (1ll << 30);
+    if (split) return page16 ? launch_mfma_t<D, true, true>(p, qw, s) : launch_mfma_t<D, true, false>(p, qw, s);
+    return page16 ? launch_mfma_t<D, false, true>(p, qw, s) : launch_mfma_t<D, false, false>(p, qw, s);
+}
+
+hipError_t launch_mfma(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s) {
+    if (!mfma_supported(head_dim, qw) || p.Hq % qw) return hipErrorInvalidValue;
+    if (head_dim == 128) return launch_mfma_d<128>(p, qw, split, s);
+    return launch_mfma_d<256>(p, qw, split, s);
 }
 
 }  // namespace pa

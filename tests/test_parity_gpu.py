@@ -18,7 +18,7 @@ from workloads import WORKLOADS, custom, make_inputs, to_device
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["valu"]
+VARIANTS = ["valu", "mfma"]
 
 
 def bits(t):
@@ -251,3 +251,36 @@ def test_device_errors_do_not_stick():
                      torch.empty_like(q))
     y, _ = gpu_run(d)
     assert_parity(y, oracle_run(inp), "after error")
+
+
+def test_graph_capture_replays_match_eager():
+    """Calls captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, equals the eager result bit for bit."""
+    inp = make_inputs("single_seq", seed=2)
+    d = to_device(inp)
+    q, k, v = d.call(3)
+    eager = pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    ws = torch.empty(pa.pa_decode_workspace_bytes(1, 16, 8, 128, d.block_tables.shape[1], 16,
+                                                  pa.make_opts()) + 256,
+                     dtype=torch.uint8, device="cuda")
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, workspace=ws)
+    for i in range(4):
+        out.zero_()
+        junk = pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale * 0.5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        assert not torch.equal(junk, eager)
