@@ -28,11 +28,38 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "paged-attn decode µs/call + achieved KV-read GB/s (% of MI355X HBM peak)"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources and build script; a profile's HBM
+    traffic is only reported while the kernels still hash to it."""
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "paged_attention_decode_04_amd")
+    files = sorted(os.listdir(os.path.join(pkg, "csrc")))
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(pkg, "csrc", f), "rb").read())
+    h.update(open(os.path.join(pkg, "build.py"), "rb").read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str, partition_tokens: int):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None if absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"pa_decode_mfma_{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    if doc.get("source_sha256") != kernel_source_hash() or doc.get("partition_tokens") != partition_tokens:
+        return None
+    return int(round(doc["traffic_bytes_per_launch"]))
 
 
 def parse():
@@ -133,8 +160,10 @@ def per_config(pa, variant, partition_tokens, torch, workloads_mod):
             ms = event_time_ms(calls[0], 10, torch) / 10
             entry["us_per_call"] = round(1e3 * ms, 2)
         else:
-            reps = max(3, int(20000 // max(1, n_calls)))
-            entry["us_per_call"] = round(graph_time_us(calls, min(reps, 200), torch), 3)
+            # one graph of at least 64 calls, so graph-launch cost is amortised
+            warm = calls * max(1, -(-64 // n_calls))
+            reps = max(3, min(200, int(20000 // len(warm))))
+            entry["us_per_call"] = round(graph_time_us(warm, reps, torch), 3)
             footprint = kvb * (w.layers if w.layers > 1 else 1)
             R = min(int(np.ceil(1.0e9 / max(footprint, 1))), 64)
             if R > 1:
@@ -302,7 +331,9 @@ def main():
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": (profiled_traffic(w.name, int(st["last_partition_tokens"]))
+                        if variant == "mfma" else None),
             "kernel": kernel + (" + pa_lse_merge_kernel" if st["merge_launches"] else ""),
             "duration_us": round(us_per_call_ev, 3),
             "note": "achieved = algorithmic KV bytes per call / HIP-event time per call over the "

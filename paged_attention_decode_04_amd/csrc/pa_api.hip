@@ -143,9 +143,13 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
 
 Plan make_plan(const Geometry& g, const pa_opts* opts) {
     Plan pl{};
-    pl.variant = (opts && opts->variant) ? opts->variant : PA_VARIANT_VALU;
+    const int qw_mfma = g.qg < 16 ? g.qg : 16;
+    if (opts && opts->variant)
+        pl.variant = opts->variant;
+    else
+        pl.variant = pa::mfma_supported((int)g.D, qw_mfma) ? PA_VARIANT_MFMA : PA_VARIANT_VALU;
     if (pl.variant == PA_VARIANT_MFMA)
-        pl.qw = g.qg < 16 ? g.qg : 16;          // one 16-column MFMA tile of queries
+        pl.qw = qw_mfma;                        // one 16-column MFMA tile of queries
     else
         pl.qw = g.qg < 8 ? g.qg : 8;
     const int64_t max_ctx = std::max<int64_t>(g.max_blk * g.P, 1);
@@ -153,6 +157,12 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     int64_t T;
     if (opts && opts->partition_tokens > 0) {
         T = (int64_t)opts->partition_tokens;
+    } else if (pl.variant == PA_VARIANT_MFMA) {
+        // Few, long partitions: each workgroup's fixed cost (page-table
+        // fetch, LDS merge, partial write) is paid per partition, so aim for
+        // about one workgroup per CU of work, partitions of 512..4096 tokens.
+        T = (max_ctx * groups + 255) / 256;
+        T = std::max<int64_t>(512, std::min<int64_t>(T, 4096));
     } else {
         // Aim for ~1024 workgroups; partitions of 64..1024 tokens.
         T = (max_ctx * groups + 1023) / 1024;

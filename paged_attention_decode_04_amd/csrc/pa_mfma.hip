@@ -5,16 +5,17 @@
 // tiles of the partition (tile j goes to wave j mod 4) and keeps its own
 // online-softmax state.  Per tile:
 //
-//   S^T (16 tokens x 16 queries) = K_tile (16 x D) . Q^T (D x 16)
-//       v_mfma_f32_16x16x32_bf16, D/32 steps.  The K rows go straight from
-//       global memory into the A operand: lane l supplies token l%16 and the
-//       16 bytes [64 kk + 16 (l/16), +16) of its row, i.e. 16 rows x 64
-//       contiguous bytes per load instruction.  Q^T (bf16, unscaled) is the
-//       B operand, loaded once; query columns past the group are zero.
-//   The C tile gives lane l the logits of query l%16 for tokens
-//   4 (l/16) + r, r = 0..3.  Scale (times log2 e), mask the tail, take the
-//   tile max across the four 16-lane rows (permlane16/32 swaps), update the
-//   running max m and sum l, rescale the accumulators, p = 2^(s - m).
+//   Logits on v_mfma_f32_16x16x32_bf16, with K rows going straight from
+//   global memory into the A operand and Q (bf16, unscaled) as the B operand,
+//   loaded once.  Two row layouts:
+//   * qg <= 8 ("split" layout): the 16 MFMA rows are 8 tokens x 2 halves of
+//     each 64-dim block and the 16 B columns are 8 queries x the same 2
+//     halves, so 8 lanes read one whole 128-byte line of a K row per load (8
+//     full lines per instruction).  The diagonal (half, half) blocks of the C
+//     tile are the two partial dot products; a permlane32 swap plus a DPP
+//     row rotate by 8 adds them, and a second swap deals the 16 tokens of
+//     two such tiles out so lane l holds query l%16, tokens 4 (l/16) + r.
+//   * qg 9..16: row = token, column = query, 16 rows x 64 bytes per load.
 //   O^T (D x 16) += V^T_tile (D x 16 tokens) . P^T (16 x 16)
 //       v_mfma_f32_16x16x16_bf16, D/16 steps.  P^T is exactly the C tile
 //       held as bf16 (lane l: query l%16, tokens 4 (l/16) + jj).  V^T: lane l
@@ -63,30 +64,49 @@ __device__ __forceinline__ int64_t row_offset(const DecodeParams& p, const int* 
 }
 
 // Per-lane 32-bit element offsets inside one page, fixed for the whole
-// kernel: K row n (chunk q) and the four V rows 4q + jj (chunk n).
+// kernel: the lane's K row and chunk, and the four V rows 4q + jj (chunk n).
 struct LaneOffsets {
     int k;
     int v[4];
 };
 
-// Issue the loads of the 16-token tile starting at tb.  K: token tb + n
-// (A operand rows); V: tokens tb + 4q + jj (16 lanes per row).  Tokens at or
-// past te are clamped to te - 1, a real row, and masked out of the softmax.
-// PAGE16: the page size is a power of two >= 16, so the tile lies in one page;
-// the page base is wave-uniform and each lane adds a fixed 32-bit offset.
-template <int D, bool PAGE16>
+// K row (token offset inside the tile) and element offset inside the row of
+// load i (0 .. D/32 - 1) of lane (n, q).
+template <int D, bool HALF>
+__device__ __forceinline__ int k_row(int i, int n) {
+    if constexpr (HALF) return (i / (D / 64)) * 8 + (n & 7);
+    else return n;
+}
+template <int D, bool HALF>
+__device__ __forceinline__ int k_col(int i, int n, int q) {
+    if constexpr (HALF) return 64 * (i % (D / 64)) + 32 * (n >> 3) + 8 * q;
+    else return 32 * i + 8 * q;
+}
+
+// Issue the loads of the 16-token tile starting at tb.  K: see k_row/k_col
+// (A operand layout); V: tokens tb + 4q + jj, 16 lanes per row.  Tokens at
+// or past te are clamped to te - 1, a real row, and masked out of the
+// softmax.  PAGE16: the page size is a power of two >= 16, so the tile lies
+// in one page; the page base is wave-uniform and each lane adds a fixed
+// 32-bit offset.
+template <int D, bool PAGE16, bool HALF>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pages, int pg0, int g,
                                           int n, int q, const LaneOffsets& lo, int tb, int te,
                                           TileFrag<D>& f) {
+    constexpr int KK = TileFrag<D>::KK;
     if constexpr (PAGE16) {
         const int lp = tb >> p.p_shift;
         const int page = __builtin_amdgcn_readfirstlane(s_pages[lp - pg0]);
         const int slot0 = tb - (lp << p.p_shift);
         const uint16_t* kt = p.k + (int64_t)page * p.k_sp + (int64_t)g * p.k_sh + (int64_t)slot0 * p.k_ss;
         const uint16_t* vt = p.v + (int64_t)page * p.v_sp + (int64_t)g * p.v_sh + (int64_t)slot0 * p.v_ss;
+        const int ks = (int)p.k_ss, vs = (int)p.v_ss;
         if (tb + kTile <= te) {                 // full tile (wave-uniform)
 #pragma unroll
-            for (int kk = 0; kk < TileFrag<D>::KK; ++kk) f.k[kk] = load16_nt(kt + lo.k + 32 * kk);
+            for (int i = 0; i < KK; ++i) {
+                const int extra = HALF ? (i / (D / 64)) * 8 * ks + 64 * (i % (D / 64)) : 32 * i;
+                f.k[i] = load16_nt(kt + lo.k + extra);
+            }
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
@@ -94,10 +114,9 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pa
                     f.v[jj][hh] = load16_nt(vt + lo.v[jj] + 128 * hh);
         } else {                                // tail tile: clamp rows to te - 1
             const int last = te - 1 - tb;
-            const int ks = (int)p.k_ss, vs = (int)p.v_ss;
-            const int ko = min(n, last) * ks + 8 * q;
 #pragma unroll
-            for (int kk = 0; kk < TileFrag<D>::KK; ++kk) f.k[kk] = load16_nt(kt + ko + 32 * kk);
+            for (int i = 0; i < KK; ++i)
+                f.k[i] = load16_nt(kt + min(k_row<D, HALF>(i, n), last) * ks + k_col<D, HALF>(i, n, q));
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int vo = min(4 * q + jj, last) * vs + 8 * n;
@@ -107,10 +126,12 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pa
         }
     } else {
         const int64_t gk = (int64_t)g * p.k_sh, gv = (int64_t)g * p.v_sh;
-        const int tk = min(tb + n, te - 1);
-        const uint16_t* kr = p.k + row_offset(p, s_pages, pg0, tk, p.k_sp, p.k_ss, gk) + 8 * q;
 #pragma unroll
-        for (int kk = 0; kk < TileFrag<D>::KK; ++kk) f.k[kk] = load16_nt(kr + 32 * kk);
+        for (int i = 0; i < KK; ++i) {
+            const int tk = min(tb + k_row<D, HALF>(i, n), te - 1);
+            f.k[i] = load16_nt(p.k + row_offset(p, s_pages, pg0, tk, p.k_sp, p.k_ss, gk) +
+                               k_col<D, HALF>(i, n, q));
+        }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int tv = min(tb + 4 * q + jj, te - 1);
@@ -129,6 +150,17 @@ __device__ __forceinline__ float xmax32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// Value of lane l + 32 (meaningful in lanes 0..31) / of lane l - 32 (in 32..63).
+__device__ __forceinline__ float from_hi32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float from_lo32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]);
+}
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8 (lane i <- lane (i + 8) mod 16)
+
 __device__ __forceinline__ float xsum16(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -139,24 +171,50 @@ __device__ __forceinline__ float xsum32(float x) {
 }
 
 // One 16-token tile: logits on MFMA, online-softmax update, O^T += V^T P^T.
-template <int D>
+template <int D, bool HALF>
 __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<D>& cur,
                                           const u32x4 (&qop)[D / 32], int tb, int te, int q,
-                                          f32x4 (&o)[D / 16], float& m_run, float& l_run) {
+                                          bool col_live, f32x4 (&o)[D / 16], float& m_run,
+                                          float& l_run) {
     constexpr int KK = TileFrag<D>::KK;
     constexpr int VH = TileFrag<D>::VH;
     constexpr int NO = D / 16;
-    // logits S^T: lane -> query n, tokens tb + 4q + r
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    // logits: lane (n, q) ends with query n, tokens tb + 4q + r
+    f32x4 s;
+    if constexpr (HALF) {
+        constexpr int KH = D / 64;
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[kk]),
-                                                    __builtin_bit_cast(bf16x8, qop[kk]), s, 0, 0, 0);
+        for (int kk = 0; kk < KH; ++kk) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[kk]),
+                                                         __builtin_bit_cast(bf16x8, qop[kk]), c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[KH + kk]),
+                                                         __builtin_bit_cast(bf16x8, qop[kk]), c1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            // (token, half 0) sits in lane (n, q<2), (token, half 1) in lane (n+8, q+2)
+            // Every cross-lane move runs with all 64 lanes active: evaluate
+            // both candidates first, then select (a conditional operand would
+            // become a branch, and a lane swap under a partial exec mask reads
+            // inactive lanes).
+            const float f0 = c0[r] + dpp_mov<kDppRowRor8>(from_hi32(c0[r]));
+            const float f1 = c1[r] + dpp_mov<kDppRowRor8>(from_hi32(c1[r]));
+            const float f1_lo = from_lo32(f1);
+            s[r] = q < 2 ? f0 : f1_lo;
+        }
+    } else {
+        s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[kk]),
+                                                        __builtin_bit_cast(bf16x8, qop[kk]), s, 0, 0, 0);
+    }
     float sv[4];
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        sv[r] = (tb + 4 * q + r < te) ? s[r] * p.scale_log2 : -INFINITY;
+        sv[r] = (col_live && tb + 4 * q + r < te) ? s[r] * p.scale_log2 : -INFINITY;
         mt = fmaxf(mt, sv[r]);
     }
     mt = xmax32(xmax16(mt));
@@ -197,7 +255,7 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
         }
 }
 
-template <int D, bool SPLIT, bool PAGE16>
+template <int D, bool SPLIT, bool PAGE16, bool HALF, int NBUF>
 __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p) {
     constexpr int KK = TileFrag<D>::KK;
     constexpr int VH = TileFrag<D>::VH;
@@ -215,7 +273,8 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     const int qw = p.qw;                        // query heads of this workgroup (<= 16)
     const int h0 = qb * qw;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int n = lane & 15, q = lane >> 4;
     const int g = h0 / (p.Hq / p.Hkv);
 
@@ -236,14 +295,21 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
             s_pages[i] = clampi(btrow[pg0 + i], 0, p.num_pages - 1);
     }
 
-    // Q^T as the B operand: column n = query h0 + n, 8 dims per lane per step.
+    // Q^T as the B operand (same k <-> dim map as the K rows of the layout).
+    // Columns past the group are zero.
     u32x4 qop[KK];
+    const int qcol = HALF ? (n & 7) : n;
+    const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
     {
-        const bool live = n < qw;
-        const uint16_t* qr = p.q + (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? n : 0)) * p.q_sh + 8 * q;
+        const bool live = qcol < qw;
+        const uint16_t* qr = p.q + (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? qcol : 0)) * p.q_sh;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            u32x4 w = load16(qr + 32 * kk);
+            if (HALF && kk >= D / 64) {
+                qop[kk] = u32x4{0u, 0u, 0u, 0u};          // unused in the split layout
+                continue;
+            }
+            u32x4 w = load16(qr + k_col<D, HALF>(kk, n, q));
             qop[kk] = live ? w : u32x4{0u, 0u, 0u, 0u};
         }
     }
@@ -256,33 +322,37 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
 
     const int n_tiles = (n_tok + kTile - 1) / kTile;
     LaneOffsets lo;
-    lo.k = n * (int)p.k_ss + 8 * q;
+    lo.k = k_row<D, HALF>(0, n) * (int)p.k_ss + k_col<D, HALF>(0, n, q);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
-    // Ping-pong between two register buffers: the next tile's loads are
-    // always issued before the current tile is consumed, with no copies
-    // between buffers (so the waits cover only the current tile).
-    int j = wave;
-    if (j < n_tiles) {
-        TileFrag<D> fa, fb;
-        load_tile<D, PAGE16>(p, s_pages, pg0, g, n, q, lo, ts + j * kTile, te, fa);
-        while (true) {
-            if (j + kMWaves >= n_tiles) {
-                tile_step<D>(p, fa, qop, ts + j * kTile, te, q, o, m_run, l_run);
-                break;
-            }
-            load_tile<D, PAGE16>(p, s_pages, pg0, g, n, q, lo, ts + (j + kMWaves) * kTile, te, fb);
+    // This wave's tiles are j_k = wave + 4k, k < n_my.  Rotate through NBUF
+    // register buffers so NBUF - 1 tiles' loads are in flight while one is
+    // consumed.  The steady-state loop issues its prefetches unconditionally
+    // (so each wait covers exactly the tile being consumed); the last few
+    // tiles drain in a short unrolled tail.  No data moves between buffers.
+    const int n_my = n_tiles > wave ? (n_tiles - wave + kMWaves - 1) / kMWaves : 0;
+    auto tile_tb = [&](int k) { return ts + (wave + k * kMWaves) * kTile; };
+    TileFrag<D> fb[NBUF];
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+        if (i < n_my) load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(i), te, fb[i]);
+    int k = 0;
+    for (; k + 2 * NBUF - 2 < n_my; k += NBUF) {
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) {
+            load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
+                                 fb[(i + NBUF - 1) % NBUF]);
             __builtin_amdgcn_sched_barrier(0);
-            tile_step<D>(p, fa, qop, ts + j * kTile, te, q, o, m_run, l_run);
-            j += kMWaves;
-            if (j + kMWaves >= n_tiles) {
-                tile_step<D>(p, fb, qop, ts + j * kTile, te, q, o, m_run, l_run);
-                break;
-            }
-            load_tile<D, PAGE16>(p, s_pages, pg0, g, n, q, lo, ts + (j + kMWaves) * kTile, te, fa);
-            __builtin_amdgcn_sched_barrier(0);
-            tile_step<D>(p, fb, qop, ts + j * kTile, te, q, o, m_run, l_run);
-            j += kMWaves;
+            tile_step<D, HALF>(p, fb[i], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NBUF - 1; ++i) {
+        if (k + i < n_my) {
+            if (k + i + NBUF - 1 < n_my)
+                load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
+                                     fb[(i + NBUF - 1) % NBUF]);
+            tile_step<D, HALF>(p, fb[i % NBUF], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
         }
     }
 
@@ -352,8 +422,13 @@ bool mfma_supported(int head_dim, int qw) {
 template <int D, bool SPLIT, bool PAGE16>
 static hipError_t launch_mfma_t(const DecodeParams& p, int qw, hipStream_t s) {
     dim3 grid((uint32_t)((int64_t)p.n_part * (p.Hq / qw) * p.B));
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16>), grid, dim3(kMBlock),
-                       pages_lds_bytes(p), s, p);
+    constexpr int NBUF = D == 128 ? 3 : 2;
+    if (qw <= 8)
+        hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16, true, NBUF>), grid, dim3(kMBlock),
+                           pages_lds_bytes(p), s, p);
+    else
+        hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16, false, NBUF>), grid, dim3(kMBlock),
+                           pages_lds_bytes(p), s, p);
     return hipGetLastError();
 }
 

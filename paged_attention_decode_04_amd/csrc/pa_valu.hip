@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
     const int h0 = blockIdx.y * QW;
     const int b = blockIdx.z;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int row = lane >> 4, c = lane & 15;
     const int qg = p.Hq / p.Hkv;
     const int g = h0 / qg;
