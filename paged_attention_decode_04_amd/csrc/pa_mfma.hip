@@ -278,22 +278,25 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     const int n = lane & 15, q = lane >> 4;
     const int g = h0 / (p.Hq / p.Hkv);
 
-    const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+    // Page ids of the partition's token range are fetched without waiting for
+    // the sequence length (entries past the sequence's end are never used),
+    // so the two dependent reads of the prologue overlap.
     const int ts = part * p.part_tokens;
+    extern __shared__ int s_pages[];
+    int pg0, unused;
+    page_slot(p, ts, pg0, unused);
+    {
+        int lp_hi;
+        page_slot(p, ts + p.part_tokens - 1, lp_hi, unused);
+        lp_hi = min(lp_hi, p.max_blk - 1);
+        const int32_t* btrow = p.bt + (int64_t)b * p.bt_sb;
+        for (int i = tid; i <= lp_hi - pg0; i += kMBlock)
+            s_pages[i] = clampi(btrow[pg0 + i], 0, p.num_pages - 1);
+    }
+    const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     if (ts >= L && part > 0) return;
     const int te = min(L, ts + p.part_tokens);
     const int n_tok = max(te - ts, 0);
-
-    extern __shared__ int s_pages[];
-    int pg0 = 0;
-    if (n_tok > 0) {
-        int lp_last, unused;
-        page_slot(p, ts, pg0, unused);
-        page_slot(p, te - 1, lp_last, unused);
-        const int32_t* btrow = p.bt + (int64_t)b * p.bt_sb;
-        for (int i = tid; i <= lp_last - pg0; i += kMBlock)
-            s_pages[i] = clampi(btrow[pg0 + i], 0, p.num_pages - 1);
-    }
 
     // Q^T as the B operand (same k <-> dim map as the K rows of the layout).
     // Columns past the group are zero.
