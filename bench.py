@@ -50,14 +50,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def profiled_traffic(workload: str, partition_tokens: int):
+def profiled_traffic(kernel: str, workload: str, launch: dict):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None if absent or taken on other kernel sources."""
-    path = os.path.join(PROFILES, f"pa_decode_mfma_{workload}.traffic.json")
+    WRITE_SIZE summary of this kernel and workload, or None if absent, taken
+    on other kernel sources or in another launch configuration."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     doc = json.load(open(path))
-    if doc.get("source_sha256") != kernel_source_hash() or doc.get("partition_tokens") != partition_tokens:
+    if doc.get("source_sha256") != kernel_source_hash() or doc.get("launch") != launch:
         return None
     return int(round(doc["traffic_bytes_per_launch"]))
 
@@ -70,6 +71,8 @@ def parse():
     ap.add_argument("--workload", default="long_ctx_gqa8")
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "partitions", "balanced"])
+    ap.add_argument("--shares", type=int, default=0, help="balanced schedule: shares (0 = automatic)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
@@ -84,14 +87,15 @@ def parse():
 
 
 # ----------------------------------------------------------------------------
-def make_call(pa, d, call, variant, partition_tokens):
-    """A closure issuing one decode call on the current stream."""
+def make_call(pa, d, call, knobs):
+    """A closure issuing one decode call on the current stream; knobs are
+    make_opts' keyword arguments (variant, partition_tokens, schedule, shares)."""
     import torch
     q, k, v = d.call(call)
     out = torch.empty_like(q)
     B, Hq, D = q.shape
     NP, P, Hkv, _ = k.shape
-    opts = pa.make_opts(variant, partition_tokens)
+    opts = pa.make_opts(**knobs)
     n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, opts)
     ws = None
     if n:
@@ -137,7 +141,23 @@ def graph_time_us(calls, reps, torch):
 
 
 # ----------------------------------------------------------------------------
-def per_config(pa, variant, partition_tokens, torch, workloads_mod):
+def launch_info(st):
+    """Kernel names and launch configuration of the last call, from the counters."""
+    variant = {1: "valu", 2: "mfma"}.get(int(st["last_variant"]), "?")
+    balanced = int(st["last_schedule"]) == 2
+    if variant == "valu":
+        kernel, merge = "pa_decode_valu_kernel", "pa_lse_merge_kernel"
+    elif balanced:
+        kernel, merge = "pa_decode_mfma_lean_kernel", "pa_lean_merge_kernel"
+    else:
+        kernel, merge = "pa_decode_mfma_kernel", "pa_lse_merge_kernel"
+    launch = {"variant": variant, "schedule": "balanced" if balanced else "partitions",
+              "partition_tokens": int(st["last_partition_tokens"]),
+              ("shares" if balanced else "partitions"): int(st["last_num_partitions"])}
+    return kernel, (merge if st["merge_launches"] else None), launch
+
+
+def per_config(pa, knobs, torch, workloads_mod):
     """Time every workload: warm (inputs reused, MALL may hold them) and, for
     footprints that fit the 256 MB MALL, cold (calls rotate over replicas of
     the KV pools totalling >= 1 GB)."""
@@ -152,8 +172,7 @@ def per_config(pa, variant, partition_tokens, torch, workloads_mod):
         lens = d.layout.context_lens
         kvb = workloads_mod.kv_bytes(w, lens)
         n_calls = w.calls if w.calls > 1 else 1
-        calls = [make_call(pa, d, i, variant, partition_tokens)[0] for i in range(n_calls)]
-        st = pa.pa_get_stats()
+        calls = [make_call(pa, d, i, knobs)[0] for i in range(n_calls)]
         entry = {"kv_bytes_per_call": kvb, "calls": n_calls}
         if name == "long_ctx_gqa8":
             ms = event_time_ms(calls[0], 3, torch)
@@ -177,15 +196,14 @@ def per_config(pa, variant, partition_tokens, torch, workloads_mod):
                 cold_calls = []
                 for i in range(n_calls):
                     for d2 in reps_k:
-                        cold_calls.append(make_call(pa, d2, i, variant, partition_tokens)[0])
+                        cold_calls.append(make_call(pa, d2, i, knobs)[0])
                 cold_calls = cold_calls[:min(len(cold_calls), max(R, 2048))]
                 entry["us_per_call_cold"] = round(graph_time_us(cold_calls, 5, torch), 3)
                 entry["cold_replicas"] = R
                 del reps_k
-        st2 = pa.pa_get_stats()
-        entry["partition_tokens"] = int(st2["last_partition_tokens"])
-        entry["partitions"] = int(st2["last_num_partitions"])
-        entry["variant"] = {1: "valu", 2: "mfma"}.get(int(st2["last_variant"]), "?")
+        kernel, _, launch = launch_info(pa.pa_get_stats())
+        entry["kernel"] = kernel
+        entry.update(launch)
         for key in ("us_per_call", "us_per_call_cold"):
             if key in entry:
                 gbs = kvb / (entry[key] * 1e-6) / 1e9
@@ -273,7 +291,9 @@ def main():
     log(f"[bench] inputs for {w.name} ready in {time.perf_counter() - t_gen:.1f}s")
     kvb_per_call = wl.kv_bytes(w, d.layout.context_lens)
     n_calls = w.calls
-    calls = [make_call(pa, d, i, args.variant, args.partition_tokens)[0] for i in range(n_calls)]
+    knobs = dict(variant=args.variant, partition_tokens=args.partition_tokens,
+                 schedule=args.schedule, shares=args.shares)
+    calls = [make_call(pa, d, i, knobs)[0] for i in range(n_calls)]
 
     def step():                       # one pass of the whole path over the batch
         for c in calls:
@@ -299,12 +319,11 @@ def main():
     kv_per_step = kvb_per_call * n_calls
     value = kv_per_step / (ms_per_step * 1e-3) / 1e9
     achieved = kvb_per_call / (us_per_call_ev * 1e-6) / 1e9
-    variant = {1: "valu", 2: "mfma"}.get(int(st["last_variant"]), "?")
+    kernel, merge, launch = launch_info(st)
+    variant = launch["variant"]
     log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step wall, {us_per_call_ev:.2f} us/call (events), "
-        f"{achieved:.0f} GB/s KV, variant {variant}, T={st['last_partition_tokens']} "
-        f"x {st['last_num_partitions']}")
+        f"{achieved:.0f} GB/s KV, {kernel} {launch}")
 
-    kernel = ("pa_decode_valu_kernel" if variant == "valu" else "pa_decode_mfma_kernel")
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -323,18 +342,15 @@ def main():
             "workload": w.name, "desc": w.desc, "batch": w.batch,
             "sum_ctx": int(d.layout.context_lens.sum()), "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
-            "calls_per_step": n_calls, "kv_bytes_per_call": kvb_per_call, "variant": variant,
-            "partition_tokens": int(st["last_partition_tokens"]),
-            "partitions": int(st["last_num_partitions"]),
+            "calls_per_step": n_calls, "kv_bytes_per_call": kvb_per_call, **launch,
         },
         "us_per_call": round(us_per_call_ev, 3),
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (profiled_traffic(w.name, int(st["last_partition_tokens"]))
-                        if variant == "mfma" else None),
-            "kernel": kernel + (" + pa_lse_merge_kernel" if st["merge_launches"] else ""),
+            "traffic": profiled_traffic(kernel, w.name, launch),
+            "kernel": kernel + (f" + {merge}" if merge else ""),
             "duration_us": round(us_per_call_ev, 3),
             "note": "achieved = algorithmic KV bytes per call / HIP-event time per call over the "
                     "timed region (decode kernel plus merge kernel, on the launch stream)",
@@ -344,7 +360,7 @@ def main():
         result["copy_probe"] = copy_probe(args.copy_probe_mib, torch)
         log(f"[bench] copy probe: {result['copy_probe']}")
     if not args.profile and not args.no_per_config:
-        result["per_config"] = per_config(pa, args.variant, args.partition_tokens, torch, wl)
+        result["per_config"] = per_config(pa, knobs, torch, wl)
     if not args.profile and not args.no_cpu_baseline:
         t = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds, wl)

@@ -99,10 +99,16 @@ typedef struct pa_tensor {
  * [0, NP), so a violation gives unspecified output, never an out-of-range
  * access.
  *
- * Long contexts are split into partitions whose partial results are merged
- * by a second kernel (log-sum-exp merge); the library keeps a per-device
- * workspace for those partials, grown on demand with hipMalloc and freed by
- * pa_release().  Returns PA_OK or an error code above.
+ * Work is split over workgroups either as fixed-size partitions of each
+ * sequence or, on the MFMA variant, as equal shares of all sequences' work
+ * (chosen automatically for large calls: at most 4096 sequences and at
+ * least 131072 units of (sequence, query block, 16 tokens of capacity
+ * MaxBlk * P)); partial results are
+ * merged with the log-sum-exp rule by a second kernel.  The library keeps a
+ * per-device workspace for the partials, grown on demand with hipMalloc and
+ * freed by pa_release(); calls that use it must not overlap in time on one
+ * device (callers that overlap calls pass their own workspaces to
+ * pa_decode_ex).  Returns PA_OK or an error code above.
  */
 int pa_decode(const pa_tensor* q,
               const pa_tensor* k_cache,
@@ -122,12 +128,24 @@ int pa_decode(const pa_tensor* q,
 #define PA_VARIANT_VALU  1   /* vector-ALU kernel (any supported qg)            */
 #define PA_VARIANT_MFMA  2   /* matrix-core kernel (bf16 MFMA for Q.K and P.V)  */
 
+#define PA_SCHEDULE_AUTO        0  /* the library picks                         */
+#define PA_SCHEDULE_PARTITIONS  1  /* one workgroup per fixed-size partition of
+                                      each sequence (split-KV partitions)      */
+#define PA_SCHEDULE_BALANCED    2  /* MFMA only: the work of all sequences cut
+                                      into equal shares, one per workgroup     */
+
 typedef struct pa_opts {
     int32_t variant;            /* PA_VARIANT_*                                */
     int32_t partition_tokens;   /* 0 = automatic; else tokens per split-KV
                                    partition, a multiple of 64 (rounded up).
-                                   A value >= MaxBlk * P disables the split.   */
-    int32_t reserved[6];        /* must be zero                                */
+                                   A value >= MaxBlk * P disables the split.
+                                   Setting it selects the partition schedule
+                                   unless schedule says otherwise.             */
+    int32_t schedule;           /* PA_SCHEDULE_*                               */
+    int32_t shares;             /* balanced schedule: 0 = automatic (one per
+                                   compute unit at most), else the number of
+                                   shares (workgroups), 1 .. 1024              */
+    int32_t reserved[4];        /* must be zero                                */
 } pa_opts;
 
 /*
@@ -189,9 +207,13 @@ typedef struct pa_stats {
     uint64_t mfma_launches;     /* decode-kernel launches, MFMA variant        */
     uint64_t split_calls;       /* calls that split the context                */
     uint64_t merge_launches;    /* log-sum-exp merge kernel launches           */
-    uint64_t last_partition_tokens; /* partition size of the last call         */
-    uint64_t last_num_partitions;   /* partitions of the last call (grid x)    */
+    uint64_t last_partition_tokens; /* partition size of the last call (0 on the
+                                       balanced schedule)                      */
+    uint64_t last_num_partitions;   /* partitions of the last call, or shares
+                                       (workgroups) on the balanced schedule   */
     uint64_t last_variant;          /* PA_VARIANT_* of the last call           */
+    uint64_t balanced_calls;        /* calls run on the balanced schedule      */
+    uint64_t last_schedule;         /* PA_SCHEDULE_* of the last call          */
 } pa_stats;
 
 int  pa_get_stats(pa_stats* stats);   /* PA_EINVAL if stats is NULL            */

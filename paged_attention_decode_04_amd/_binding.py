@@ -19,6 +19,9 @@ PA_OK, PA_EINVAL, PA_ENOTSUP, PA_EALIGN, PA_ENODEV, PA_ENOMEM, PA_EHIP = range(7
 PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32 = 1, 2, 3
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 VARIANTS = {"auto": PA_VARIANT_AUTO, "valu": PA_VARIANT_VALU, "mfma": PA_VARIANT_MFMA}
+PA_SCHEDULE_AUTO, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED = 0, 1, 2
+SCHEDULES = {"auto": PA_SCHEDULE_AUTO, "partitions": PA_SCHEDULE_PARTITIONS,
+             "balanced": PA_SCHEDULE_BALANCED}
 
 
 class PaTensor(ctypes.Structure):
@@ -28,13 +31,15 @@ class PaTensor(ctypes.Structure):
 
 class PaOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("schedule", ctypes.c_int32), ("shares", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 class PaStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
-        "last_partition_tokens", "last_num_partitions", "last_variant")]
+        "last_partition_tokens", "last_num_partitions", "last_variant", "balanced_calls",
+        "last_schedule")]
 
 
 class PaError(RuntimeError):
@@ -125,10 +130,12 @@ def _require_device(*ts):
             raise ValueError("all tensors must live on the same GPU device")
 
 
-def make_opts(variant="auto", partition_tokens: int = 0) -> PaOpts:
+def make_opts(variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0) -> PaOpts:
     o = PaOpts()
+    o.shares = int(shares)
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     o.partition_tokens = int(partition_tokens)
+    o.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
     return o
 
 
@@ -206,7 +213,8 @@ def pa_release() -> None:
 
 # ------------------------------------------------------------------ convenience
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None, *,
-           variant="auto", partition_tokens: int = 0, workspace=None, stream=None):
+           variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0,
+           workspace=None, stream=None):
     """Decode paged attention on torch tensors.
 
     q [B, Hq, D] bf16; k_cache/v_cache [NP, P, Hkv, D] bf16 (NHD pool);
@@ -221,7 +229,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    opts = make_opts(variant, partition_tokens)
+    opts = make_opts(variant, partition_tokens, schedule, shares)
     if workspace is None:
         n = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], P, opts)
         if n:

@@ -35,8 +35,8 @@ int fail(int code, const char* fmt, ...) {
 }
 
 struct Counters {
-    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0};
-    std::atomic<uint64_t> last_t{0}, last_np{0}, last_variant{0};
+    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0}, lean{0};
+    std::atomic<uint64_t> last_t{0}, last_np{0}, last_variant{0}, last_schedule{0};
 } g_stats;
 
 // Validated call geometry.
@@ -53,9 +53,25 @@ struct Plan {
     bool split;
     size_t ws_bytes;
     size_t lse_offset;  // byte offset of the lse array inside the workspace
+    bool lean;          // balanced schedule (MFMA): shares instead of partitions
+    bool n_part_fixed;  // balanced schedule: share count given by the caller
+    size_t meta_offset; // balanced schedule: byte offset of the tile prefix sums
 };
 
+// Balanced schedule: at most this many shares (workgroups) per call, so the
+// workspace size does not depend on the device it runs on.
+constexpr int kLeanMaxShares = 1024;
+constexpr int kLeanMaxBatch = 4096;           // prefix sums live in LDS
+constexpr int kLeanMinTiles = 8;              // smallest share worth a workgroup
+// The automatic choice takes the balanced schedule once there are at least
+// this many (sequence, query block, 16-token tile) units of capacity, i.e.
+// >= 256 tiles per share on a 512-share device.  Below it, work per share is
+// so short that the schedule's prologue and the segments' serial latency
+// cost more than the tail the partitions leave.
+constexpr int64_t kLeanAutoMinTiles = 131072;
+
 constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;               // CU-count cache entries
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -117,11 +133,15 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
     if (out->shape[0] != B || out->shape[1] != num_q_heads || out->shape[2] != head_dim)
         return fail(PA_EINVAL, "out shape does not match q");
     if (opts) {
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 4; ++i)
             if (opts->reserved[i]) return fail(PA_EINVAL, "pa_opts.reserved must be zero");
         if (opts->variant < PA_VARIANT_AUTO || opts->variant > PA_VARIANT_MFMA)
             return fail(PA_EINVAL, "unknown variant %d", opts->variant);
         if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
+        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_BALANCED)
+            return fail(PA_EINVAL, "unknown schedule %d", opts->schedule);
+        if (opts->shares < 0 || opts->shares > kLeanMaxShares)
+            return fail(PA_EINVAL, "shares %d outside 0..%d", opts->shares, kLeanMaxShares);
     }
     if (head_dim != 128 && head_dim != 256) return fail(PA_ENOTSUP, "head_dim %d (supported: 128, 256)", head_dim);
     const int qg = num_q_heads / num_kv_heads;
@@ -154,6 +174,32 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         pl.qw = g.qg < 8 ? g.qg : 8;
     const int64_t max_ctx = std::max<int64_t>(g.max_blk * g.P, 1);
     const int64_t groups = g.B * (g.Hq / pl.qw);
+
+    // Balanced schedule (MFMA): equal shares of all (sequence, query block,
+    // tile) work, whatever the mix of sequence lengths.
+    const int64_t ub_tiles = groups * ((max_ctx + 15) / 16);
+    const int sched = opts ? opts->schedule : PA_SCHEDULE_AUTO;
+    const bool lean_ok = pl.variant == PA_VARIANT_MFMA && g.B <= kLeanMaxBatch &&
+                         ub_tiles < ((int64_t)1 << 30);
+    if (sched == PA_SCHEDULE_BALANCED)
+        pl.lean = lean_ok;
+    else if (sched == PA_SCHEDULE_AUTO)
+        pl.lean = lean_ok && !(opts && opts->partition_tokens > 0) && ub_tiles >= kLeanAutoMinTiles;
+    else
+        pl.lean = false;
+    if (pl.lean) {
+        const int64_t n_wg = std::max<int64_t>(1, std::min<int64_t>(kLeanMaxShares, ub_tiles / kLeanMinTiles));
+        pl.n_part_fixed = opts && opts->shares > 0;
+        pl.n_part = pl.n_part_fixed ? opts->shares : (int)n_wg;   // shares (workgroups)
+        pl.part_tokens = 0;
+        pl.split = true;
+        const size_t slots = (size_t)(groups + kLeanMaxShares) * pl.qw;
+        pl.lse_offset = align_up(slots * g.D * sizeof(float), kAlign);
+        pl.meta_offset = pl.lse_offset + align_up(slots * sizeof(float), kAlign);
+        pl.ws_bytes = pl.meta_offset + align_up((size_t)(g.B + 2) * sizeof(int), kAlign);
+        return pl;
+    }
+
     int64_t T;
     if (opts && opts->partition_tokens > 0) {
         T = (int64_t)opts->partition_tokens;
@@ -214,9 +260,29 @@ int library_workspace(int dev, size_t need, void** out) {
     return PA_OK;
 }
 
+// Compute units of a device, cached (the attribute query costs a runtime call).
+int cu_count(int dev) {
+    static std::atomic<int> cache[kMaxDevices];
+    if (dev < 0 || dev >= kMaxDevices) return 1;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int check_plan(const Geometry& g, const Plan& pl, const pa_opts* opts) {
+    if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw))
+        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
+    if (opts && opts->schedule == PA_SCHEDULE_BALANCED && !pl.lean)
+        return fail(PA_ENOTSUP, "balanced schedule needs the MFMA variant and at most %d sequences",
+                    kLeanMaxBatch);
+    return PA_OK;
+}
+
 int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* bt,
            const pa_tensor* ctx, float scale, const pa_tensor* out, void* stream,
-           const Geometry& g, const Plan& pl, void* ws) {
+           const Geometry& g, const Plan& pl, void* ws, int dev) {
     pa::DecodeParams p{};
     p.q = static_cast<const uint16_t*>(q->data);
     p.q_sb = q->stride[0];
@@ -253,6 +319,28 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     hipError_t e;
+    if (pl.lean) {
+        p.lean_meta = reinterpret_cast<int*>(static_cast<char*>(ws) + pl.meta_offset);
+        p.lean_page_slots = pa::lean_page_slots(p.P);
+        // One share per CU.  Each CU streams at a bounded rate, so the call
+        // lasts as long as the most loaded CU: share counts that are not a
+        // multiple of the CU count leave some CUs with one share more
+        // (measured: 272 shares on 256 CUs run 1.33x longer than 256), and
+        // a second share per CU brings no more bandwidth.
+        const int n_wg = pl.n_part_fixed ? pl.n_part : std::min(pl.n_part, cu_count(dev));
+        e = pa::launch_mfma_lean(p, (int)g.D, n_wg, s);
+        if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma, balanced) launch: %s", hipGetErrorString(e));
+        g_stats.mfma++;
+        g_stats.lean++;
+        g_stats.merge++;
+        g_stats.split++;
+        g_stats.calls++;
+        g_stats.last_t = 0;
+        g_stats.last_np = (uint64_t)n_wg;
+        g_stats.last_variant = (uint64_t)pl.variant;
+        g_stats.last_schedule = PA_SCHEDULE_BALANCED;
+        return PA_OK;
+    }
     if (pl.variant == PA_VARIANT_MFMA) {
         e = pa::launch_mfma(p, (int)g.D, pl.qw, pl.split, s);
         if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma) launch: %s", hipGetErrorString(e));
@@ -272,6 +360,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     g_stats.last_t = (uint64_t)pl.part_tokens;
     g_stats.last_np = (uint64_t)pl.n_part;
     g_stats.last_variant = (uint64_t)pl.variant;
+    g_stats.last_schedule = PA_SCHEDULE_PARTITIONS;
     return PA_OK;
 }
 
@@ -285,8 +374,8 @@ int decode_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, cons
                       opts, g);
     if (rc) return rc;
     Plan pl = make_plan(g, opts);
-    if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw))
-        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
+    rc = check_plan(g, pl, opts);
+    if (rc) return rc;
     if (g.B == 0) return PA_OK;
     int dev = 0;
     int ndev = 0;
@@ -307,7 +396,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, cons
         }
     }
     try {
-        return launch(q, k, v, bt, ctx, scale, out, stream, g, pl, ws);
+        return launch(q, k, v, bt, ctx, scale, out, stream, g, pl, ws, dev);
     } catch (const std::bad_alloc&) {
         return fail(PA_ENOMEM, "host allocation failed");
     } catch (...) {
@@ -347,8 +436,8 @@ int pa_check_args(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor*
                       num_kv_heads, head_dim, page_size, out, opts, g);
     if (rc) return rc;
     Plan pl = make_plan(g, opts);
-    if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw))
-        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
+    rc = check_plan(g, pl, opts);
+    if (rc) return rc;
     return PA_OK;
 }
 
@@ -373,6 +462,8 @@ int pa_get_stats(pa_stats* s) {
     s->last_partition_tokens = g_stats.last_t;
     s->last_num_partitions = g_stats.last_np;
     s->last_variant = g_stats.last_variant;
+    s->balanced_calls = g_stats.lean;
+    s->last_schedule = g_stats.last_schedule;
     return PA_OK;
 }
 
@@ -382,6 +473,8 @@ void pa_reset_stats(void) {
     g_stats.mfma = 0;
     g_stats.split = 0;
     g_stats.merge = 0;
+    g_stats.lean = 0;
+    g_stats.last_schedule = 0;
     g_stats.last_t = 0;
     g_stats.last_np = 0;
     g_stats.last_variant = 0;

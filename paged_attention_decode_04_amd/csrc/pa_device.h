@@ -23,6 +23,8 @@ struct DecodeParams {
     int   part_tokens;                                      // tokens per partition
     int   n_part;                                           // grid partitions
     int   qw;                                               // query heads per workgroup
+    int*  lean_meta;                                        // balanced schedule: S[0..B], share
+    int   lean_page_slots;                                  // balanced schedule: page-id LDS entries
     float scale_log2;                                       // scale * log2(e)
 };
 

@@ -20,6 +20,15 @@ hipError_t launch_valu(const DecodeParams& p, int head_dim, int qw, bool split, 
 hipError_t launch_mfma(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s);
 bool mfma_supported(int head_dim, int qw);
 
+// Matrix-core decode over a balanced schedule (n_wg equal shares of the
+// sequence-major list of (sequence, query block, 16-token tile)), followed by
+// the merge of the shares' partials.
+hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int n_wg, hipStream_t s);
+constexpr int kLeanTokensPerFill = 4096;     // tokens whose page ids one LDS fill holds
+// Page-id LDS entries of the balanced schedule: a run of kLeanTokensPerFill
+// tokens spans at most ceil(kLeanTokensPerFill / P) + 1 pages.
+inline int lean_page_slots(int page_size) { return kLeanTokensPerFill / page_size + 2; }
+
 // Log-sum-exp merge of split partials into bf16 output.
 hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s);
 

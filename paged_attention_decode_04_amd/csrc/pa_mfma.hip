@@ -230,14 +230,14 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
 #pragma unroll
         for (int i = 0; i < NO; ++i) o[i] *= alpha;
     }
-    float pr[4], psum = 0.f;
+    float pr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        pr[r] = fast_exp2(sv[r] - m_run);
-        psum += pr[r];
-    }
-    l_run += psum;
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - m_run);
+    // P.V takes P in bf16; the normaliser sums the same rounded weights, so
+    // the output stays an exact weighted mean of V rows (weights off by at
+    // most 2^-9 relative) rather than picking up the rounding as a bias.
     const u32x2 pb = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+    l_run += (bf16lo(pb[0]) + bf16hi(pb[0])) + (bf16lo(pb[1]) + bf16hi(pb[1]));
 
     // O^T += V^T . P^T, V transposed in registers (4 tokens x 8 dims per lane)
 #pragma unroll
@@ -255,16 +255,151 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
         }
 }
 
+// Q^T as the B operand of query heads h0 .. h0 + qw - 1 of sequence b (same
+// k <-> dim map as the K rows of the layout).  Columns past qw are zero.
+template <int D, bool HALF>
+__device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int qw, int n, int q,
+                                       u32x4 (&qop)[D / 32]) {
+    const int qcol = HALF ? (n & 7) : n;
+    const bool live = qcol < qw;
+    const uint16_t* qr = p.q + (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? qcol : 0)) * p.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        if (HALF && kk >= D / 64) {
+            qop[kk] = u32x4{0u, 0u, 0u, 0u};            // unused in the split layout
+            continue;
+        }
+        u32x4 w = load16(qr + k_col<D, HALF>(kk, n, q));
+        qop[kk] = live ? w : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// This wave's share of the tokens [ts, te): tiles ts + 16 (wave + 4k).  The
+// page ids of the range sit in s_pages from logical page pg0 on.  NBUF
+// register buffers rotate so NBUF - 1 tiles' loads are in flight while one
+// is consumed; the steady-state loop issues its prefetches unconditionally
+// (each wait covers exactly the tile being consumed) and the last few tiles
+// drain in a short unrolled tail.  No data moves between buffers.
+template <int D, bool PAGE16, bool HALF, int NBUF>
+__device__ __forceinline__ void run_tiles(const DecodeParams& p, const int* s_pages, int pg0, int g,
+                                          int n, int q, int wave, const LaneOffsets& lo,
+                                          const u32x4 (&qop)[D / 32], bool col_live, int ts, int te,
+                                          f32x4 (&o)[D / 16], float& m_run, float& l_run) {
+    const int n_tiles = (max(te - ts, 0) + kTile - 1) / kTile;
+    const int n_my = n_tiles > wave ? (n_tiles - wave + kMWaves - 1) / kMWaves : 0;
+    auto tile_tb = [&](int k) { return ts + (wave + k * kMWaves) * kTile; };
+    TileFrag<D> fb[NBUF];
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+        if (i < n_my) load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(i), te, fb[i]);
+    int k = 0;
+    for (; k + 2 * NBUF - 2 < n_my; k += NBUF) {
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) {
+            load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
+                                       fb[(i + NBUF - 1) % NBUF]);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_step<D, HALF>(p, fb[i], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NBUF - 1; ++i) {
+        if (k + i < n_my) {
+            if (k + i + NBUF - 1 < n_my)
+                load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
+                                           fb[(i + NBUF - 1) % NBUF]);
+            tile_step<D, HALF>(p, fb[i % NBUF], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
+        }
+    }
+}
+
+// Page ids of logical pages [lp0, lp1] of sequence b into s_pages (whole
+// workgroup; the caller synchronises before use).
+__device__ __forceinline__ void fetch_pages(const DecodeParams& p, int b, int lp0, int lp1, int* s_pages,
+                                            int tid) {
+    lp1 = min(lp1, p.max_blk - 1);
+    const int32_t* btrow = p.bt + (int64_t)b * p.bt_sb;
+    for (int i = tid; i <= lp1 - lp0; i += kMBlock) s_pages[i] = clampi(btrow[lp0 + i], 0, p.num_pages - 1);
+}
+
+template <int D>
+struct MergeLds {
+    float o[kMWaves][16][D + 4];                // +4: spread the 16 query rows over banks
+    float m[kMWaves][16], l[kMWaves][16];
+};
+
+// Merge the 4 waves' online-softmax states through LDS and hand each
+// (query jq, 8 dims at d0) chunk, normalised, with its log-sum-exp, to emit().
+// O^T tile (hh, mm), element r of lane (n, q) holds query n, dim
+// 128 hh + 32 q + 8 r + mm.  Ends with the workgroup synchronised.
+template <int D, typename Emit>
+__device__ __forceinline__ void merge_waves(MergeLds<D>& lds, const f32x4 (&o)[D / 16], float m_run,
+                                            float l_run, int qw, int n, int q, int wave, int tid,
+                                            Emit emit) {
+    constexpr int VH = D / 128;
+    if (n < qw) {
+#pragma unroll
+        for (int hh = 0; hh < VH; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm)
+                    lds.o[wave][n][128 * hh + 32 * q + 8 * r + mm] = o[hh * 8 + mm][r];
+        if (q == 0) {
+            lds.m[wave][n] = m_run;
+            lds.l[wave][n] = l_run;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < qw * (D / 8); idx += kMBlock) {
+        const int jq = idx / (D / 8);
+        const int d0 = (idx % (D / 8)) * 8;
+        float M = lds.m[0][jq];
+#pragma unroll
+        for (int w = 1; w < kMWaves; ++w) M = fmaxf(M, lds.m[w][jq]);
+        float wt[kMWaves], lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kMWaves; ++w) {
+            wt[w] = fast_exp2(lds.m[w][jq] - M);
+            lsum += lds.l[w][jq] * wt[w];
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        float ov[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int w = 0; w < kMWaves; ++w) a = fmaf(lds.o[w][jq][d0 + i], wt[w], a);
+            ov[i] = a * inv;
+        }
+        emit(jq, d0, ov, lsum > 0.f ? M + __log2f(lsum) : -INFINITY);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8]) {
+    u32x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(dst) = pk;
+}
+
+__device__ __forceinline__ void store_f32x8(float* dst, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed partitions: one workgroup per (query block, sequence, partition of
+// part_tokens tokens).  Flat grid, query block fastest and partition slowest:
+// consecutive workgroups (dealt round-robin to the XCDs) cover different
+// heads and sequences of the same partition index, so every XCD gets an even
+// share of each sequence's work, and partitions past a sequence's end (which
+// exit at once) come last.
 template <int D, bool SPLIT, bool PAGE16, bool HALF, int NBUF>
 __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p) {
     constexpr int KK = TileFrag<D>::KK;
-    constexpr int VH = TileFrag<D>::VH;
     constexpr int NO = D / 16;                  // O^T accumulator tiles
-    // Flat grid, query block fastest and partition slowest: consecutive
-    // workgroups (dealt round-robin to the XCDs) cover different heads and
-    // sequences of the same partition index, so every XCD gets an even share
-    // of each sequence's work, and partitions past a sequence's end (which
-    // exit at once) come last.
     const int n_qb = p.Hq / p.qw;
     const int qb = blockIdx.x % n_qb;
     const int rest = blockIdx.x / n_qb;
@@ -283,139 +418,218 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     // so the two dependent reads of the prologue overlap.
     const int ts = part * p.part_tokens;
     extern __shared__ int s_pages[];
-    int pg0, unused;
+    int pg0, lp_hi, unused;
     page_slot(p, ts, pg0, unused);
-    {
-        int lp_hi;
-        page_slot(p, ts + p.part_tokens - 1, lp_hi, unused);
-        lp_hi = min(lp_hi, p.max_blk - 1);
-        const int32_t* btrow = p.bt + (int64_t)b * p.bt_sb;
-        for (int i = tid; i <= lp_hi - pg0; i += kMBlock)
-            s_pages[i] = clampi(btrow[pg0 + i], 0, p.num_pages - 1);
-    }
+    page_slot(p, ts + p.part_tokens - 1, lp_hi, unused);
+    fetch_pages(p, b, pg0, lp_hi, s_pages, tid);
     const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     if (ts >= L && part > 0) return;
     const int te = min(L, ts + p.part_tokens);
-    const int n_tok = max(te - ts, 0);
 
-    // Q^T as the B operand (same k <-> dim map as the K rows of the layout).
-    // Columns past the group are zero.
     u32x4 qop[KK];
-    const int qcol = HALF ? (n & 7) : n;
+    load_q<D, HALF>(p, b, h0, qw, n, q, qop);
     const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
-    {
-        const bool live = qcol < qw;
-        const uint16_t* qr = p.q + (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? qcol : 0)) * p.q_sh;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (HALF && kk >= D / 64) {
-                qop[kk] = u32x4{0u, 0u, 0u, 0u};          // unused in the split layout
-                continue;
-            }
-            u32x4 w = load16(qr + k_col<D, HALF>(kk, n, q));
-            qop[kk] = live ? w : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
     __syncthreads();
 
     f32x4 o[NO];
 #pragma unroll
     for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = kEmptyMax, l_run = 0.f;
-
-    const int n_tiles = (n_tok + kTile - 1) / kTile;
     LaneOffsets lo;
     lo.k = k_row<D, HALF>(0, n) * (int)p.k_ss + k_col<D, HALF>(0, n, q);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
-    // This wave's tiles are j_k = wave + 4k, k < n_my.  Rotate through NBUF
-    // register buffers so NBUF - 1 tiles' loads are in flight while one is
-    // consumed.  The steady-state loop issues its prefetches unconditionally
-    // (so each wait covers exactly the tile being consumed); the last few
-    // tiles drain in a short unrolled tail.  No data moves between buffers.
-    const int n_my = n_tiles > wave ? (n_tiles - wave + kMWaves - 1) / kMWaves : 0;
-    auto tile_tb = [&](int k) { return ts + (wave + k * kMWaves) * kTile; };
-    TileFrag<D> fb[NBUF];
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
-        if (i < n_my) load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(i), te, fb[i]);
-    int k = 0;
-    for (; k + 2 * NBUF - 2 < n_my; k += NBUF) {
-#pragma unroll
-        for (int i = 0; i < NBUF; ++i) {
-            load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
-                                 fb[(i + NBUF - 1) % NBUF]);
-            __builtin_amdgcn_sched_barrier(0);
-            tile_step<D, HALF>(p, fb[i], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * NBUF - 1; ++i) {
-        if (k + i < n_my) {
-            if (k + i + NBUF - 1 < n_my)
-                load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
-                                     fb[(i + NBUF - 1) % NBUF]);
-            tile_step<D, HALF>(p, fb[i % NBUF], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
-        }
-    }
+    run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, ts, te, o, m_run, l_run);
+    l_run = xsum32(xsum16(l_run));              // row sums over the four 16-lane rows
 
-    // Row sums over the four 16-lane rows (each saw different tokens).
-    l_run = xsum32(xsum16(l_run));
-
-    // Merge the waves through LDS.  O^T tile (hh, mm), element r of lane
-    // (n, q) holds query n, dim 128 hh + 32 q + 8 r + mm.
-    __shared__ float s_o[kMWaves][16][D + 4];   // +4: spread the 16 query rows over banks
-    __shared__ float s_m[kMWaves][16], s_l[kMWaves][16];
-    if (n < qw) {
-#pragma unroll
-        for (int hh = 0; hh < VH; ++hh)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int mm = 0; mm < 8; ++mm)
-                    s_o[wave][n][128 * hh + 32 * q + 8 * r + mm] = o[hh * 8 + mm][r];
-        if (q == 0) {
-            s_m[wave][n] = m_run;
-            s_l[wave][n] = l_run;
-        }
-    }
-    __syncthreads();
-
-    for (int idx = tid; idx < qw * (D / 8); idx += kMBlock) {
-        const int jq = idx / (D / 8);
-        const int d0 = (idx % (D / 8)) * 8;
-        float M = s_m[0][jq];
-#pragma unroll
-        for (int w = 1; w < kMWaves; ++w) M = fmaxf(M, s_m[w][jq]);
-        float wt[kMWaves], lsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kMWaves; ++w) {
-            wt[w] = fast_exp2(s_m[w][jq] - M);
-            lsum += s_l[w][jq] * wt[w];
-        }
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        float ov[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float a = 0.f;
-#pragma unroll
-            for (int w = 0; w < kMWaves; ++w) a = fmaf(s_o[w][jq][d0 + i], wt[w], a);
-            ov[i] = a * inv;
-        }
+    __shared__ MergeLds<D> lds;
+    merge_waves<D>(lds, o, m_run, l_run, qw, n, q, wave, tid,
+                   [&](int jq, int d0, const float (&ov)[8], float lse) {
         const int h = h0 + jq;
         if constexpr (!SPLIT) {
-            u32x4 pk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(ov[2 * i], ov[2 * i + 1]);
-            *reinterpret_cast<u32x4*>(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0) = pk;
+            store_bf16x8(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
         } else {
             const int64_t slot = ((int64_t)b * p.Hq + h) * p.n_part + part;
-            float* op = p.part_o + slot * D + d0;
-            *reinterpret_cast<float4*>(op) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-            *reinterpret_cast<float4*>(op + 4) = make_float4(ov[4], ov[5], ov[6], ov[7]);
-            if (d0 == 0) p.part_lse[slot] = lsum > 0.f ? M + __log2f(lsum) : -INFINITY;
+            store_f32x8(p.part_o + slot * D + d0, ov);
+            if (d0 == 0) p.part_lse[slot] = lse;
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Balanced schedule.  Order all work as the sequence of (sequence b, query
+// block qb, 16-token tile) triples, sequence-major, and give workgroup w the
+// w-th of gridDim.x equal contiguous shares of it.  A share may cover the end
+// of one (b, qb) group and the start of others; each covered piece is one
+// "segment".  Group G = b * n_qb + qb meets the shares in a monotone staircase,
+// so slot G + w names its piece uniquely; a piece that is a whole group is
+// written straight to the output, the others as partials for the merge kernel.
+// Workgroups need the tile prefix sums of all sequences (kept in LDS); the
+// first one also leaves them, with the share size, in lean_meta.  Page ids
+// are fetched kLeanTokensPerFill tokens at a time.
+
+template <int D, bool PAGE16, bool HALF, int NBUF>
+__global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodeParams p) {
+    constexpr int KK = TileFrag<D>::KK;
+    constexpr int NO = D / 16;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, q = lane >> 4;
+    const int w = blockIdx.x;
+    const int qw = p.qw;
+    const int n_qb = p.Hq / qw;
+
+    extern __shared__ int s_dyn[];
+    int* s_pages = s_dyn;                       // kLeanTokensPerFill / P + 2 entries
+    int* s_pref = s_dyn + p.lean_page_slots;    // B + 1 tile prefix sums
+
+    // Tile prefix sums S[b] = sum_{b' < b} ceil(L_b' / 16), in chunks of 256.
+    __shared__ int s_carry;
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int c = 0; c < p.B; c += kMBlock) {
+        const int bb = c + tid;
+        const int L = bb < p.B ? clampi(p.ctx[bb], 0, p.max_blk * p.P) : 0;
+        int v = (L + kTile - 1) / kTile;
+        // inclusive scan of v over the workgroup: per-wave DPP-free shuffle scan, then across waves
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(v, off);
+            if (lane >= off) v += t;
+        }
+        __shared__ int s_wsum[kMWaves];
+        if (lane == 63) s_wsum[wave] = v;
+        __syncthreads();
+        int before = s_carry;
+        for (int i = 0; i < wave; ++i) before += s_wsum[i];
+        if (bb < p.B) s_pref[bb + 1] = before + v;
+        if (c == 0 && tid == 0) s_pref[0] = 0;
+        __syncthreads();
+        if (tid == 0) s_carry = s_pref[min(c + kMBlock, p.B)];
+        __syncthreads();
+    }
+    // Everything that steers the segment loop is read through readfirstlane:
+    // it is wave-uniform (LDS values every lane reads alike), and saying so
+    // keeps the loop on scalar branches, so the cross-lane reductions inside
+    // always run with the full wave active.  Totals stay below 2^30 (the host
+    // bounds the tile count).
+    auto sp = [&](int i) { return __builtin_amdgcn_readfirstlane(s_pref[i]); };
+    const int total = n_qb * sp(p.B);
+    const int share = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    if (w == 0) {
+        for (int i = tid; i <= p.B; i += kMBlock) p.lean_meta[i] = s_pref[i];
+        if (tid == 0) p.lean_meta[p.B + 1] = share;
+    }
+    int x = w * share;
+    const int hi = min(total, x + share);
+
+    __shared__ MergeLds<D> lds;
+    while (x < hi) {
+        // sequence b: the last one with n_qb * S[b] <= x (empty sequences skipped)
+        int lo_b = 0, hi_b = p.B - 1;
+        while (lo_b < hi_b) {
+            const int mid = (lo_b + hi_b + 1) >> 1;
+            if (n_qb * sp(mid) <= x) lo_b = mid; else hi_b = mid - 1;
+        }
+        const int b = lo_b;
+        const int s_b = sp(b);
+        const int tiles_b = sp(b + 1) - s_b;
+        const int y = x - n_qb * s_b;
+        const int qb = y / tiles_b;
+        const int t_lo = y - qb * tiles_b;
+        const int seg_end = min(hi, n_qb * s_b + (qb + 1) * tiles_b);
+        const int t_hi = t_lo + (seg_end - x);
+        const bool whole = t_lo == 0 && t_hi == tiles_b;
+        const int G = b * n_qb + qb;
+        const int h0 = qb * qw;
+        const int g = h0 / (p.Hq / p.Hkv);
+        const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+        const int ts = t_lo * kTile, te = min(t_hi * kTile, L);
+
+        u32x4 qop[KK];
+        load_q<D, HALF>(p, b, h0, qw, n, q, qop);
+        const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
+        f32x4 o[NO];
+#pragma unroll
+        for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = kEmptyMax, l_run = 0.f;
+        LaneOffsets lo;
+        lo.k = k_row<D, HALF>(0, n) * (int)p.k_ss + k_col<D, HALF>(0, n, q);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
+        for (int c0 = ts; c0 < te; c0 += kLeanTokensPerFill) {
+            const int c1 = min(te, c0 + kLeanTokensPerFill);
+            int pg0, lp1, unused;
+            page_slot(p, c0, pg0, unused);
+            page_slot(p, c1 - 1, lp1, unused);
+            __syncthreads();                    // previous chunk's page ids are no longer read
+            fetch_pages(p, b, pg0, lp1, s_pages, tid);
+            __syncthreads();
+            run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, c0, c1, o,
+                                             m_run, l_run);
+        }
+        l_run = xsum32(xsum16(l_run));
+        merge_waves<D>(lds, o, m_run, l_run, qw, n, q, wave, tid,
+                       [&](int jq, int d0, const float (&ov)[8], float lse) {
+            const int h = h0 + jq;
+            if (whole) {
+                store_bf16x8(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
+            } else {
+                const int64_t slot = ((int64_t)(G + w)) * qw + jq;
+                store_f32x8(p.part_o + slot * D + d0, ov);
+                if (d0 == 0) p.part_lse[slot] = lse;
+            }
+        });
+        x = seg_end;
+    }
+    // Sequences with no tokens still owe zero rows: the first workgroup writes them.
+    if (w == 0) {
+        for (int bb = 0; bb < p.B; ++bb) {
+            if (s_pref[bb + 1] != s_pref[bb]) continue;
+            for (int idx = tid; idx < p.Hq * (D / 8); idx += kMBlock) {
+                const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                store_bf16x8(p.out + (int64_t)bb * p.o_sb + (int64_t)(idx / (D / 8)) * p.o_sh +
+                             (idx % (D / 8)) * 8, z);
+            }
         }
     }
+}
+
+// Merge of the balanced schedule's partials: one 64-thread group per
+// (head, sequence).  Groups covered by a single share were written directly.
+template <int D>
+__global__ __launch_bounds__(64) void pa_lean_merge_kernel(DecodeParams p) {
+    constexpr int EPT = D / 64;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int qw = p.qw;
+    const int n_qb = p.Hq / qw;
+    const int qb = h / qw, jq = h % qw;
+    const int* S = p.lean_meta;
+    const int64_t share = p.lean_meta[p.B + 1];
+    const int tiles_b = S[b + 1] - S[b];
+    if (tiles_b == 0 || share <= 0) return;
+    const int64_t start = (int64_t)n_qb * S[b] + (int64_t)qb * tiles_b;
+    const int64_t w0 = start / share, w1 = (start + tiles_b - 1) / share;
+    if (w0 == w1) return;
+    const int64_t G = (int64_t)b * n_qb + qb;
+    float M = -INFINITY;
+    for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, p.part_lse[(G + w) * qw + jq]);
+    float o[EPT], wsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) o[e] = 0.f;
+    for (int64_t w = w0; w <= w1; ++w) {
+        const int64_t slot = (G + w) * qw + jq;
+        const float wt = fast_exp2(p.part_lse[slot] - M);
+        wsum += wt;
+        const float* op = p.part_o + slot * D + threadIdx.x * EPT;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) o[e] = fmaf(wt, op[e], o[e]);
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + threadIdx.x * EPT;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 2)
+        *reinterpret_cast<uint32_t*>(orow + e) = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
 }
 
 bool mfma_supported(int head_dim, int qw) {
@@ -442,6 +656,31 @@ static hipError_t launch_mfma_d(const DecodeParams& p, int qw, bool split, hipSt
     const bool page16 = p.p_shift >= 4 && (int64_t)p.P * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) < (1ll << 30);
     if (split) return page16 ? launch_mfma_t<D, true, true>(p, qw, s) : launch_mfma_t<D, true, false>(p, qw, s);
     return page16 ? launch_mfma_t<D, false, true>(p, qw, s) : launch_mfma_t<D, false, false>(p, qw, s);
+}
+
+template <int D, bool PAGE16, bool HALF>
+static hipError_t launch_lean_t(const DecodeParams& p, int n_wg, hipStream_t s) {
+    constexpr int NBUF = D == 128 ? 3 : 2;
+    const size_t lds = sizeof(int) * (size_t)(p.lean_page_slots + p.B + 1);
+    hipLaunchKernelGGL((pa_decode_mfma_lean_kernel<D, PAGE16, HALF, NBUF>), dim3(n_wg), dim3(kMBlock), lds, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pa_lean_merge_kernel<D>, dim3(p.Hq, p.B), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_lean_d(const DecodeParams& p, int n_wg, hipStream_t s) {
+    const bool page16 = p.p_shift >= 4 && (int64_t)p.P * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) < (1ll << 30);
+    const bool half = p.qw <= 8;
+    if (page16) return half ? launch_lean_t<D, true, true>(p, n_wg, s) : launch_lean_t<D, true, false>(p, n_wg, s);
+    return half ? launch_lean_t<D, false, true>(p, n_wg, s) : launch_lean_t<D, false, false>(p, n_wg, s);
+}
+
+hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int n_wg, hipStream_t s) {
+    if (!mfma_supported(head_dim, p.qw) || p.Hq % p.qw) return hipErrorInvalidValue;
+    if (head_dim == 128) return launch_lean_d<128>(p, n_wg, s);
+    return launch_lean_d<256>(p, n_wg, s);
 }
 
 hipError_t launch_mfma(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s) {

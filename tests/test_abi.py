@@ -123,6 +123,19 @@ def test_opts_are_validated():
     assert check(args(), o) == pa.PA_EINVAL
     o = pa.make_opts("valu", -5)
     assert check(args(), o) == pa.PA_EINVAL
+    o = pa.make_opts("mfma", 0, 3)
+    assert check(args(), o) == pa.PA_EINVAL
+    for sched in ("auto", "partitions", "balanced"):
+        assert check(args(), pa.make_opts("mfma", 0, sched)) == pa.PA_OK
+
+
+def test_balanced_schedule_needs_mfma_and_bounded_batch():
+    assert check(args(), pa.make_opts("valu", 0, "balanced")) == pa.PA_ENOTSUP
+    assert "balanced" in pa.last_error()
+    assert check(args(B=4096), pa.make_opts("mfma", 0, "balanced")) == pa.PA_OK
+    assert check(args(B=4097), pa.make_opts("mfma", 0, "balanced")) == pa.PA_ENOTSUP
+    # automatic choice falls back to partitions past 4096 sequences
+    assert check(args(B=4097), pa.make_opts("mfma", 0, "auto")) == pa.PA_OK
 
 
 def test_null_descriptor_is_einval_not_a_crash():
@@ -168,6 +181,26 @@ def test_workspace_bytes():
     rnd = lambda x: (x + 255) // 256 * 256
     assert n == rnd(o_bytes) + rnd(lse_bytes)
     assert pa.pa_decode_workspace_bytes(-1, 16, 8, 128, 4, 32, None) == 0
+    # balanced schedule: one partial slot per (group, share) pair it can
+    # produce (groups + 1024 shares at most) of qw = qg query rows, plus the
+    # B + 2 ints of tile prefix sums and share size
+    B, Hq, Hkv, D = 3, 32, 4, 256
+    n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, 100, 16, pa.make_opts("mfma", 0, "balanced"))
+    slots = (B * (Hq // 8) + 1024) * 8
+    assert n == rnd(slots * D * 4) + rnd(slots * 4) + rnd((B + 2) * 4)
+    # the automatic choice: balanced for a large call (64 sequences of up to
+    # 32768 tokens, 8 query blocks), partitions for a small one
+    big = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, None)
+    slots = (64 * 8 + 1024) * 8
+    assert big == rnd(slots * 128 * 4) + rnd(slots * 4) + rnd(66 * 4)
+    assert big == pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16,
+                                               pa.make_opts("mfma", 0, "balanced"))
+    small = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, None)
+    assert small == pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16,
+                                                 pa.make_opts("mfma", 0, "partitions"))
+    # setting partition_tokens alone selects the partition schedule
+    n = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma", 64))
+    assert n == rnd(1 * 16 * 18 * 128 * 4) + rnd(1 * 16 * 18 * 4)
     assert pa.pa_decode_workspace_bytes(1, 15, 8, 128, 4, 32, None) == 0
 
 
@@ -176,4 +209,5 @@ def test_stats_roundtrip():
     s = pa.pa_get_stats()
     assert s["calls"] == 0 and s["valu_launches"] == 0
     assert set(s) == {"calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
-                      "last_partition_tokens", "last_num_partitions", "last_variant"}
+                      "last_partition_tokens", "last_num_partitions", "last_variant",
+                      "balanced_calls", "last_schedule"}

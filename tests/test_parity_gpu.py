@@ -18,22 +18,45 @@ from workloads import WORKLOADS, custom, make_inputs, to_device
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["valu", "mfma"]
+# Kernel variant and work schedule: vector-ALU kernel on fixed partitions,
+# MFMA kernel on fixed partitions, MFMA kernel on balanced shares.
+VARIANTS = ["valu", "mfma", "mfma-bal"]
+_MODE = {"valu": ("valu", "partitions"), "mfma": ("mfma", "partitions"),
+         "mfma-bal": ("mfma", "balanced")}
+# Share counts the balanced schedule is exercised with: automatic, a single
+# share (every group written directly), and counts whose boundaries fall
+# mid-group, mid-sequence and on 16-token tiles of different sequences.
+SHARES = (0, 1, 3, 37, 1024)
 
 
 def bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def gpu_run(d, call=0, variant="valu", partition_tokens=0):
+def knobs(variant, tokens):
+    """Split settings to sweep: partition sizes, or share counts when balanced."""
+    if _MODE[variant][1] == "balanced":
+        return [dict(shares=n) for n in SHARES]
+    return [dict(partition_tokens=T) for T in tokens]
+
+
+def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0):
+    kernel, schedule = _MODE[variant]
     q, k, v = d.call(call)
+    out = torch.full_like(q, float("nan"))      # every row must be written
     pa.pa_reset_stats()
-    out = pa.decode(q, k, v, d.block_tables, d.context_lens, d.w.scale,
-                    variant=variant, partition_tokens=partition_tokens)
+    pa.decode(q, k, v, d.block_tables, d.context_lens, d.w.scale, out=out, variant=kernel,
+              partition_tokens=partition_tokens, schedule=schedule, shares=shares)
     torch.cuda.synchronize()
     s = pa.pa_get_stats()
     assert s["calls"] == 1
-    assert s[f"{variant}_launches"] == 1, s
+    assert s[f"{kernel}_launches"] == 1, s
+    assert s["last_schedule"] == (pa.PA_SCHEDULE_BALANCED if schedule == "balanced"
+                                  else pa.PA_SCHEDULE_PARTITIONS), s
+    if schedule == "balanced":
+        assert s["balanced_calls"] == 1 and s["merge_launches"] == 1, s
+        if shares:
+            assert s["last_num_partitions"] == shares, s
     return bits(out), s
 
 
@@ -109,9 +132,9 @@ def test_head_geometries(D, Hq, Hkv, variant):
     inp = make_inputs(w, seed=D + Hq)
     d = to_device(inp)
     ref = oracle_run(inp)
-    for T in (0, 64, 4096):
-        y, _ = gpu_run(d, variant=variant, partition_tokens=T)
-        assert_parity(y, ref, f"D={D} Hq={Hq} Hkv={Hkv} T={T}")
+    for kn in knobs(variant, (0, 64, 4096)):
+        y, _ = gpu_run(d, variant=variant, **kn)
+        assert_parity(y, ref, f"D={D} Hq={Hq} Hkv={Hkv} {kn}")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -125,10 +148,10 @@ def test_page_boundary_sweep_poisoned(P, lens, variant):
     inp = make_inputs(w, seed=P, poison_unused=True)
     d = to_device(inp)
     ref = oracle_run(inp)
-    for T in (0, 64, 128):
-        y, _ = gpu_run(d, variant=variant, partition_tokens=T)
+    for kn in knobs(variant, (0, 64, 128)):
+        y, _ = gpu_run(d, variant=variant, **kn)
         assert np.all(np.isfinite(workloads_f32(y)))
-        assert_parity(y, ref, f"P={P} T={T}")
+        assert_parity(y, ref, f"P={P} {kn}")
 
 
 def workloads_f32(b):
@@ -180,11 +203,11 @@ def test_split_sizes_agree(variant):
     d = to_device(inp)
     ref = oracle_run(inp)
     seen = set()
-    for T in (64, 128, 320, 1024, 1 << 20):
-        y, s = gpu_run(d, variant=variant, partition_tokens=T)
+    for kn in knobs(variant, (64, 128, 320, 1024, 1 << 20)):
+        y, s = gpu_run(d, variant=variant, **kn)
         seen.add(s["split_calls"])
-        assert_parity(y, ref, f"T={T}")
-    assert seen == {0, 1}
+        assert_parity(y, ref, f"{kn}")
+    assert seen == ({1} if variant == "mfma-bal" else {0, 1})
 
 
 # ------------------------------------------------------------------ layouts
@@ -203,11 +226,12 @@ def test_strided_views(variant):
     qpad[..., :D] = q0
     obuf = torch.zeros((q0.shape[0] + 1, q0.shape[1], D), dtype=torch.bfloat16, device=q0.device)
     out = obuf[1:]
+    kernel, schedule = _MODE[variant]
     pa.pa_reset_stats()
     pa.decode(qpad[..., :D], kv[..., :D], kv[..., D:], d.block_tables, d.context_lens,
-              inp.w.scale, out=out, variant=variant)
+              inp.w.scale, out=out, variant=kernel, schedule=schedule)
     torch.cuda.synchronize()
-    assert pa.pa_get_stats()[f"{variant}_launches"] == 1
+    assert pa.pa_get_stats()[f"{kernel}_launches"] == 1
     assert_parity(bits(out), oracle_run(inp), "strided views")
     assert torch.all(obuf[0] == 0)
 
@@ -218,11 +242,18 @@ def test_empty_sequences_and_batch(variant):
                ctx=(0, 40, 0), pool_pages=4)
     inp = make_inputs(w, seed=8)
     d = to_device(inp)
-    for T in (0, 64):
-        y, _ = gpu_run(d, variant=variant, partition_tokens=T)
+    for kn in knobs(variant, (0, 64)):
+        y, _ = gpu_run(d, variant=variant, **kn)
         y = y.reshape(3, 8, 128)
         assert np.all(y[0] == 0) and np.all(y[2] == 0)
-        assert_parity(y, oracle_run(inp), f"empty T={T}")
+        assert_parity(y, oracle_run(inp), f"empty {kn}")
+    # every sequence empty: all rows zero, and no partial is ever read
+    w0 = custom(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                ctx=(0, 0), pool_pages=1)
+    d0 = to_device(make_inputs(w0, seed=8))
+    for kn in knobs(variant, (0,)):
+        y, _ = gpu_run(d0, variant=variant, **kn)
+        assert np.all(y == 0)
     q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
     out = pa.decode(q, d.k[0], d.v[0], d.block_tables[:0], d.context_lens[:0], 0.1)
     assert out.shape == (0, 8, 128)
@@ -284,3 +315,34 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         assert not torch.equal(junk, eager)
+
+
+# ------------------------------------------------------------------ balanced schedule
+def test_balanced_max_batch_ragged():
+    """4096 sequences (the balanced schedule's limit) of 0..70 tokens: the
+    tile prefix sums span 16 chunks of the in-LDS scan, and shares cut through
+    many short sequences and empty ones."""
+    rng = np.random.default_rng(11)
+    lens = tuple(int(x) for x in rng.integers(0, 71, 4096))
+    w = custom(batch=4096, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=16, ctx=lens)
+    inp = make_inputs(w, seed=11)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for n in (0, 1, 255, 1024):
+        y, _ = gpu_run(d, variant="mfma-bal", shares=n)
+        assert_parity(y, ref, f"B=4096 shares={n}")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 8), (256, 32, 4), (128, 64, 4)])
+def test_balanced_share_sweep(D, Hq, Hkv):
+    """Many share counts over a length mix with one long sequence: share
+    boundaries land in every position of the (sequence, query block, tile)
+    order, including the 4096-token page-id refills of a long piece."""
+    w = custom(batch=5, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=16,
+               ctx=(9000, 1, 300, 0, 4100))
+    inp = make_inputs(w, seed=D + Hq)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for n in (1, 2, 5, 16, 100, 333, 1000):
+        y, _ = gpu_run(d, variant="mfma-bal", shares=n)
+        assert_parity(y, ref, f"D={D} Hq={Hq} Hkv={Hkv} shares={n}")
