@@ -99,7 +99,7 @@ def make_call(pa, d, call, knobs):
     n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, opts)
     ws = None
     if n:
-        raw = torch.empty(n + 256, dtype=torch.uint8, device=q.device)
+        raw = torch.zeros(n + 256, dtype=torch.uint8, device=q.device)
         off = (-raw.data_ptr()) % 256
         ws = raw[off:off + n]
     scale = d.w.scale

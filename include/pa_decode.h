@@ -132,7 +132,9 @@ int pa_decode(const pa_tensor* q,
 #define PA_SCHEDULE_PARTITIONS  1  /* one workgroup per fixed-size partition of
                                       each sequence (split-KV partitions)      */
 #define PA_SCHEDULE_BALANCED    2  /* MFMA only: the work of all sequences cut
-                                      into equal shares, one per workgroup     */
+                                      into one equal static share per
+                                      workgroup plus small units taken from a
+                                      counter as workgroups finish           */
 
 typedef struct pa_opts {
     int32_t variant;            /* PA_VARIANT_*                                */
@@ -144,7 +146,7 @@ typedef struct pa_opts {
     int32_t schedule;           /* PA_SCHEDULE_*                               */
     int32_t shares;             /* balanced schedule: 0 = automatic (one per
                                    compute unit at most), else the number of
-                                   shares (workgroups), 1 .. 1024              */
+                                   workgroups, 1 .. 1024                       */
     int32_t reserved[4];        /* must be zero                                */
 } pa_opts;
 
@@ -162,8 +164,11 @@ size_t pa_decode_workspace_bytes(int64_t num_seqs, int num_q_heads, int num_kv_h
  * opts may be NULL (automatic).  workspace is a device buffer of at least
  * pa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the caller
  * and in use until the enqueued work finishes; if workspace is NULL the
- * library's own per-device workspace is used (as in pa_decode).  Returns
- * PA_ENOMEM if the given workspace is too small.
+ * library's own per-device workspace is used (as in pa_decode).  Its first
+ * 256 bytes hold the balanced schedule's work counters: they must be zero
+ * before the workspace's first use (e.g. allocate it zeroed), and every call
+ * leaves them zero, so a workspace can be reused by any later call of either
+ * schedule.  Returns PA_ENOMEM if the given workspace is too small.
  */
 int pa_decode_ex(const pa_tensor* q,
                  const pa_tensor* k_cache,

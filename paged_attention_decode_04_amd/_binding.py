@@ -219,8 +219,9 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
 
     q [B, Hq, D] bf16; k_cache/v_cache [NP, P, Hkv, D] bf16 (NHD pool);
     block_tables [B, MaxBlk] int32; context_lens [B] int32; scale defaults to
-    1/sqrt(D).  Returns out [B, Hq, D] bf16.  The split-KV workspace comes from
-    torch's caching allocator unless one is given.
+    1/sqrt(D).  Returns out [B, Hq, D] bf16.  The split-KV workspace comes
+    zero-filled from torch's caching allocator unless one is given (a given
+    one must start with 256 zero bytes; see pa_decode_ex).
     """
     import torch
     B, Hq, D = q.shape
@@ -233,7 +234,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
     if workspace is None:
         n = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], P, opts)
         if n:
-            workspace = torch.empty(n + 256, dtype=torch.uint8, device=q.device)
+            workspace = torch.zeros(n + 256, dtype=torch.uint8, device=q.device)
             off = (-workspace.data_ptr()) % 256
             workspace = workspace[off:off + n]
     return pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, Hq, Hkv, D, P,

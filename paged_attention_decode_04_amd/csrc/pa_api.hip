@@ -52,6 +52,7 @@ struct Plan {
     int n_part;
     bool split;
     size_t ws_bytes;
+    size_t o_offset;    // byte offset of the partial outputs inside the workspace
     size_t lse_offset;  // byte offset of the lse array inside the workspace
     bool lean;          // balanced schedule (MFMA): shares instead of partitions
     bool n_part_fixed;  // balanced schedule: share count given by the caller
@@ -63,6 +64,9 @@ struct Plan {
 constexpr int kLeanMaxShares = 1024;
 constexpr int kLeanMaxBatch = 4096;           // prefix sums live in LDS
 constexpr int kLeanMinTiles = 8;              // smallest share worth a workgroup
+// Units of the balanced schedule: one static unit per workgroup plus at most
+// kLeanDynPerWg dynamic units per workgroup.
+constexpr int64_t kLeanMaxUnits = (int64_t)kLeanMaxShares * (1 + pa::kLeanDynPerWg);
 // The automatic choice takes the balanced schedule once there are at least
 // this many (sequence, query block, 16-token tile) units of capacity, i.e.
 // >= 256 tiles per share on a 512-share device.  Below it, work per share is
@@ -193,10 +197,12 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         pl.n_part = pl.n_part_fixed ? opts->shares : (int)n_wg;   // shares (workgroups)
         pl.part_tokens = 0;
         pl.split = true;
-        const size_t slots = (size_t)(groups + kLeanMaxShares) * pl.qw;
-        pl.lse_offset = align_up(slots * g.D * sizeof(float), kAlign);
+        // One partial slot row per (group, unit) piece: groups + units at most.
+        const size_t slots = (size_t)(groups + kLeanMaxUnits) * pl.qw;
+        pl.o_offset = pa::kLeanCounterBytes;
+        pl.lse_offset = pl.o_offset + align_up(slots * g.D * sizeof(float), kAlign);
         pl.meta_offset = pl.lse_offset + align_up(slots * sizeof(float), kAlign);
-        pl.ws_bytes = pl.meta_offset + align_up((size_t)(g.B + 2) * sizeof(int), kAlign);
+        pl.ws_bytes = pl.meta_offset + align_up((size_t)(g.B + 4) * sizeof(int), kAlign);
         return pl;
     }
 
@@ -221,8 +227,11 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     pl.n_part = (int)((max_ctx + T - 1) / T);
     pl.split = pl.n_part > 1;
     if (pl.split) {
+        // The balanced schedule's counters keep their place at the start, so
+        // one workspace can serve both schedules.
         const size_t n = (size_t)g.B * g.Hq * pl.n_part;
-        pl.lse_offset = align_up(n * g.D * sizeof(float), kAlign);
+        pl.o_offset = pa::kLeanCounterBytes;
+        pl.lse_offset = pl.o_offset + align_up(n * g.D * sizeof(float), kAlign);
         pl.ws_bytes = pl.lse_offset + align_up(n * sizeof(float), kAlign);
     }
     return pl;
@@ -253,6 +262,14 @@ int library_workspace(int dev, size_t need, void** out) {
         if (e != hipSuccess) {
             w.ptr = nullptr;
             return fail(PA_ENOMEM, "hipMalloc(%zu): %s", sz, hipGetErrorString(e));
+        }
+        // The balanced schedule's counters must start at zero (every call
+        // leaves them so).
+        e = hipMemset(w.ptr, 0, pa::kLeanCounterBytes);
+        if (e != hipSuccess) {
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            return fail(PA_EHIP, "hipMemset: %s", hipGetErrorString(e));
         }
         w.bytes = sz;
     }
@@ -301,7 +318,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     p.out = static_cast<uint16_t*>(out->data);
     p.o_sb = out->stride[0];
     p.o_sh = out->stride[1];
-    p.part_o = pl.split ? static_cast<float*>(ws) : nullptr;
+    p.part_o = pl.split ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.o_offset) : nullptr;
     p.part_lse = pl.split ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.lse_offset) : nullptr;
     p.B = (int)g.B;
     p.Hq = (int)g.Hq;
@@ -321,6 +338,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     hipError_t e;
     if (pl.lean) {
         p.lean_meta = reinterpret_cast<int*>(static_cast<char*>(ws) + pl.meta_offset);
+        p.lean_ctr = static_cast<int*>(ws);
         p.lean_page_slots = pa::lean_page_slots(p.P);
         // One share per CU.  Each CU streams at a bounded rate, so the call
         // lasts as long as the most loaded CU: share counts that are not a

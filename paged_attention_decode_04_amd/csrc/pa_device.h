@@ -23,7 +23,8 @@ struct DecodeParams {
     int   part_tokens;                                      // tokens per partition
     int   n_part;                                           // grid partitions
     int   qw;                                               // query heads per workgroup
-    int*  lean_meta;                                        // balanced schedule: S[0..B], share
+    int*  lean_meta;                                        // balanced schedule: S[0..B], s0, s1, n_wg
+    int*  lean_ctr;                                         // balanced schedule: next unit, finished WGs
     int   lean_page_slots;                                  // balanced schedule: page-id LDS entries
     float scale_log2;                                       // scale * log2(e)
 };
@@ -91,6 +92,50 @@ __device__ __forceinline__ void page_slot(const DecodeParams& p, int t, int& lp,
         lp = t / p.P;
         slot = t - lp * p.P;
     }
+}
+
+// Log-sum-exp merge of n split partials (o_p fp32 rows of D, lse_p base 2)
+// at slots first, first + step, ... into one bf16 output row, by 64 threads
+// holding D / 64 elements each.  Partials are read four at a time with
+// their lse and o rows together, so a merge of up to four costs one round
+// trip to memory; the running maximum rescales between batches.  n == 0
+// writes zeros.
+template <int D>
+__device__ __forceinline__ void merge_partials(const DecodeParams& p, int64_t first, int64_t step, int n,
+                                               uint16_t* orow) {
+    constexpr int EPT = D / 64;
+    typedef float vec_t __attribute__((ext_vector_type(EPT)));
+    const int t = threadIdx.x;
+    float M = -INFINITY, wsum = 0.f;
+    vec_t o = {};
+    for (int i0 = 0; i0 < n; i0 += 4) {
+        float l[4];
+        vec_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = min(i0 + j, n - 1);           // in range; extra entries are ignored
+            const int64_t slot = first + (int64_t)i * step;
+            l[j] = i0 + j < n ? p.part_lse[slot] : -INFINITY;
+            v[j] = *reinterpret_cast<const vec_t*>(p.part_o + slot * D + t * EPT);
+        }
+        const float mb = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
+        if (mb == -INFINITY) continue;
+        const float mn = fmaxf(M, mb);
+        const float a = fast_exp2(M - mn);
+        wsum *= a;
+        o *= a;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w = fast_exp2(l[j] - mn);
+            wsum += w;
+            o += w * v[j];
+        }
+        M = mn;
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 2)
+        *reinterpret_cast<uint32_t*>(orow + t * EPT + e) = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
 }
 
 }  // namespace pa

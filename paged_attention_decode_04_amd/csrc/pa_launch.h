@@ -20,14 +20,25 @@ hipError_t launch_valu(const DecodeParams& p, int head_dim, int qw, bool split, 
 hipError_t launch_mfma(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s);
 bool mfma_supported(int head_dim, int qw);
 
-// Matrix-core decode over a balanced schedule (n_wg equal shares of the
-// sequence-major list of (sequence, query block, 16-token tile)), followed by
-// the merge of the shares' partials.
+// Matrix-core decode over a balanced schedule (the sequence-major list of
+// (sequence, query block, 16-token tile) cut into one static unit per
+// workgroup and dynamic units taken from a counter), followed by the merge
+// of the units' partials.
 hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int n_wg, hipStream_t s);
 constexpr int kLeanTokensPerFill = 4096;     // tokens whose page ids one LDS fill holds
 // Page-id LDS entries of the balanced schedule: a run of kLeanTokensPerFill
 // tokens spans at most ceil(kLeanTokensPerFill / P) + 1 pages.
 inline int lean_page_slots(int page_size) { return kLeanTokensPerFill / page_size + 2; }
+// Units of the balanced schedule: static units cover kLeanStaticNum /
+// kLeanStaticDen of the work, the rest is cut into at most kLeanDynPerWg
+// dynamic units per workgroup of at least kLeanMinUnit tiles.
+constexpr int kLeanStaticNum = 4, kLeanStaticDen = 5;
+constexpr int kLeanDynPerWg = 6;
+constexpr int kLeanMinUnit = 16;
+// Below this many tiles per workgroup the static units cover all the work.
+constexpr int kLeanDynMinPerWg = 256;
+// Workspace: two int counters at its start, zero between calls.
+constexpr int kLeanCounterBytes = 256;
 
 // Log-sum-exp merge of split partials into bf16 output.
 hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s);

@@ -458,15 +458,64 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
 
 // ---------------------------------------------------------------------------
 // Balanced schedule.  Order all work as the sequence of (sequence b, query
-// block qb, 16-token tile) triples, sequence-major, and give workgroup w the
-// w-th of gridDim.x equal contiguous shares of it.  A share may cover the end
-// of one (b, qb) group and the start of others; each covered piece is one
-// "segment".  Group G = b * n_qb + qb meets the shares in a monotone staircase,
-// so slot G + w names its piece uniquely; a piece that is a whole group is
-// written straight to the output, the others as partials for the merge kernel.
-// Workgroups need the tile prefix sums of all sequences (kept in LDS); the
-// first one also leaves them, with the share size, in lean_meta.  Page ids
-// are fetched kLeanTokensPerFill tokens at a time.
+// block qb, 16-token tile) triples, sequence-major, and cut it into units
+// (LeanUnits): one static unit per workgroup covering the first
+// kLeanStaticNum / kLeanStaticDen of the work, then smaller dynamic units
+// that workgroups take from a counter as they finish, so CUs that stream
+// faster take more.  A unit may cover the end of one (b, qb) group and the
+// start of others; each covered piece is one "segment".  Group G = b * n_qb
+// + qb meets the units in a monotone staircase, so slot G + u names its piece
+// in unit u uniquely; a piece that is a whole group is written straight to
+// the output, the others as partials for the merge kernel.  Workgroups need
+// the tile prefix sums of all sequences (kept in LDS); the first one also
+// leaves them, with the unit sizes, in lean_meta.  Page ids are fetched
+// kLeanTokensPerFill tokens at a time.
+//
+// The two counters (next dynamic unit, finished workgroups) start at zero;
+// the last workgroup to finish sets both back to zero for the next call.
+
+// Unit boundaries: n_wg static units of s0 tiles from 0, then dynamic units
+// of s1 tiles from x_dyn = n_wg * s0 to the end (at most n_wg *
+// kLeanDynPerWg of them; none when x_dyn >= total).
+struct LeanUnits {
+    int n_wg, s0, s1, x_dyn, n_units;
+    __device__ __forceinline__ static LeanUnits plan(int total, int n_wg) {
+        LeanUnits l;
+        l.n_wg = n_wg;
+        l.s1 = kLeanMinUnit;
+        if (total < (int64_t)n_wg * kLeanDynMinPerWg) {
+            // Little work per workgroup: a unit's own cost (Q and page-id
+            // reads, wave merge) would outweigh the balance it buys, so the
+            // static units cover everything.
+            l.s0 = (total + n_wg - 1) / n_wg;
+            l.x_dyn = l.s0 * n_wg;
+            l.n_units = n_wg;
+            return l;
+        }
+        l.s0 = (int)((int64_t)total * kLeanStaticNum / ((int64_t)kLeanStaticDen * n_wg));
+        l.x_dyn = l.s0 * n_wg;
+        const int rem = total - l.x_dyn;
+        const int per = n_wg * kLeanDynPerWg;
+        l.s1 = max(kLeanMinUnit, (rem + per - 1) / per);
+        l.n_units = n_wg + (rem + l.s1 - 1) / l.s1;
+        return l;
+    }
+    __device__ __forceinline__ static LeanUnits from(int s0, int s1, int n_wg) {
+        LeanUnits l;
+        l.n_wg = n_wg;
+        l.s0 = s0;
+        l.s1 = s1;
+        l.x_dyn = s0 * n_wg;
+        l.n_units = 0;                          // not needed to locate units
+        return l;
+    }
+    __device__ __forceinline__ int begin(int u) const {
+        return u <= n_wg ? u * s0 : x_dyn + (u - n_wg) * s1;
+    }
+    __device__ __forceinline__ int unit_of(int x) const {
+        return x < x_dyn ? x / s0 : n_wg + (x - x_dyn) / s1;
+    }
+};
 
 template <int D, bool PAGE16, bool HALF, int NBUF>
 __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodeParams p) {
@@ -515,72 +564,101 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
     // bounds the tile count).
     auto sp = [&](int i) { return __builtin_amdgcn_readfirstlane(s_pref[i]); };
     const int total = n_qb * sp(p.B);
-    const int share = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    const LeanUnits lu = LeanUnits::plan(total, (int)gridDim.x);
     if (w == 0) {
         for (int i = tid; i <= p.B; i += kMBlock) p.lean_meta[i] = s_pref[i];
-        if (tid == 0) p.lean_meta[p.B + 1] = share;
+        if (tid == 0) {
+            p.lean_meta[p.B + 1] = lu.s0;
+            p.lean_meta[p.B + 2] = lu.s1;
+            p.lean_meta[p.B + 3] = lu.n_wg;
+        }
     }
-    int x = w * share;
-    const int hi = min(total, x + share);
 
     __shared__ MergeLds<D> lds;
-    while (x < hi) {
-        // sequence b: the last one with n_qb * S[b] <= x (empty sequences skipped)
-        int lo_b = 0, hi_b = p.B - 1;
-        while (lo_b < hi_b) {
-            const int mid = (lo_b + hi_b + 1) >> 1;
-            if (n_qb * sp(mid) <= x) lo_b = mid; else hi_b = mid - 1;
-        }
-        const int b = lo_b;
-        const int s_b = sp(b);
-        const int tiles_b = sp(b + 1) - s_b;
-        const int y = x - n_qb * s_b;
-        const int qb = y / tiles_b;
-        const int t_lo = y - qb * tiles_b;
-        const int seg_end = min(hi, n_qb * s_b + (qb + 1) * tiles_b);
-        const int t_hi = t_lo + (seg_end - x);
-        const bool whole = t_lo == 0 && t_hi == tiles_b;
-        const int G = b * n_qb + qb;
-        const int h0 = qb * qw;
-        const int g = h0 / (p.Hq / p.Hkv);
-        const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
-        const int ts = t_lo * kTile, te = min(t_hi * kTile, L);
-
-        u32x4 qop[KK];
-        load_q<D, HALF>(p, b, h0, qw, n, q, qop);
-        const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
-        f32x4 o[NO];
-#pragma unroll
-        for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run = kEmptyMax, l_run = 0.f;
-        LaneOffsets lo;
-        lo.k = k_row<D, HALF>(0, n) * (int)p.k_ss + k_col<D, HALF>(0, n, q);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
-        for (int c0 = ts; c0 < te; c0 += kLeanTokensPerFill) {
-            const int c1 = min(te, c0 + kLeanTokensPerFill);
-            int pg0, lp1, unused;
-            page_slot(p, c0, pg0, unused);
-            page_slot(p, c1 - 1, lp1, unused);
-            __syncthreads();                    // previous chunk's page ids are no longer read
-            fetch_pages(p, b, pg0, lp1, s_pages, tid);
-            __syncthreads();
-            run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, c0, c1, o,
-                                             m_run, l_run);
-        }
-        l_run = xsum32(xsum16(l_run));
-        merge_waves<D>(lds, o, m_run, l_run, qw, n, q, wave, tid,
-                       [&](int jq, int d0, const float (&ov)[8], float lse) {
-            const int h = h0 + jq;
-            if (whole) {
-                store_bf16x8(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
-            } else {
-                const int64_t slot = ((int64_t)(G + w)) * qw + jq;
-                store_f32x8(p.part_o + slot * D + d0, ov);
-                if (d0 == 0) p.part_lse[slot] = lse;
+    __shared__ int s_next[2];                    // next unit (double-buffered by iteration)
+    int u = w;                                   // the static unit first
+    for (int it = 0; u < lu.n_units; ++it) {
+        // Thread 0 takes the next dynamic unit now and publishes it after
+        // this unit's work, so the atomic's latency hides behind the work.
+        int taken = 0;
+        if (tid == 0) taken = atomicAdd(&p.lean_ctr[0], 1);
+        int x = lu.begin(u);
+        const int hi = min(total, lu.begin(u + 1));
+        while (x < hi) {
+            // sequence b: the last one with n_qb * S[b] <= x (empty sequences skipped)
+            int lo_b = 0, hi_b = p.B - 1;
+            while (lo_b < hi_b) {
+                const int mid = (lo_b + hi_b + 1) >> 1;
+                if (n_qb * sp(mid) <= x) lo_b = mid; else hi_b = mid - 1;
             }
-        });
-        x = seg_end;
+            const int b = lo_b;
+            const int s_b = sp(b);
+            const int tiles_b = sp(b + 1) - s_b;
+            const int y = x - n_qb * s_b;
+            const int qb = y / tiles_b;
+            const int t_lo = y - qb * tiles_b;
+            const int seg_end = min(hi, n_qb * s_b + (qb + 1) * tiles_b);
+            const int t_hi = t_lo + (seg_end - x);
+            const bool whole = t_lo == 0 && t_hi == tiles_b;
+            const int G = b * n_qb + qb;
+            const int h0 = qb * qw;
+            const int g = h0 / (p.Hq / p.Hkv);
+            const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+            const int ts = t_lo * kTile, te = min(t_hi * kTile, L);
+
+            u32x4 qop[KK];
+            load_q<D, HALF>(p, b, h0, qw, n, q, qop);
+            const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
+            f32x4 o[NO];
+#pragma unroll
+            for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float m_run = kEmptyMax, l_run = 0.f;
+            LaneOffsets lo;
+            lo.k = k_row<D, HALF>(0, n) * (int)p.k_ss + k_col<D, HALF>(0, n, q);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
+            for (int c0 = ts; c0 < te; c0 += kLeanTokensPerFill) {
+                const int c1 = min(te, c0 + kLeanTokensPerFill);
+                int pg0, lp1, unused;
+                page_slot(p, c0, pg0, unused);
+                page_slot(p, c1 - 1, lp1, unused);
+                // The previous chunk's page ids must no longer be in use.  For a
+                // segment's first chunk the merge (or the prologue) that ended the
+                // previous one already synchronised, and skipping the barrier lets
+                // the page-id reads overlap the Q reads above.
+                if (c0 != ts) __syncthreads();
+                fetch_pages(p, b, pg0, lp1, s_pages, tid);
+                __syncthreads();
+                run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, c0, c1, o,
+                                                 m_run, l_run);
+            }
+            l_run = xsum32(xsum16(l_run));
+            merge_waves<D>(lds, o, m_run, l_run, qw, n, q, wave, tid,
+                           [&](int jq, int d0, const float (&ov)[8], float lse) {
+                const int h = h0 + jq;
+                if (whole) {
+                    store_bf16x8(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
+                } else {
+                    const int64_t slot = ((int64_t)(G + u)) * qw + jq;
+                    store_f32x8(p.part_o + slot * D + d0, ov);
+                    if (d0 == 0) p.part_lse[slot] = lse;
+                }
+            });
+            x = seg_end;
+        }
+        // One barrier per unit: the slot written here is rewritten two units
+        // later, after every thread has passed the next unit's barrier.
+        // A counter outside [0, units left) ends the loop: only a workspace
+        // whose counters did not start at zero can produce one.
+        if (tid == 0) s_next[it & 1] = (taken >= 0 && taken < lu.n_units - lu.n_wg) ? lu.n_wg + taken : lu.n_units;
+        __syncthreads();
+        u = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
+    }
+    // The last workgroup out resets the counters for the next call.  Every
+    // workgroup has taken its last (failed) unit before it counts itself out.
+    if (tid == 0 && atomicAdd(&p.lean_ctr[1], 1) == (int)gridDim.x - 1) {
+        atomicExch(&p.lean_ctr[0], 0);
+        atomicExch(&p.lean_ctr[1], 0);
     }
     // Sequences with no tokens still owe zero rows: the first workgroup writes them.
     if (w == 0) {
@@ -596,40 +674,23 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
 }
 
 // Merge of the balanced schedule's partials: one 64-thread group per
-// (head, sequence).  Groups covered by a single share were written directly.
+// (head, sequence).  Groups inside a single unit were written directly.
 template <int D>
 __global__ __launch_bounds__(64) void pa_lean_merge_kernel(DecodeParams p) {
-    constexpr int EPT = D / 64;
     const int h = blockIdx.x, b = blockIdx.y;
     const int qw = p.qw;
     const int n_qb = p.Hq / qw;
     const int qb = h / qw, jq = h % qw;
     const int* S = p.lean_meta;
-    const int64_t share = p.lean_meta[p.B + 1];
     const int tiles_b = S[b + 1] - S[b];
-    if (tiles_b == 0 || share <= 0) return;
-    const int64_t start = (int64_t)n_qb * S[b] + (int64_t)qb * tiles_b;
-    const int64_t w0 = start / share, w1 = (start + tiles_b - 1) / share;
-    if (w0 == w1) return;
+    if (tiles_b == 0) return;
+    const LeanUnits lu = LeanUnits::from(S[p.B + 1], S[p.B + 2], S[p.B + 3]);
+    const int start = n_qb * S[b] + qb * tiles_b;
+    const int u0 = lu.unit_of(start), u1 = lu.unit_of(start + tiles_b - 1);
+    if (u0 == u1) return;
     const int64_t G = (int64_t)b * n_qb + qb;
-    float M = -INFINITY;
-    for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, p.part_lse[(G + w) * qw + jq]);
-    float o[EPT], wsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) o[e] = 0.f;
-    for (int64_t w = w0; w <= w1; ++w) {
-        const int64_t slot = (G + w) * qw + jq;
-        const float wt = fast_exp2(p.part_lse[slot] - M);
-        wsum += wt;
-        const float* op = p.part_o + slot * D + threadIdx.x * EPT;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) o[e] = fmaf(wt, op[e], o[e]);
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + threadIdx.x * EPT;
-#pragma unroll
-    for (int e = 0; e < EPT; e += 2)
-        *reinterpret_cast<uint32_t*>(orow + e) = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
+    merge_partials<D>(p, (G + u0) * qw + jq, qw, u1 - u0 + 1,
+                      p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
 }
 
 bool mfma_supported(int head_dim, int qw) {

@@ -246,29 +246,11 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
 // Log-sum-exp merge of the split-KV partials: one 64-thread group per (h, b).
 template <int D>
 __global__ __launch_bounds__(64) void pa_lse_merge_kernel(DecodeParams p) {
-    constexpr int EPT = D / 64;
     const int h = blockIdx.x, b = blockIdx.y;
     const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     const int n_used = (L + p.part_tokens - 1) / p.part_tokens;
-    const int64_t base = ((int64_t)b * p.Hq + h) * p.n_part;
-    const float* lse = p.part_lse + base;
-    float M = -INFINITY;
-    for (int i = 0; i < n_used; ++i) M = fmaxf(M, lse[i]);
-    float o[EPT], wsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) o[e] = 0.f;
-    for (int i = 0; i < n_used; ++i) {
-        const float w = fast_exp2(lse[i] - M);
-        wsum += w;
-        const float* op = p.part_o + (base + i) * D + threadIdx.x * EPT;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) o[e] = fmaf(w, op[e], o[e]);
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + threadIdx.x * EPT;
-#pragma unroll
-    for (int e = 0; e < EPT; e += 2)
-        *reinterpret_cast<uint32_t*>(orow + e) = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
+    merge_partials<D>(p, ((int64_t)b * p.Hq + h) * p.n_part, 1, n_used,
+                      p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
 }
 
 // ------------------------------------------------------------------ launch

@@ -179,20 +179,21 @@ def test_workspace_bytes():
     o_bytes = 1 * 16 * parts * 128 * 4
     lse_bytes = 1 * 16 * parts * 4
     rnd = lambda x: (x + 255) // 256 * 256
-    assert n == rnd(o_bytes) + rnd(lse_bytes)
+    HDR = 256                    # the balanced schedule's counters, kept in both layouts
+    assert n == HDR + rnd(o_bytes) + rnd(lse_bytes)
     assert pa.pa_decode_workspace_bytes(-1, 16, 8, 128, 4, 32, None) == 0
-    # balanced schedule: one partial slot per (group, share) pair it can
-    # produce (groups + 1024 shares at most) of qw = qg query rows, plus the
-    # B + 2 ints of tile prefix sums and share size
+    # balanced schedule: one partial slot per (group, unit) piece it can
+    # produce (groups + 1024 * 7 units at most) of qw = qg query rows, plus the
+    # B + 4 ints of tile prefix sums and unit sizes
     B, Hq, Hkv, D = 3, 32, 4, 256
     n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, 100, 16, pa.make_opts("mfma", 0, "balanced"))
-    slots = (B * (Hq // 8) + 1024) * 8
-    assert n == rnd(slots * D * 4) + rnd(slots * 4) + rnd((B + 2) * 4)
+    slots = (B * (Hq // 8) + 1024 * 7) * 8
+    assert n == HDR + rnd(slots * D * 4) + rnd(slots * 4) + rnd((B + 4) * 4)
     # the automatic choice: balanced for a large call (64 sequences of up to
     # 32768 tokens, 8 query blocks), partitions for a small one
     big = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, None)
-    slots = (64 * 8 + 1024) * 8
-    assert big == rnd(slots * 128 * 4) + rnd(slots * 4) + rnd(66 * 4)
+    slots = (64 * 8 + 1024 * 7) * 8
+    assert big == HDR + rnd(slots * 128 * 4) + rnd(slots * 4) + rnd(68 * 4)
     assert big == pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16,
                                                pa.make_opts("mfma", 0, "balanced"))
     small = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, None)
@@ -200,7 +201,7 @@ def test_workspace_bytes():
                                                  pa.make_opts("mfma", 0, "partitions"))
     # setting partition_tokens alone selects the partition schedule
     n = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma", 64))
-    assert n == rnd(1 * 16 * 18 * 128 * 4) + rnd(1 * 16 * 18 * 4)
+    assert n == HDR + rnd(1 * 16 * 18 * 128 * 4) + rnd(1 * 16 * 18 * 4)
     assert pa.pa_decode_workspace_bytes(1, 15, 8, 128, 4, 32, None) == 0
 
 

@@ -284,37 +284,41 @@ def test_device_errors_do_not_stick():
     assert_parity(y, oracle_run(inp), "after error")
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("schedule", ["partitions", "balanced"])
+def test_graph_capture_replays_match_eager(schedule):
     """Calls captured in a HIP graph: every replay, with eager work and
-    synchronisations in between, equals the eager result bit for bit."""
+    synchronisations in between, equals the eager result bit for bit (the
+    balanced schedule's work counters return to zero after every replay)."""
     inp = make_inputs("single_seq", seed=2)
     d = to_device(inp)
     q, k, v = d.call(3)
-    eager = pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale)
+    kw = dict(variant="mfma", schedule=schedule)
+    eager = pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, **kw)
     torch.cuda.synchronize()
     out = torch.empty_like(q)
-    ws = torch.empty(pa.pa_decode_workspace_bytes(1, 16, 8, 128, d.block_tables.shape[1], 16,
-                                                  pa.make_opts()) + 256,
+    ws = torch.zeros(pa.pa_decode_workspace_bytes(1, 16, 8, 128, d.block_tables.shape[1], 16,
+                                                  pa.make_opts(**kw)) + 256,
                      dtype=torch.uint8, device="cuda")
     off = (-ws.data_ptr()) % 256
     ws = ws[off:]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, workspace=ws)
+        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, workspace=ws, **kw)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, workspace=ws)
+        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, workspace=ws, **kw)
     for i in range(4):
         out.zero_()
-        junk = pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale * 0.5)
+        junk = pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale * 0.5, **kw)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         assert not torch.equal(junk, eager)
+        assert torch.all(ws[:256] == 0), f"counters after replay {i}"
 
 
 # ------------------------------------------------------------------ balanced schedule
@@ -346,3 +350,35 @@ def test_balanced_share_sweep(D, Hq, Hkv):
     for n in (1, 2, 5, 16, 100, 333, 1000):
         y, _ = gpu_run(d, variant="mfma-bal", shares=n)
         assert_parity(y, ref, f"D={D} Hq={Hq} Hkv={Hkv} shares={n}")
+
+
+def test_balanced_workspace_reuse_and_counters():
+    """One caller workspace serves many calls of both schedules: the work
+    counters are zero after every call and balanced reruns are bitwise
+    identical (units have fixed bounds, whichever workgroup takes them)."""
+    inp = make_inputs("hd256_gqa4", seed=3)
+    d = to_device(inp)
+    q, k, v = d.call(0)
+    B, Hq, D = q.shape
+    NP, P, Hkv, _ = k.shape
+    n = max(pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P,
+                                         pa.make_opts("mfma", 0, sch)) for sch in ("partitions", "balanced"))
+    raw = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + n]
+    ref = oracle_run(inp)
+    first = None
+    for i, (sch, shares) in enumerate([("balanced", 0), ("partitions", 0), ("balanced", 256),
+                                       ("balanced", 7), ("balanced", 256), ("partitions", 0),
+                                       ("balanced", 1024), ("balanced", 256)]):
+        out = torch.full_like(q, float("nan"))
+        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, variant="mfma",
+                  schedule=sch, shares=shares, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.all(ws[:256] == 0), f"call {i}: counters not reset"
+        y = bits(out)
+        assert_parity(y, ref, f"reuse call {i} {sch} {shares}")
+        if sch == "balanced" and shares == 256:
+            if first is None:
+                first = y
+            assert np.array_equal(y, first), f"call {i}: rerun differs"
