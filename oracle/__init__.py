@@ -67,6 +67,10 @@ def _load():
     lib.pa_oracle_f64_pairs.restype = i32
     lib.pa_oracle_f64_mutant.argtypes = common + [p, i32, i32]
     lib.pa_oracle_f64_mutant.restype = i32
+    lib.pa_oracle_f64_window.argtypes = common + [i64, p, i32, i32]
+    lib.pa_oracle_f64_window.restype = i32
+    lib.pa_oracle_f64_pairs_window.argtypes = common + [i64, p, i64, p, i32]
+    lib.pa_oracle_f64_pairs_window.restype = i32
     lib.pa_oracle_num_mutants.argtypes = []
     lib.pa_oracle_num_mutants.restype = i32
     _lib = lib
@@ -108,28 +112,31 @@ def _ptr(a):
 
 
 def attention(q, k_cache, v_cache, block_tables, context_lens, scale,
-              num_kv_heads, threads: int | None = None, mutant: int = 0):
+              num_kv_heads, threads: int | None = None, mutant: int = 0, window: int = 0):
     """fp64 output [B, Hq, D] of the plain definition.  ``scale`` is taken as
-    the fp32 value a caller would pass to the GPU and widened exactly."""
+    the fp32 value a caller would pass to the GPU and widened exactly.
+    ``window`` > 0 restricts each query to its sequence's last ``window``
+    tokens."""
     lib = _load()
     q, bt, ctx, (B, Hq, D, NP, P, Hkv), st, qst = _prep(
         q, k_cache, v_cache, block_tables, context_lens, num_kv_heads)
     out = np.zeros((B, Hq, D), dtype=np.float64)
     n = threads or default_threads()
     args = [_ptr(q), qst[0], qst[1], _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], NP,
-            _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale),
-            _ptr(out), n]
-    if mutant:
-        rc = lib.pa_oracle_f64_mutant(*args, mutant)
+            _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale)]
+    if window:
+        rc = lib.pa_oracle_f64_window(*args, int(window), _ptr(out), n, mutant)
+    elif mutant:
+        rc = lib.pa_oracle_f64_mutant(*args, _ptr(out), n, mutant)
     else:
-        rc = lib.pa_oracle_f64(*args)
+        rc = lib.pa_oracle_f64(*args, _ptr(out), n)
     if rc != 0:
         raise OracleError(f"oracle returned {rc}")
     return out
 
 
 def attention_pairs(q, k_cache, v_cache, block_tables, context_lens, scale,
-                    num_kv_heads, pairs, threads: int | None = None):
+                    num_kv_heads, pairs, threads: int | None = None, window: int = 0):
     """fp64 rows [n, D] for the selected (b, h) pairs (an int array [n, 2])."""
     lib = _load()
     q, bt, ctx, (B, Hq, D, NP, P, Hkv), st, qst = _prep(
@@ -137,10 +144,10 @@ def attention_pairs(q, k_cache, v_cache, block_tables, context_lens, scale,
     pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
     out = np.zeros((pairs.shape[0], D), dtype=np.float64)
     n = threads or default_threads()
-    rc = lib.pa_oracle_f64_pairs(
+    rc = lib.pa_oracle_f64_pairs_window(
         _ptr(q), qst[0], qst[1], _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], NP,
         _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale),
-        _ptr(pairs), pairs.shape[0], _ptr(out), n)
+        int(window), _ptr(pairs), pairs.shape[0], _ptr(out), n)
     if rc != 0:
         raise OracleError(f"oracle returned {rc}")
     return out

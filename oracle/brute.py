@@ -35,8 +35,9 @@ def _dense_kv(pool, bt_row, L, P):
     return pages.reshape(n * P, *pool.shape[2:])[:L]        # [L, Hkv, D]
 
 
-def dense(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads):
-    """[B, Hq, D] fp64 via dense per-sequence K/V and a library softmax."""
+def dense(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, window=0):
+    """[B, Hq, D] fp64 via dense per-sequence K/V and a library softmax.
+    ``window`` > 0 keeps only the last ``window`` rows of each sequence."""
     qf = bf16_bits_to_f64(q)
     kf = bf16_bits_to_f64(k_cache)
     vf = bf16_bits_to_f64(v_cache)
@@ -51,6 +52,8 @@ def dense(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads):
             continue
         Kb = _dense_kv(kf, block_tables[b], L, P)              # [L, Hkv, D]
         Vb = _dense_kv(vf, block_tables[b], L, P)
+        if window > 0:
+            Kb, Vb = Kb[-window:], Vb[-window:]
         for h in range(Hq):
             g = h // qg
             logits = (Kb[:, g, :] @ qf[b, h]) * s              # [L]

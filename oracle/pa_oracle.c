@@ -23,11 +23,18 @@
  *   w_t   = exp(x_t - m),  Z = sum_t w_t
  *   o[i]  = (sum_t w_t * V[page][slot][g][i]) / Z
  *
+ * Sliding window (page 3, PR "head_dim-128 arm for the warp-split-KV decode
+ * kernel", LIMITATIONS, names a windowed variant without defining it): with
+ * a window of W >= 1 tokens the query attends to the last W tokens only,
+ * t in [max(0, L - W), L); W == 0 means no window.  This is the plainest
+ * reading: the decode query sits at position L - 1 and sees itself and the
+ * W - 1 tokens before it.
+ *
  * Readings where the pages are silent: L == 0 gives an all-zero row; the
  * scale is the fp32 value the caller passes, widened exactly; there is no
- * mask, window, soft-cap or positional term.  Sums run in ascending t and
- * ascending i inside one (b, h) pair, so the result does not depend on the
- * number of threads.
+ * mask other than the window, no soft-cap and no positional term.  Sums run
+ * in ascending t and ascending i inside one (b, h) pair, so the result does
+ * not depend on the number of threads.
  *
  * Every input is read as exact bf16 bits widened to fp64.  Block-table
  * entries of used pages are range-checked; bad input returns an error code.
@@ -58,6 +65,7 @@ typedef struct {
     const int32_t* ctx;
     int B, Hq, Hkv, D, P;
     double scale;
+    int64_t window;                     /* 0 = none, else the last W tokens  */
     int mutant;
     /* work list */
     const int32_t* pairs;               /* (b, h) pairs, or NULL = all       */
@@ -93,12 +101,16 @@ static int attend_row(const orc_args* a, int b, int h, double* o)
     int g = h / qg;
     if (a->mutant == 1) g = h % a->Hkv;            /* wrong head map          */
 
+    /* first attended token: the window keeps t >= L - W */
+    int64_t t0 = (a->window > 0 && L > a->window) ? L - a->window : 0;
+    if (a->mutant == 9 && a->window > 0 && L > a->window) t0 += 1;   /* window one short */
+
     const uint16_t* qrow = a->q + (int64_t)b * a->q_sb + (int64_t)h * a->q_sh;
     double* x = (double*)malloc((size_t)L * sizeof(double));
     const uint16_t** vrows = (const uint16_t**)malloc((size_t)L * sizeof(void*));
     if (!x || !vrows) { free(x); free(vrows); return ORC_ENOMEM; }
 
-    for (int64_t t = 0; t < L; ++t) {
+    for (int64_t t = t0; t < L; ++t) {
         int64_t lp = t / a->P, slot = t % a->P;
         if (a->mutant == 2) slot = (t + 1) % a->P;        /* off-by-one slot */
         if (lp >= a->max_blk) { free(x); free(vrows); return ORC_EPAGE; }
@@ -121,16 +133,16 @@ static int attend_row(const orc_args* a, int b, int h, double* o)
         if (a->mutant == 4) x[t] = -a->scale * dot;       /* wrong sign      */
     }
 
-    double m = x[0];
-    for (int64_t t = 1; t < L; ++t) if (x[t] > m) m = x[t];
+    double m = x[t0];
+    for (int64_t t = t0 + 1; t < L; ++t) if (x[t] > m) m = x[t];
     double Z = 0.0;
-    for (int64_t t = 0; t < L; ++t) {
+    for (int64_t t = t0; t < L; ++t) {
         x[t] = exp(x[t] - m);                             /* x now holds w_t */
         Z += x[t];
     }
     int64_t t_end = L;
     if (a->mutant == 7) t_end = L - 1;                    /* last token lost */
-    for (int64_t t = 0; t < t_end; ++t) {
+    for (int64_t t = t0; t < t_end; ++t) {
         const uint16_t* vrow = vrows[t];
         for (int i = 0; i < D; ++i) o[i] += x[t] * bf16_bits_to_f64(vrow[i]);
     }
@@ -244,6 +256,46 @@ int pa_oracle_f64_pairs(const uint16_t* q, int64_t q_sb, int64_t q_sh,
     return run(&a, n_threads);
 }
 
+/* Every (b, h) row with a sliding window of `window` tokens (0 = none), and
+ * an optional planted mistake (0 = none; tests of the pins only). */
+int pa_oracle_f64_window(const uint16_t* q, int64_t q_sb, int64_t q_sh,
+                         const uint16_t* k, const uint16_t* v,
+                         int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                         const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                         int B, int Hq, int Hkv, int D, int P, float scale,
+                         int64_t window, double* out, int n_threads, int mutant)
+{
+    orc_args a;
+    if (window < 0) return ORC_EINVAL;
+    fill(&a, q, q_sb, q_sh, k, v, s_page, s_slot, s_head, num_pages, bt, max_blk, ctx,
+         B, Hq, Hkv, D, P, scale);
+    a.out = out;
+    a.n_items = (int64_t)B * Hq;
+    a.window = window;
+    a.mutant = mutant;
+    return run(&a, n_threads);
+}
+
+/* Selected rows with a sliding window (see above). */
+int pa_oracle_f64_pairs_window(const uint16_t* q, int64_t q_sb, int64_t q_sh,
+                               const uint16_t* k, const uint16_t* v,
+                               int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                               const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                               int B, int Hq, int Hkv, int D, int P, float scale,
+                               int64_t window, const int32_t* pairs, int64_t n_pairs, double* out,
+                               int n_threads)
+{
+    orc_args a;
+    if (window < 0) return ORC_EINVAL;
+    fill(&a, q, q_sb, q_sh, k, v, s_page, s_slot, s_head, num_pages, bt, max_blk, ctx,
+         B, Hq, Hkv, D, P, scale);
+    a.out = out;
+    a.pairs = pairs;
+    a.n_items = n_pairs;
+    a.window = window;
+    return run(&a, n_threads);
+}
+
 /* As pa_oracle_f64 with a planted mistake (tests of the pins only). */
 int pa_oracle_f64_mutant(const uint16_t* q, int64_t q_sb, int64_t q_sh,
                          const uint16_t* k, const uint16_t* v,
@@ -261,4 +313,4 @@ int pa_oracle_f64_mutant(const uint16_t* q, int64_t q_sb, int64_t q_sh,
     return run(&a, n_threads);
 }
 
-int pa_oracle_num_mutants(void) { return 8; }
+int pa_oracle_num_mutants(void) { return 9; }

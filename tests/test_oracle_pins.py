@@ -18,7 +18,11 @@ Each pin follows something the source pages or plain mathematics fix:
   kernel", numerics table) and 15/16/17 at page 16;
 * every planted mistake in the oracle (wrong head map, off-by-one slot, lost
   scale, flipped sign, K read for V, dropped term, lost token, lost batch
-  row) is caught by the brute-force pin.
+  row, window one token short) is caught by the brute-force pin;
+* sliding window (page 3, LIMITATIONS, names the windowed variant): a window
+  covering the whole sequence changes nothing, a window of one returns the
+  last V row, and a window equals plain attention over a copy of the
+  sequence's last W tokens relaid into fresh pages, bit for bit.
 """
 import itertools
 import json
@@ -62,9 +66,9 @@ def run_oracle(c, **kw):
                             c["context_lens"], c["scale"], c["num_kv_heads"], **kw)
 
 
-def run_dense(c):
+def run_dense(c, window=0):
     return brute.dense(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
-                       c["context_lens"], c["scale"], c["num_kv_heads"])
+                       c["context_lens"], c["scale"], c["num_kv_heads"], window=window)
 
 
 def rel_err(a, b):
@@ -257,19 +261,85 @@ def test_bad_page_id_is_an_error_not_a_crash():
 
 
 # --------------------------------------------------------------------------
+# sliding window
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [1, 2, 5, 16, 31])
+@pytest.mark.parametrize("P", [1, 4, 16])
+def test_window_matches_dense_bruteforce(W, P):
+    rng = np.random.default_rng(100 + W + P)
+    c = random_case(rng, 4, 8, 2, 32, P, [1, W, W + 1, 3 * W + 7])
+    assert rel_err(run_oracle(c, window=W), run_dense(c, W)) <= 1e-12
+
+
+def test_window_covering_the_sequence_changes_nothing():
+    rng = np.random.default_rng(31)
+    c = random_case(rng, 3, 4, 2, 16, 4, [1, 9, 40])
+    ref = run_oracle(c)
+    for W in (40, 41, 1 << 20):
+        assert np.array_equal(run_oracle(c, window=W), ref)
+
+
+def test_window_one_returns_last_v_row():
+    rng = np.random.default_rng(32)
+    P, Hq, Hkv = 4, 8, 2
+    lens = [1, 5, 17]
+    c = random_case(rng, 3, Hq, Hkv, 16, P, lens)
+    out = run_oracle(c, window=1)
+    vf = brute.bf16_bits_to_f64(c["v_cache"])
+    for b, L in enumerate(lens):
+        page, slot = c["block_tables"][b, (L - 1) // P], (L - 1) % P
+        for h in range(Hq):
+            assert np.array_equal(out[b, h], vf[page, slot, h // (Hq // Hkv)])
+
+
+@pytest.mark.parametrize("W,P", [(3, 4), (16, 16), (21, 8), (33, 32)])
+def test_window_equals_truncated_sequence(W, P):
+    """Each sequence's last W tokens copied, in order, into fresh pages: plain
+    attention over the copy equals windowed attention over the original, bit
+    for bit (the same dot products and the same summation order)."""
+    rng = np.random.default_rng(40 + W)
+    lens = np.array([1, W - 1 if W > 1 else 1, W, W + 1, 4 * W + 3], dtype=np.int32)
+    B, Hq, Hkv, D = len(lens), 8, 2, 32
+    c = random_case(rng, B, Hq, Hkv, D, P, lens)
+    k, v, bt = c["k_cache"], c["v_cache"], c["block_tables"]
+    new_lens = np.minimum(lens, W)
+    n_b = (new_lens + P - 1) // P
+    NP2 = int(n_b.sum())
+    k2 = np.zeros((NP2, P, Hkv, D), dtype=np.uint16)
+    v2 = np.zeros_like(k2)
+    bt2 = np.full((B, int(n_b.max())), -1, dtype=np.int32)
+    page = 0
+    for b in range(B):
+        L, t0 = int(lens[b]), int(lens[b] - new_lens[b])
+        for j in range(n_b[b]):
+            bt2[b, j] = page + j
+        for t in range(t0, L):
+            src_p, src_s = bt[b, t // P], t % P
+            u = t - t0
+            k2[page + u // P, u % P] = k[src_p, src_s]
+            v2[page + u // P, u % P] = v[src_p, src_s]
+        page += n_b[b]
+    c2 = dict(c, k_cache=k2, v_cache=v2, block_tables=bt2, context_lens=new_lens)
+    assert np.array_equal(run_oracle(c, window=W), run_oracle(c2))
+
+
+# --------------------------------------------------------------------------
 # planted mistakes: every mutant must be caught
 # --------------------------------------------------------------------------
-def test_every_planted_mistake_is_caught():
+@pytest.mark.parametrize("window", [0, 5])
+def test_every_planted_mistake_is_caught(window):
     rng = np.random.default_rng(22)
     c = random_case(rng, 3, 8, 2, 16, 4, [1, 7, 13])
-    ref = run_dense(c)
-    assert rel_err(run_oracle(c), ref) <= 1e-12
+    ref = run_dense(c, window)
+    assert rel_err(run_oracle(c, window=window), ref) <= 1e-12
     for m in range(1, oracle.num_mutants() + 1):
+        if m == 9 and not window:
+            continue                        # the window mistake needs a window
         try:
-            out = run_oracle(c, mutant=m)
+            out = run_oracle(c, mutant=m, window=window)
         except oracle.OracleError:
             continue                        # an error is also a catch
-        assert rel_err(out, ref) > 1e-6, f"mutant {m} slipped through"
+        assert rel_err(out, ref) > 1e-6, f"mutant {m} slipped through (window {window})"
 
 
 # --------------------------------------------------------------------------
