@@ -157,23 +157,35 @@ def launch_info(st):
     return kernel, (merge if st["merge_launches"] else None), launch
 
 
+# Extra per-config lines: the sliding-window variant on two workloads.
+WINDOWED = (("long_ctx_gqa8", 4096), ("hd256_gqa4", 1024))
+
+
 def per_config(pa, knobs, torch, workloads_mod):
     """Time every workload: warm (inputs reused, MALL may hold them) and, for
     footprints that fit the 256 MB MALL, cold (calls rotate over replicas of
-    the KV pools totalling >= 1 GB)."""
+    the KV pools totalling >= 1 GB).  Windowed lines count the KV bytes of
+    the attended tokens only."""
     import numpy as np
     res = {}
-    for name in workloads_mod.ORDER:
+    runs = [(name, 0) for name in workloads_mod.ORDER] + list(WINDOWED)
+    for name, window in runs:
         w = workloads_mod.WORKLOADS[name]
         if name == "long_ctx_gqa8":
             d = workloads_mod.device_inputs(w, seed=0)
         else:
             d = workloads_mod.to_device(workloads_mod.make_inputs(w, seed=0))
         lens = d.layout.context_lens
-        kvb = workloads_mod.kv_bytes(w, lens)
+        kn = dict(knobs, window=window)
+        if window:
+            kvb = int(np.minimum(lens.astype(np.int64), window).sum()) * w.num_kv_heads * w.head_dim * 4
+        else:
+            kvb = workloads_mod.kv_bytes(w, lens)
         n_calls = w.calls if w.calls > 1 else 1
-        calls = [make_call(pa, d, i, knobs)[0] for i in range(n_calls)]
+        calls = [make_call(pa, d, i, kn)[0] for i in range(n_calls)]
         entry = {"kv_bytes_per_call": kvb, "calls": n_calls}
+        if window:
+            entry["window"] = window
         if name == "long_ctx_gqa8":
             ms = event_time_ms(calls[0], 3, torch)
             ms = event_time_ms(calls[0], 10, torch) / 10
@@ -196,7 +208,7 @@ def per_config(pa, knobs, torch, workloads_mod):
                 cold_calls = []
                 for i in range(n_calls):
                     for d2 in reps_k:
-                        cold_calls.append(make_call(pa, d2, i, knobs)[0])
+                        cold_calls.append(make_call(pa, d2, i, kn)[0])
                 cold_calls = cold_calls[:min(len(cold_calls), max(R, 2048))]
                 entry["us_per_call_cold"] = round(graph_time_us(cold_calls, 5, torch), 3)
                 entry["cold_replicas"] = R
@@ -209,8 +221,9 @@ def per_config(pa, knobs, torch, workloads_mod):
                 gbs = kvb / (entry[key] * 1e-6) / 1e9
                 entry[key.replace("us_per_call", "kv_GBps")] = round(gbs, 1)
                 entry[key.replace("us_per_call", "hbm_frac")] = round(gbs / HBM_PEAK_GBS, 4)
-        res[name] = entry
-        log(f"[per_config] {name}: {entry}")
+        key = f"{name}_w{window}" if window else name
+        res[key] = entry
+        log(f"[per_config] {key}: {entry}")
         del d, calls
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

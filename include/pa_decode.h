@@ -102,8 +102,8 @@ typedef struct pa_tensor {
  * Work is split over workgroups either as fixed-size partitions of each
  * sequence or, on the MFMA variant, as equal shares of all sequences' work
  * (chosen automatically for large calls: at most 4096 sequences and at
- * least 131072 units of (sequence, query block, 16 tokens of capacity
- * MaxBlk * P)); partial results are
+ * least 262144 units of (sequence, query block, 16 tokens of capacity
+ * MaxBlk * P, or of the window)); partial results are
  * merged with the log-sum-exp rule by a second kernel.  The library keeps a
  * per-device workspace for the partials, grown on demand with hipMalloc and
  * freed by pa_release(); calls that use it must not overlap in time on one
@@ -147,7 +147,11 @@ typedef struct pa_opts {
     int32_t shares;             /* balanced schedule: 0 = automatic (one per
                                    compute unit at most), else the number of
                                    workgroups, 1 .. 1024                       */
-    int32_t reserved[4];        /* must be zero                                */
+    int32_t window;             /* sliding window: 0 = attend to all L tokens;
+                                   W >= 1 = only the last W, tokens
+                                   [max(0, L - W), L) (page 3, LIMITATIONS,
+                                   the windowed variant)                       */
+    int32_t reserved[3];        /* must be zero                                */
 } pa_opts;
 
 /*

@@ -32,7 +32,7 @@ class PaTensor(ctypes.Structure):
 class PaOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
                 ("schedule", ctypes.c_int32), ("shares", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class PaStats(ctypes.Structure):
@@ -130,9 +130,11 @@ def _require_device(*ts):
             raise ValueError("all tensors must live on the same GPU device")
 
 
-def make_opts(variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0) -> PaOpts:
+def make_opts(variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0,
+              window: int = 0) -> PaOpts:
     o = PaOpts()
     o.shares = int(shares)
+    o.window = int(window)
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     o.partition_tokens = int(partition_tokens)
     o.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
@@ -214,12 +216,13 @@ def pa_release() -> None:
 # ------------------------------------------------------------------ convenience
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None, *,
            variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0,
-           workspace=None, stream=None):
+           window: int = 0, workspace=None, stream=None):
     """Decode paged attention on torch tensors.
 
     q [B, Hq, D] bf16; k_cache/v_cache [NP, P, Hkv, D] bf16 (NHD pool);
     block_tables [B, MaxBlk] int32; context_lens [B] int32; scale defaults to
-    1/sqrt(D).  Returns out [B, Hq, D] bf16.  The split-KV workspace comes
+    1/sqrt(D); ``window`` > 0 attends to each sequence's last ``window``
+    tokens only.  Returns out [B, Hq, D] bf16.  The split-KV workspace comes
     zero-filled from torch's caching allocator unless one is given (a given
     one must start with 256 zero bytes; see pa_decode_ex).
     """
@@ -230,7 +233,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    opts = make_opts(variant, partition_tokens, schedule, shares)
+    opts = make_opts(variant, partition_tokens, schedule, shares, window)
     if workspace is None:
         n = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], P, opts)
         if n:

@@ -26,6 +26,7 @@ struct DecodeParams {
     int*  lean_meta;                                        // balanced schedule: S[0..B], s0, s1, n_wg
     int*  lean_ctr;                                         // balanced schedule: next unit, finished WGs
     int   lean_page_slots;                                  // balanced schedule: page-id LDS entries
+    int   window;                                           // 0 = none, else the last `window` tokens
     float scale_log2;                                       // scale * log2(e)
 };
 
@@ -84,6 +85,14 @@ __device__ __forceinline__ u32x4 load16_nt(const uint16_t* p) {
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // Logical page index and slot of token t (P a power of two takes shifts).
+// First attended token t_begin (the window keeps [L - window, L)) and the
+// start t_base of the work, t_begin rounded down to a 16-token tile: kernels
+// walk [t_base, L) in tiles and mask the tokens below t_begin.
+__device__ __forceinline__ void window_bounds(const DecodeParams& p, int L, int& t_begin, int& t_base) {
+    t_begin = (p.window > 0 && L > p.window) ? L - p.window : 0;
+    t_base = t_begin & ~15;
+}
+
 __device__ __forceinline__ void page_slot(const DecodeParams& p, int t, int& lp, int& slot) {
     if (p.p_shift >= 0) {
         lp = t >> p.p_shift;

@@ -84,15 +84,17 @@ __device__ __forceinline__ int k_col(int i, int n, int q) {
 }
 
 // Issue the loads of the 16-token tile starting at tb.  K: see k_row/k_col
-// (A operand layout); V: tokens tb + 4q + jj, 16 lanes per row.  Tokens at
-// or past te are clamped to te - 1, a real row, and masked out of the
-// softmax.  PAGE16: the page size is a power of two >= 16, so the tile lies
-// in one page; the page base is wave-uniform and each lane adds a fixed
-// 32-bit offset.
+// (A operand layout); V: tokens tb + 4q + jj, 16 lanes per row.  Tokens
+// outside [t_min, te) -- past the end, or before a window -- are clamped to
+// the nearest row inside it and masked out of the softmax, so nothing
+// outside is read (a weight of 0 times a non-finite row would not vanish).
+// PAGE16: the page size is a power of two >= 16, so the tile lies in one
+// page; the page base is wave-uniform and each lane adds a fixed 32-bit
+// offset.
 template <int D, bool PAGE16, bool HALF>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pages, int pg0, int g,
-                                          int n, int q, const LaneOffsets& lo, int tb, int te,
-                                          TileFrag<D>& f) {
+                                          int n, int q, const LaneOffsets& lo, int tb, int t_min,
+                                          int te, TileFrag<D>& f) {
     constexpr int KK = TileFrag<D>::KK;
     if constexpr (PAGE16) {
         const int lp = tb >> p.p_shift;
@@ -101,7 +103,7 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pa
         const uint16_t* kt = p.k + (int64_t)page * p.k_sp + (int64_t)g * p.k_sh + (int64_t)slot0 * p.k_ss;
         const uint16_t* vt = p.v + (int64_t)page * p.v_sp + (int64_t)g * p.v_sh + (int64_t)slot0 * p.v_ss;
         const int ks = (int)p.k_ss, vs = (int)p.v_ss;
-        if (tb + kTile <= te) {                 // full tile (wave-uniform)
+        if (tb + kTile <= te && tb >= t_min) {  // full tile (wave-uniform)
 #pragma unroll
             for (int i = 0; i < KK; ++i) {
                 const int extra = HALF ? (i / (D / 64)) * 8 * ks + 64 * (i % (D / 64)) : 32 * i;
@@ -112,14 +114,14 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pa
 #pragma unroll
                 for (int hh = 0; hh < TileFrag<D>::VH; ++hh)
                     f.v[jj][hh] = load16_nt(vt + lo.v[jj] + 128 * hh);
-        } else {                                // tail tile: clamp rows to te - 1
-            const int last = te - 1 - tb;
+        } else {                                // edge tile: clamp rows into [t_min, te)
+            const int first = max(t_min - tb, 0), last = te - 1 - tb;
 #pragma unroll
             for (int i = 0; i < KK; ++i)
-                f.k[i] = load16_nt(kt + min(k_row<D, HALF>(i, n), last) * ks + k_col<D, HALF>(i, n, q));
+                f.k[i] = load16_nt(kt + clampi(k_row<D, HALF>(i, n), first, last) * ks + k_col<D, HALF>(i, n, q));
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int vo = min(4 * q + jj, last) * vs + 8 * n;
+                const int vo = clampi(4 * q + jj, first, last) * vs + 8 * n;
 #pragma unroll
                 for (int hh = 0; hh < TileFrag<D>::VH; ++hh) f.v[jj][hh] = load16_nt(vt + vo + 128 * hh);
             }
@@ -128,13 +130,13 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pa
         const int64_t gk = (int64_t)g * p.k_sh, gv = (int64_t)g * p.v_sh;
 #pragma unroll
         for (int i = 0; i < KK; ++i) {
-            const int tk = min(tb + k_row<D, HALF>(i, n), te - 1);
+            const int tk = clampi(tb + k_row<D, HALF>(i, n), t_min, te - 1);
             f.k[i] = load16_nt(p.k + row_offset(p, s_pages, pg0, tk, p.k_sp, p.k_ss, gk) +
                                k_col<D, HALF>(i, n, q));
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int tv = min(tb + 4 * q + jj, te - 1);
+            const int tv = clampi(tb + 4 * q + jj, t_min, te - 1);
             const uint16_t* vr = p.v + row_offset(p, s_pages, pg0, tv, p.v_sp, p.v_ss, gv) + 8 * n;
 #pragma unroll
             for (int hh = 0; hh < TileFrag<D>::VH; ++hh) f.v[jj][hh] = load16_nt(vr + 128 * hh);
@@ -173,8 +175,8 @@ __device__ __forceinline__ float xsum32(float x) {
 // One 16-token tile: logits on MFMA, online-softmax update, O^T += V^T P^T.
 template <int D, bool HALF>
 __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<D>& cur,
-                                          const u32x4 (&qop)[D / 32], int tb, int te, int q,
-                                          bool col_live, f32x4 (&o)[D / 16], float& m_run,
+                                          const u32x4 (&qop)[D / 32], int tb, int t_min, int te,
+                                          int q, bool col_live, f32x4 (&o)[D / 16], float& m_run,
                                           float& l_run) {
     constexpr int KK = TileFrag<D>::KK;
     constexpr int VH = TileFrag<D>::VH;
@@ -214,7 +216,8 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        sv[r] = (col_live && tb + 4 * q + r < te) ? s[r] * p.scale_log2 : -INFINITY;
+        const int t = tb + 4 * q + r;
+        sv[r] = (col_live && t < te && t >= t_min) ? s[r] * p.scale_log2 : -INFINITY;
         mt = fmaxf(mt, sv[r]);
     }
     mt = xmax32(xmax16(mt));
@@ -284,31 +287,31 @@ template <int D, bool PAGE16, bool HALF, int NBUF>
 __device__ __forceinline__ void run_tiles(const DecodeParams& p, const int* s_pages, int pg0, int g,
                                           int n, int q, int wave, const LaneOffsets& lo,
                                           const u32x4 (&qop)[D / 32], bool col_live, int ts, int te,
-                                          f32x4 (&o)[D / 16], float& m_run, float& l_run) {
+                                          int t_min, f32x4 (&o)[D / 16], float& m_run, float& l_run) {
     const int n_tiles = (max(te - ts, 0) + kTile - 1) / kTile;
     const int n_my = n_tiles > wave ? (n_tiles - wave + kMWaves - 1) / kMWaves : 0;
     auto tile_tb = [&](int k) { return ts + (wave + k * kMWaves) * kTile; };
     TileFrag<D> fb[NBUF];
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i)
-        if (i < n_my) load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(i), te, fb[i]);
+        if (i < n_my) load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(i), t_min, te, fb[i]);
     int k = 0;
     for (; k + 2 * NBUF - 2 < n_my; k += NBUF) {
 #pragma unroll
         for (int i = 0; i < NBUF; ++i) {
-            load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
+            load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), t_min, te,
                                        fb[(i + NBUF - 1) % NBUF]);
             __builtin_amdgcn_sched_barrier(0);
-            tile_step<D, HALF>(p, fb[i], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
+            tile_step<D, HALF>(p, fb[i], qop, tile_tb(k + i), t_min, te, q, col_live, o, m_run, l_run);
         }
     }
 #pragma unroll
     for (int i = 0; i < 2 * NBUF - 1; ++i) {
         if (k + i < n_my) {
             if (k + i + NBUF - 1 < n_my)
-                load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), te,
+                load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), t_min, te,
                                            fb[(i + NBUF - 1) % NBUF]);
-            tile_step<D, HALF>(p, fb[i % NBUF], qop, tile_tb(k + i), te, q, col_live, o, m_run, l_run);
+            tile_step<D, HALF>(p, fb[i % NBUF], qop, tile_tb(k + i), t_min, te, q, col_live, o, m_run, l_run);
         }
     }
 }
@@ -416,13 +419,20 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     // Page ids of the partition's token range are fetched without waiting for
     // the sequence length (entries past the sequence's end are never used),
     // so the two dependent reads of the prologue overlap.
-    const int ts = part * p.part_tokens;
+    // With a window the partitions start at the window's first tile, so the
+    // sequence length is needed first.
+    int L = 0, t_begin = 0, t_base = 0;
+    if (p.window > 0) {
+        L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+        window_bounds(p, L, t_begin, t_base);
+    }
+    const int ts = t_base + part * p.part_tokens;
     extern __shared__ int s_pages[];
     int pg0, lp_hi, unused;
     page_slot(p, ts, pg0, unused);
     page_slot(p, ts + p.part_tokens - 1, lp_hi, unused);
     fetch_pages(p, b, pg0, lp_hi, s_pages, tid);
-    const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+    if (p.window <= 0) L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     if (ts >= L && part > 0) return;
     const int te = min(L, ts + p.part_tokens);
 
@@ -439,7 +449,8 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     lo.k = k_row<D, HALF>(0, n) * (int)p.k_ss + k_col<D, HALF>(0, n, q);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
-    run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, ts, te, o, m_run, l_run);
+    run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, ts, te, t_begin, o,
+                                     m_run, l_run);
     l_run = xsum32(xsum16(l_run));              // row sums over the four 16-lane rows
 
     __shared__ MergeLds<D> lds;
@@ -533,14 +544,17 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
     int* s_pages = s_dyn;                       // kLeanTokensPerFill / P + 2 entries
     int* s_pref = s_dyn + p.lean_page_slots;    // B + 1 tile prefix sums
 
-    // Tile prefix sums S[b] = sum_{b' < b} ceil(L_b' / 16), in chunks of 256.
+    // Tile prefix sums S[b] = sum_{b' < b} ceil((L_b' - t_base_b') / 16), in
+    // chunks of 256 (t_base = 0 without a window).
     __shared__ int s_carry;
     if (tid == 0) s_carry = 0;
     __syncthreads();
     for (int c = 0; c < p.B; c += kMBlock) {
         const int bb = c + tid;
         const int L = bb < p.B ? clampi(p.ctx[bb], 0, p.max_blk * p.P) : 0;
-        int v = (L + kTile - 1) / kTile;
+        int t_begin, t_base;
+        window_bounds(p, L, t_begin, t_base);
+        int v = (L - t_base + kTile - 1) / kTile;
         // inclusive scan of v over the workgroup: per-wave DPP-free shuffle scan, then across waves
         for (int off = 1; off < 64; off <<= 1) {
             const int t = __shfl_up(v, off);
@@ -604,7 +618,9 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
             const int h0 = qb * qw;
             const int g = h0 / (p.Hq / p.Hkv);
             const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
-            const int ts = t_lo * kTile, te = min(t_hi * kTile, L);
+            int t_begin, t_base;
+            window_bounds(p, L, t_begin, t_base);
+            const int ts = t_base + t_lo * kTile, te = min(t_base + t_hi * kTile, L);
 
             u32x4 qop[KK];
             load_q<D, HALF>(p, b, h0, qw, n, q, qop);
@@ -629,8 +645,8 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
                 if (c0 != ts) __syncthreads();
                 fetch_pages(p, b, pg0, lp1, s_pages, tid);
                 __syncthreads();
-                run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, c0, c1, o,
-                                                 m_run, l_run);
+                run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, c0, c1,
+                                                 t_begin, o, m_run, l_run);
             }
             l_run = xsum32(xsum16(l_run));
             merge_waves<D>(lds, o, m_run, l_run, qw, n, q, wave, tid,

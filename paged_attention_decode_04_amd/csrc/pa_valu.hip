@@ -40,13 +40,15 @@ struct RowFrag {
 
 template <int D, int U>
 __device__ __forceinline__ void load_rows(const DecodeParams& p, const int* s_pages, int pg0,
-                                          int g, int c, int t_first, int te, int ts,
+                                          int g, int c, int t_first, int te, int ts, int t_min,
                                           RowFrag<D, U>& f) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int t = t_first + u * kRowsPerBlock;
-        f.valid[u] = t < te;
-        const int tt = f.valid[u] ? t : ts;     // a real token: never read past L
+        f.valid[u] = t < te && t >= t_min;
+        // Masked rows read a token inside [t_min, te) instead: a weight of 0
+        // times a row outside (past L, or before the window) need not vanish.
+        const int tt = f.valid[u] ? t : max(ts, t_min);
         int lp, slot;
         page_slot(p, tt, lp, slot);
         const int64_t page = s_pages[lp - pg0];
@@ -75,7 +77,9 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
     const int g = h0 / qg;
 
     const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
-    const int ts = part * p.part_tokens;
+    int t_begin, t_base;
+    window_bounds(p, L, t_begin, t_base);
+    const int ts = t_base + part * p.part_tokens;
     if (ts >= L && part > 0) return;            // unused partition (merge skips it)
     const int te = min(L, ts + p.part_tokens);
     const int n_tok = max(te - ts, 0);
@@ -121,11 +125,11 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
     constexpr int TPI = kRowsPerBlock * U;      // tokens per iteration per workgroup
     const int my_row = wave * kRowsPerWave + row;
     RowFrag<D, U> cur;
-    if (n_tok > 0) load_rows<D, U>(p, s_pages, pg0, g, c, ts + my_row, te, ts, cur);
+    if (n_tok > 0) load_rows<D, U>(p, s_pages, pg0, g, c, ts + my_row, te, ts, t_begin, cur);
     for (int base = 0; base < n_tok; base += TPI) {
         RowFrag<D, U> nxt;
         const bool more = base + TPI < n_tok;
-        if (more) load_rows<D, U>(p, s_pages, pg0, g, c, ts + base + TPI + my_row, te, ts, nxt);
+        if (more) load_rows<D, U>(p, s_pages, pg0, g, c, ts + base + TPI + my_row, te, ts, t_begin, nxt);
 
         float s[U][QW];
         float vf[U][E];
@@ -248,7 +252,9 @@ template <int D>
 __global__ __launch_bounds__(64) void pa_lse_merge_kernel(DecodeParams p) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
-    const int n_used = (L + p.part_tokens - 1) / p.part_tokens;
+    int t_begin, t_base;
+    window_bounds(p, L, t_begin, t_base);
+    const int n_used = (L - t_base + p.part_tokens - 1) / p.part_tokens;
     merge_partials<D>(p, ((int64_t)b * p.Hq + h) * p.n_part, 1, n_used,
                       p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
 }

@@ -125,6 +125,8 @@ def test_opts_are_validated():
     assert check(args(), o) == pa.PA_EINVAL
     o = pa.make_opts("mfma", 0, 3)
     assert check(args(), o) == pa.PA_EINVAL
+    assert check(args(), pa.make_opts(window=-1)) == pa.PA_EINVAL
+    assert check(args(), pa.make_opts(window=7)) == pa.PA_OK
     for sched in ("auto", "partitions", "balanced"):
         assert check(args(), pa.make_opts("mfma", 0, sched)) == pa.PA_OK
 
@@ -199,6 +201,11 @@ def test_workspace_bytes():
     small = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, None)
     assert small == pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16,
                                                  pa.make_opts("mfma", 0, "partitions"))
+    # a window bounds the span a sequence's work covers (W + 15 tokens): the
+    # same large call with a 4096-token window falls below the balanced
+    # threshold and splits into ceil(4111 / 4096) = 2 partitions of 4096
+    n = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, pa.make_opts(window=4096))
+    assert n == HDR + rnd(64 * 64 * 2 * 128 * 4) + rnd(64 * 64 * 2 * 4)
     # setting partition_tokens alone selects the partition schedule
     n = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma", 64))
     assert n == HDR + rnd(1 * 16 * 18 * 128 * 4) + rnd(1 * 16 * 18 * 4)

@@ -40,13 +40,13 @@ def knobs(variant, tokens):
     return [dict(partition_tokens=T) for T in tokens]
 
 
-def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0):
+def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0):
     kernel, schedule = _MODE[variant]
     q, k, v = d.call(call)
     out = torch.full_like(q, float("nan"))      # every row must be written
     pa.pa_reset_stats()
     pa.decode(q, k, v, d.block_tables, d.context_lens, d.w.scale, out=out, variant=kernel,
-              partition_tokens=partition_tokens, schedule=schedule, shares=shares)
+              partition_tokens=partition_tokens, schedule=schedule, shares=shares, window=window)
     torch.cuda.synchronize()
     s = pa.pa_get_stats()
     assert s["calls"] == 1
@@ -60,10 +60,10 @@ def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0):
     return bits(out), s
 
 
-def oracle_run(inp, call=0):
+def oracle_run(inp, call=0, window=0):
     q, k, v = inp.call(call)
     return oracle.attention(q, k, v, inp.block_tables, inp.context_lens, inp.w.scale,
-                            inp.w.num_kv_heads)
+                            inp.w.num_kv_heads, window=window)
 
 
 def assert_parity(y, ref, what=""):
@@ -382,3 +382,67 @@ def test_balanced_workspace_reuse_and_counters():
             if first is None:
                 first = y
             assert np.array_equal(y, first), f"call {i}: rerun differs"
+
+
+# ------------------------------------------------------------------ sliding window
+def poison_before_window(inp, W):
+    """Copy of the inputs whose K/V rows before each sequence's window hold
+    bf16 NaN: a kernel that reads them into the softmax shows it."""
+    k, v = inp.k.copy(), inp.v.copy()
+    P = inp.w.page_size
+    for b, L in enumerate(inp.context_lens):
+        for t in range(max(0, int(L) - W)):
+            pg, sl = inp.block_tables[b, t // P], t % P
+            k[:, pg, sl] = 0x7FC0
+            v[:, pg, sl] = 0x7FC0
+    return workloads.Inputs(inp.w, inp.q, k, v, inp.layout)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 16), (256, 8, 2, 32), (128, 64, 8, 16),
+                                        (128, 16, 4, 7)])
+def test_window_parity_poisoned(variant, D, Hq, Hkv, P):
+    """Windows of 1 token to beyond the longest sequence, every row before a
+    window set to NaN, lengths on and off tile and page boundaries."""
+    w = custom(batch=7, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
+               ctx=(1, 15, 16, 17, 300, 1000, 2500))
+    inp0 = make_inputs(w, seed=D + Hq + P)
+    for W in (1, 7, 16, 100, 1000, 4096):
+        inp = poison_before_window(inp0, W)
+        d = to_device(inp)
+        ref = oracle_run(inp, window=W)
+        for kn in knobs(variant, (0, 64)):
+            y, _ = gpu_run(d, variant=variant, window=W, **kn)
+            assert np.all(np.isfinite(workloads_f32(y))), f"W={W} {kn}: NaN leaked from before the window"
+            assert_parity(y, ref, f"W={W} {kn}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_window_covering_every_sequence_is_bitwise_unwindowed(variant):
+    inp = make_inputs("hd256_gqa4", seed=5)
+    d = to_device(inp)
+    y0, _ = gpu_run(d, variant=variant)
+    Lmax = int(inp.context_lens.max())
+    for W in (Lmax, Lmax + 1, 1 << 30):
+        y1, _ = gpu_run(d, variant=variant, window=W)
+        assert np.array_equal(y0, y1), f"W={W}"
+
+
+@pytest.mark.parametrize("variant", ["mfma", "mfma-bal"])
+def test_window_long_context_sampled(variant):
+    """Full-size long-context workload with a 4096-token window; the oracle
+    evaluates a sample of (sequence, head) rows with the same window."""
+    W = 4096
+    w = WORKLOADS["long_ctx_gqa8"]
+    d = workloads.device_inputs(w, seed=0)
+    y, s = gpu_run(d, variant=variant, window=W)
+    host = workloads.host_copy(d)
+    rng = np.random.default_rng(7)
+    pairs = np.stack([rng.integers(0, w.batch, 48), rng.integers(0, w.num_q_heads, 48)],
+                     1).astype(np.int32)
+    ref = oracle.attention_pairs(host.q[0], host.k[0], host.v[0], host.block_tables,
+                                 host.context_lens, w.scale, w.num_kv_heads, pairs, window=W)
+    yb = y.reshape(w.batch, w.num_q_heads, w.head_dim)[pairs[:, 0], pairs[:, 1]]
+    assert_parity(yb, ref, f"long ctx W={W} sampled {len(pairs)} rows")
+    del d, host
+    torch.cuda.empty_cache()
