@@ -155,3 +155,30 @@ def attention_pairs(q, k_cache, v_cache, block_tables, context_lens, scale,
 
 def num_mutants() -> int:
     return _load().pa_oracle_num_mutants()
+
+
+def cache_append(k_cache, v_cache, block_tables, context_lens, k_new, v_new):
+    """KV-cache append, the step before decode attention: sequence b's newest
+    token, position t = context_lens[b] - 1 (the length already counts it),
+    has its K and V rows written to page block_tables[b][t // P], slot t % P.
+    Sequences with no tokens write nothing.  Returns new (k_cache, v_cache)
+    arrays (uint16 bf16 bits); the inputs are not modified.
+
+    The pages name no cache-write kernel; this is the plainest neighbour of
+    the decode step (the cache layout is the same NHD pool the decode reads,
+    page 1, issue "ROCm gfx1200: PagedAttnOnline is 8.1x slower per call",
+    section "Where to look")."""
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    P = k_cache.shape[1]
+    for b, L in enumerate(np.asarray(context_lens)):
+        L = int(L)
+        if L <= 0:
+            continue
+        t = L - 1
+        page = int(block_tables[b][t // P])
+        if not 0 <= page < k_cache.shape[0]:
+            raise OracleError(f"sequence {b}: page id {page} out of range")
+        k_out[page, t % P] = k_new[b]
+        v_out[page, t % P] = v_new[b]
+    return k_out, v_out

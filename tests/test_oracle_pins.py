@@ -19,6 +19,9 @@ Each pin follows something the source pages or plain mathematics fix:
 * every planted mistake in the oracle (wrong head map, off-by-one slot, lost
   scale, flipped sign, K read for V, dropped term, lost token, lost batch
   row, window one token short) is caught by the brute-force pin;
+* KV-cache append writes exactly the newest token's K/V rows: every other
+  byte is unchanged, the rows read back through the block table, and
+  appending into a fresh one-token sequence makes attention return v_new;
 * sliding window (page 3, LIMITATIONS, names the windowed variant): a window
   covering the whole sequence changes nothing, a window of one returns the
   last V row, and a window equals plain attention over a copy of the
@@ -321,6 +324,57 @@ def test_window_equals_truncated_sequence(W, P):
         page += n_b[b]
     c2 = dict(c, k_cache=k2, v_cache=v2, block_tables=bt2, context_lens=new_lens)
     assert np.array_equal(run_oracle(c, window=W), run_oracle(c2))
+
+
+# --------------------------------------------------------------------------
+# KV-cache append
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("P", [1, 7, 16])
+def test_append_touches_only_the_newest_slots(P):
+    rng = np.random.default_rng(50 + P)
+    lens = [0, 1, P, P + 1, 3 * P + 2]
+    c = random_case(rng, len(lens), 8, 2, 32, P, lens)
+    k_new = bf16(rng, (len(lens), 2, 32))
+    v_new = bf16(rng, (len(lens), 2, 32))
+    k2, v2 = oracle.cache_append(c["k_cache"], c["v_cache"], c["block_tables"], c["context_lens"],
+                                 k_new, v_new)
+    changed = np.zeros(c["k_cache"].shape[:2], dtype=bool)
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        pg, sl = c["block_tables"][b, (L - 1) // P], (L - 1) % P
+        changed[pg, sl] = True
+        assert np.array_equal(k2[pg, sl], k_new[b]) and np.array_equal(v2[pg, sl], v_new[b])
+    assert np.array_equal(k2[~changed], c["k_cache"][~changed])
+    assert np.array_equal(v2[~changed], c["v_cache"][~changed])
+    assert int(changed.sum()) == sum(1 for L in lens if L > 0)
+
+
+def test_append_then_attention_of_a_one_token_sequence_is_v_new():
+    """Appending into sequences of length 1 and attending gives v_new exactly
+    (the ctx = 1 pin of attention, reached through the append)."""
+    rng = np.random.default_rng(60)
+    B, Hq, Hkv, D, P = 4, 8, 2, 32, 4
+    c = random_case(rng, B, Hq, Hkv, D, P, [1] * B)
+    k_new = bf16(rng, (B, Hkv, D))
+    v_new = bf16(rng, (B, Hkv, D))
+    k2, v2 = oracle.cache_append(c["k_cache"], c["v_cache"], c["block_tables"], c["context_lens"],
+                                 k_new, v_new)
+    out = run_oracle(dict(c, k_cache=k2, v_cache=v2))
+    vf = brute.bf16_bits_to_f64(v_new)
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(out[b, h], vf[b, h // (Hq // Hkv)])
+
+
+def test_append_bad_page_id_is_an_error():
+    rng = np.random.default_rng(61)
+    c = random_case(rng, 2, 4, 2, 16, 4, [3, 5])
+    bt = c["block_tables"].copy()
+    bt[1, 1] = 10 ** 6
+    with pytest.raises(oracle.OracleError):
+        oracle.cache_append(c["k_cache"], c["v_cache"], bt, c["context_lens"],
+                            bf16(rng, (2, 2, 16)), bf16(rng, (2, 2, 16)))
 
 
 # --------------------------------------------------------------------------
