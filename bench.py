@@ -230,6 +230,28 @@ def per_config(pa, knobs, torch, workloads_mod):
     return res
 
 
+def append_line(pa, torch, workloads_mod, name="long_ctx_gqa8"):
+    """KV-cache append at one workload's geometry (one new token per
+    sequence): graph-timed microseconds per call.  Algorithmic bytes: the new
+    K and V rows read and written once."""
+    w = workloads_mod.WORKLOADS[name]
+    d = workloads_mod.device_inputs(w, seed=0) if name == "long_ctx_gqa8" else \
+        workloads_mod.to_device(workloads_mod.make_inputs(w, seed=0))
+    B, Hkv, D = w.batch, w.num_kv_heads, w.head_dim
+    kn = torch.randn((B, Hkv, D), device="cuda").to(torch.bfloat16)
+    vn = torch.randn((B, Hkv, D), device="cuda").to(torch.bfloat16)
+    k, v = d.k[0], d.v[0]
+    calls = [lambda: pa.cache_append(kn, vn, k, v, d.block_tables, d.context_lens)] * 64
+    us = graph_time_us(calls, 50, torch)
+    nbytes = 2 * 2 * B * Hkv * D * 2
+    entry = {"workload": name, "us_per_call": round(us, 3), "bytes_per_call": nbytes,
+             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "kernel": "pa_cache_append_kernel"}
+    log(f"[append] {entry}")
+    del d
+    torch.cuda.empty_cache()
+    return entry
+
+
 def cpu_baseline(d, w, target_s, workloads_mod):
     """The oracle as it stands, on the host cores, over whole sequences of the
     same workload (all query heads) until about target_s seconds."""
@@ -374,6 +396,7 @@ def main():
         log(f"[bench] copy probe: {result['copy_probe']}")
     if not args.profile and not args.no_per_config:
         result["per_config"] = per_config(pa, knobs, torch, wl)
+        result["append"] = append_line(pa, torch, wl)
     if not args.profile and not args.no_cpu_baseline:
         t = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds, wl)

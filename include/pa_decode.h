@@ -123,6 +123,39 @@ int pa_decode(const pa_tensor* q,
               const pa_tensor* out,
               void* stream);
 
+/*
+ * pa_cache_append -- enqueue the KV-cache write of every sequence's newest
+ * token: the step that precedes pa_decode in a decode step.  Not on the
+ * source pages (their kernels only read the cache); the plainest neighbour of
+ * the decode step, on the same NHD pool (page 1, issue "ROCm gfx1200:
+ * PagedAttnOnline is 8.1x slower per call", section "Where to look").
+ *
+ *  k_new, v_new  [B, Hkv, D]        bf16, stride[2] == 1, 16-byte aligned rows.
+ *  k_cache, v_cache [NP, P, Hkv, D] bf16 NHD pools, as in pa_decode; written.
+ *  block_tables  [B, MaxBlk] int32; context_lens [B] int32 -- lengths that
+ *                already count the new token.
+ *  num_kv_heads, head_dim, page_size must equal the shapes; head_dim is any
+ *                multiple of 8.
+ *
+ * For each b with L = context_lens[b] >= 1 and t = L - 1, the rows
+ * k_new[b][g][:] and v_new[b][g][:] of every KV head g are written to
+ * k_cache / v_cache[block_tables[b][t / P]][t % P][g][:].  L <= 0 writes
+ * nothing.  Device-side preconditions, not checked on the host: L <= MaxBlk * P
+ * and that page id in [0, NP); a sequence that violates them writes nothing.
+ * Sequences whose newest tokens share a slot race (one of them wins).
+ * Asynchronous on the stream; returns PA_OK or an error code.
+ */
+int pa_cache_append(const pa_tensor* k_new,
+                    const pa_tensor* v_new,
+                    const pa_tensor* k_cache,
+                    const pa_tensor* v_cache,
+                    const pa_tensor* block_tables,
+                    const pa_tensor* context_lens,
+                    int num_kv_heads,
+                    int head_dim,
+                    int page_size,
+                    void* stream);
+
 /* ---------------------------------------------------------------- options */
 #define PA_VARIANT_AUTO  0   /* the library picks                              */
 #define PA_VARIANT_VALU  1   /* vector-ALU kernel (any supported qg)            */
@@ -223,6 +256,7 @@ typedef struct pa_stats {
     uint64_t last_variant;          /* PA_VARIANT_* of the last call           */
     uint64_t balanced_calls;        /* calls run on the balanced schedule      */
     uint64_t last_schedule;         /* PA_SCHEDULE_* of the last call          */
+    uint64_t append_launches;       /* pa_cache_append kernel launches         */
 } pa_stats;
 
 int  pa_get_stats(pa_stats* stats);   /* PA_EINVAL if stats is NULL            */

@@ -39,7 +39,7 @@ class PaStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
         "last_partition_tokens", "last_num_partitions", "last_variant", "balanced_calls",
-        "last_schedule")]
+        "last_schedule", "append_launches")]
 
 
 class PaError(RuntimeError):
@@ -80,10 +80,26 @@ def _load() -> ctypes.CDLL:
     lib.pa_release.restype = ctypes.c_int
     lib.pa_version.argtypes = []
     lib.pa_version.restype = ctypes.c_char_p
+    T = ctypes.POINTER(PaTensor)
+    lib.pa_cache_append.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.pa_cache_append.restype = ctypes.c_int
     return lib
 
 
-LIB = _load()
+class _Library:
+    """The shared library, loaded on first use: importing the package (for
+    instance to build the library) does not need it, and every call through
+    the binding fails loudly with ImportError if it is missing or stale."""
+    _lib = None
+
+    def __getattr__(self, name):
+        if _Library._lib is None:
+            _Library._lib = _load()
+        return getattr(_Library._lib, name)
+
+
+LIB = _Library()
 
 
 def strerror(code: int) -> str:
@@ -162,6 +178,26 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_head
                            _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
     return out
+
+
+def pa_cache_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
+                    head_dim, page_size, stream=None):
+    """C ``pa_cache_append``: write each sequence's newest token (position
+    context_lens[b] - 1) into its page slot of the K and V pools."""
+    import torch
+    _require_device(k_new, v_new, k_cache, v_cache, block_tables, context_lens)
+    with torch.cuda.device(k_new.device):
+        rc = LIB.pa_cache_append(tensor_desc(k_new), tensor_desc(v_new), tensor_desc(k_cache),
+                                 tensor_desc(v_cache), tensor_desc(block_tables),
+                                 tensor_desc(context_lens), num_kv_heads, head_dim, page_size,
+                                 _stream_handle(stream, k_new.device))
+    _check(rc, "pa_cache_append")
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, stream=None):
+    """KV-cache append on torch tensors; sizes come from the shapes."""
+    NP, P, Hkv, D = k_cache.shape
+    pa_cache_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, Hkv, D, P, stream)
 
 
 def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -35,7 +35,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 struct Counters {
-    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0}, lean{0};
+    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0}, lean{0}, append{0};
     std::atomic<uint64_t> last_t{0}, last_np{0}, last_variant{0}, last_schedule{0};
 } g_stats;
 
@@ -431,9 +431,94 @@ int decode_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, cons
     }
 }
 
+int validate_append(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* k, const pa_tensor* v,
+                    const pa_tensor* bt, const pa_tensor* ctx, int num_kv_heads, int head_dim,
+                    int page_size) {
+    int rc;
+    if ((rc = check_tensor(kn, "k_new", PA_DTYPE_BF16, 3))) return rc;
+    if ((rc = check_tensor(vn, "v_new", PA_DTYPE_BF16, 3))) return rc;
+    if ((rc = check_tensor(k, "k_cache", PA_DTYPE_BF16, 4))) return rc;
+    if ((rc = check_tensor(v, "v_cache", PA_DTYPE_BF16, 4))) return rc;
+    if ((rc = check_tensor(bt, "block_tables", PA_DTYPE_INT32, 2))) return rc;
+    if ((rc = check_tensor(ctx, "context_lens", PA_DTYPE_INT32, 1))) return rc;
+    if (page_size < 1) return fail(PA_EINVAL, "page_size %d < 1", page_size);
+    if (num_kv_heads < 1) return fail(PA_EINVAL, "num_kv_heads must be >= 1");
+    if (head_dim < 8 || head_dim % 8) return fail(PA_ENOTSUP, "head_dim %d is not a multiple of 8", head_dim);
+    const int64_t B = kn->shape[0];
+    for (int i = 0; i < 3; ++i)
+        if (vn->shape[i] != kn->shape[i]) return fail(PA_EINVAL, "k_new and v_new shapes differ");
+    if (kn->shape[1] != num_kv_heads || kn->shape[2] != head_dim)
+        return fail(PA_EINVAL, "k_new shape does not match Hkv=%d, D=%d", num_kv_heads, head_dim);
+    for (int i = 0; i < 4; ++i)
+        if (k->shape[i] != v->shape[i]) return fail(PA_EINVAL, "k_cache and v_cache shapes differ");
+    if (k->shape[1] != page_size || k->shape[2] != num_kv_heads || k->shape[3] != head_dim)
+        return fail(PA_EINVAL, "k_cache shape does not match P=%d, Hkv=%d, D=%d", page_size, num_kv_heads,
+                    head_dim);
+    if (bt->shape[0] != B) return fail(PA_EINVAL, "block_tables has %lld rows, batch is %lld",
+                                       (long long)bt->shape[0], (long long)B);
+    if (ctx->shape[0] != B) return fail(PA_EINVAL, "context_lens has %lld entries, batch is %lld",
+                                        (long long)ctx->shape[0], (long long)B);
+    if (B > INT32_MAX) return fail(PA_ENOTSUP, "batch too large");
+    if (bt->shape[1] > (int64_t)1 << 24 || (int64_t)bt->shape[1] * page_size > INT32_MAX / 2)
+        return fail(PA_ENOTSUP, "block table too wide");
+    if (k->shape[0] > INT32_MAX) return fail(PA_ENOTSUP, "pool too large");
+    if ((int64_t)num_kv_heads * head_dim / 8 > (1 << 20)) return fail(PA_ENOTSUP, "rows too wide");
+    if ((rc = check_rows16(kn, "k_new", 2))) return rc;
+    if ((rc = check_rows16(vn, "v_new", 2))) return rc;
+    if ((rc = check_rows16(k, "k_cache", 3))) return rc;
+    if ((rc = check_rows16(v, "v_cache", 3))) return rc;
+    if ((reinterpret_cast<uintptr_t>(bt->data) & 3u) || (reinterpret_cast<uintptr_t>(ctx->data) & 3u))
+        return fail(PA_EALIGN, "block_tables / context_lens not 4-byte aligned");
+    if (bt->shape[0] > 1 && bt->shape[1] > 0 && bt->stride[1] != 1)
+        return fail(PA_EINVAL, "block_tables: innermost stride must be 1");
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int pa_cache_append(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* k_cache,
+                    const pa_tensor* v_cache, const pa_tensor* block_tables,
+                    const pa_tensor* context_lens, int num_kv_heads, int head_dim, int page_size,
+                    void* stream) {
+    t_err.clear();
+    int rc = validate_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
+                             head_dim, page_size);
+    if (rc) return rc;
+    if (k_new->shape[0] == 0) return PA_OK;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(PA_ENODEV, "no HIP device");
+    pa::AppendParams a{};
+    a.k_new = static_cast<const uint16_t*>(k_new->data);
+    a.v_new = static_cast<const uint16_t*>(v_new->data);
+    a.kn_sb = k_new->stride[0];
+    a.kn_sh = k_new->stride[1];
+    a.vn_sb = v_new->stride[0];
+    a.vn_sh = v_new->stride[1];
+    a.k = static_cast<uint16_t*>(k_cache->data);
+    a.v = static_cast<uint16_t*>(v_cache->data);
+    a.k_sp = k_cache->stride[0];
+    a.k_ss = k_cache->stride[1];
+    a.k_sh = k_cache->stride[2];
+    a.v_sp = v_cache->stride[0];
+    a.v_ss = v_cache->stride[1];
+    a.v_sh = v_cache->stride[2];
+    a.bt = static_cast<const int32_t*>(block_tables->data);
+    a.bt_sb = block_tables->stride[0];
+    a.ctx = static_cast<const int32_t*>(context_lens->data);
+    a.B = (int)k_new->shape[0];
+    a.Hkv = num_kv_heads;
+    a.D = head_dim;
+    a.P = page_size;
+    a.max_blk = (int)block_tables->shape[1];
+    a.num_pages = (int)k_cache->shape[0];
+    hipError_t e = pa::launch_append(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_EHIP, "append launch: %s", hipGetErrorString(e));
+    g_stats.append++;
+    return PA_OK;
+}
+
 
 int pa_decode(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
               const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
@@ -490,6 +575,7 @@ int pa_get_stats(pa_stats* s) {
     s->last_num_partitions = g_stats.last_np;
     s->last_variant = g_stats.last_variant;
     s->balanced_calls = g_stats.lean;
+    s->append_launches = g_stats.append;
     s->last_schedule = g_stats.last_schedule;
     return PA_OK;
 }
@@ -501,6 +587,7 @@ void pa_reset_stats(void) {
     g_stats.split = 0;
     g_stats.merge = 0;
     g_stats.lean = 0;
+    g_stats.append = 0;
     g_stats.last_schedule = 0;
     g_stats.last_t = 0;
     g_stats.last_np = 0;

@@ -30,6 +30,17 @@ struct DecodeParams {
     float scale_log2;                                       // scale * log2(e)
 };
 
+// KV-cache append: newest token of each sequence into its page slot.
+struct AppendParams {
+    const uint16_t* k_new; const uint16_t* v_new;           // [B, Hkv, D]
+    int64_t kn_sb, kn_sh, vn_sb, vn_sh;                     // their batch and head strides
+    uint16_t* k; uint16_t* v;                               // pools [NP, P, Hkv, D]
+    int64_t k_sp, k_ss, k_sh, v_sp, v_ss, v_sh;
+    const int32_t* bt; int64_t bt_sb;
+    const int32_t* ctx;
+    int B, Hkv, D, P, max_blk, num_pages;
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 // Finite "no token yet" running maximum: exp2(kEmptyMax - kEmptyMax) == 1 and
 // exp2(-inf - kEmptyMax) == 0, so empty states merge without NaNs.

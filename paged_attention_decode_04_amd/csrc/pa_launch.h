@@ -40,6 +40,9 @@ constexpr int kLeanDynMinPerWg = 256;
 // Workspace: two int counters at its start, zero between calls.
 constexpr int kLeanCounterBytes = 256;
 
+// KV-cache append (one workgroup per sequence).
+hipError_t launch_append(const AppendParams& a, hipStream_t s);
+
 // Log-sum-exp merge of split partials into bf16 output.
 hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s);
 

@@ -218,4 +218,63 @@ def test_stats_roundtrip():
     assert s["calls"] == 0 and s["valu_launches"] == 0
     assert set(s) == {"calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
                       "last_partition_tokens", "last_num_partitions", "last_variant",
-                      "balanced_calls", "last_schedule"}
+                      "balanced_calls", "last_schedule", "append_launches"}
+
+
+# ------------------------------------------------------------------ KV-cache append
+def append_args(B=3, Hkv=4, D=128, P=16, NP=8, maxblk=4):
+    kn = torch.zeros(B, Hkv, D, dtype=torch.bfloat16)
+    vn = torch.zeros(B, Hkv, D, dtype=torch.bfloat16)
+    k = torch.zeros(NP, P, Hkv, D, dtype=torch.bfloat16)
+    v = torch.zeros(NP, P, Hkv, D, dtype=torch.bfloat16)
+    bt = torch.zeros(B, maxblk, dtype=torch.int32)
+    ctx = torch.ones(B, dtype=torch.int32)
+    return [kn, vn, k, v, bt, ctx], (Hkv, D, P)
+
+
+def call_append(ts, dims):
+    T = _binding.tensor_desc
+    return _binding.LIB.pa_cache_append(*[T(t) if t is not None else None for t in ts], *dims, None)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda ts, d: (ts.__setitem__(0, ts[0].float()), d), pa.PA_EINVAL),
+    (lambda ts, d: (ts.__setitem__(1, torch.zeros(3, 4, 64, dtype=torch.bfloat16)), d), pa.PA_EINVAL),
+    (lambda ts, d: (ts.__setitem__(3, torch.zeros(8, 16, 4, 64, dtype=torch.bfloat16)), d), pa.PA_EINVAL),
+    (lambda ts, d: (ts.__setitem__(4, torch.zeros(2, 4, dtype=torch.int32)), d), pa.PA_EINVAL),
+    (lambda ts, d: (ts.__setitem__(5, torch.ones(2, dtype=torch.int32)), d), pa.PA_EINVAL),
+    (lambda ts, d: (ts.__setitem__(2, None), d), pa.PA_EINVAL),
+])
+def test_append_rejects_bad_arguments(mutate, code):
+    ts, dims = append_args()
+    mutate(ts, dims)
+    assert call_append(ts, dims) == code
+    assert pa.last_error() != ""
+
+
+def test_append_geometry_and_alignment():
+    ts, dims = append_args(D=12)
+    assert call_append(ts, dims) == pa.PA_ENOTSUP        # rows must be whole 16-byte chunks
+    ts, dims = append_args()
+    big = torch.zeros(3 * 4 * 128 + 1, dtype=torch.bfloat16)
+    ts[0] = big[1:].view(3, 4, 128)
+    assert call_append(ts, dims) == pa.PA_EALIGN
+    ts, dims = append_args()
+    assert call_append(ts, (4, 128, 32)) == pa.PA_EINVAL  # page_size does not match the pool
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
+def test_valid_append_without_a_device_is_enodev():
+    ts, dims = append_args()
+    assert call_append(ts, dims) == pa.PA_ENODEV
+    ts, dims = append_args(B=0)
+    assert call_append(ts, dims) == pa.PA_OK             # nothing to write
+
+
+def test_missing_library_fails_loudly_at_first_use(monkeypatch, tmp_path):
+    """Importing the package never needs the library (so it can be built);
+    the first call through the binding raises ImportError when it is absent."""
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "libpa_decode.so"))
+    monkeypatch.setattr(_binding._Library, "_lib", None)
+    with pytest.raises(ImportError):
+        pa.version()

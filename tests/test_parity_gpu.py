@@ -446,3 +446,75 @@ def test_window_long_context_sampled(variant):
     assert_parity(yb, ref, f"long ctx W={W} sampled {len(pairs)} rows")
     del d, host
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ KV-cache append
+@pytest.mark.parametrize("D,Hkv,P", [(128, 8, 16), (256, 2, 32), (128, 4, 7), (64, 8, 1)])
+def test_append_matches_oracle_bitwise(D, Hkv, P):
+    """The whole K and V pools after the append equal the oracle's, bit for
+    bit: the newest token's rows land in their slots and nothing else moves.
+    k_new is a strided view (padded head stride)."""
+    lens = (0, 1, P, P + 1, 3 * P + 2, 100)
+    w = custom(batch=len(lens), num_q_heads=2 * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=P,
+               ctx=lens)
+    inp = make_inputs(w, seed=D + P)
+    rng = np.random.default_rng(D * P)
+    B = len(lens)
+    k_new = workloads.round_bf16(rng.standard_normal((B, Hkv, D)).astype(np.float32))
+    v_new = workloads.round_bf16(rng.standard_normal((B, Hkv, D)).astype(np.float32))
+    k_ref, v_ref = oracle.cache_append(inp.k[0], inp.v[0], inp.block_tables, inp.context_lens,
+                                       k_new, v_new)
+    d = to_device(inp)
+    k, v = d.k[0].clone(), d.v[0].clone()
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    kn_pad = torch.zeros((B, Hkv, D + 64), dtype=torch.bfloat16, device="cuda")
+    kn_pad[..., :D] = dev(k_new)
+    pa.pa_reset_stats()
+    pa.cache_append(kn_pad[..., :D], dev(v_new), k, v, d.block_tables, d.context_lens)
+    torch.cuda.synchronize()
+    assert pa.pa_get_stats()["append_launches"] == 1
+    assert np.array_equal(bits(k).reshape(k_ref.shape), k_ref)
+    assert np.array_equal(bits(v).reshape(v_ref.shape), v_ref)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_append_then_decode(variant):
+    """A decode step: append the newest token, then attend; equals the
+    oracle's append followed by the oracle's attention."""
+    w = custom(batch=5, num_q_heads=16, num_kv_heads=8, head_dim=128, page_size=16,
+               ctx=(1, 16, 17, 300, 1000))
+    inp = make_inputs(w, seed=71)
+    rng = np.random.default_rng(71)
+    k_new = workloads.round_bf16(rng.standard_normal((5, 8, 128)).astype(np.float32))
+    v_new = workloads.round_bf16(rng.standard_normal((5, 8, 128)).astype(np.float32))
+    k_ref, v_ref = oracle.cache_append(inp.k[0], inp.v[0], inp.block_tables, inp.context_lens,
+                                       k_new, v_new)
+    ref = oracle.attention(inp.q[0], k_ref, v_ref, inp.block_tables, inp.context_lens,
+                           inp.w.scale, inp.w.num_kv_heads)
+    d = to_device(inp)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    pa.cache_append(dev(k_new), dev(v_new), d.k[0], d.v[0], d.block_tables, d.context_lens)
+    y, _ = gpu_run(d, variant=variant)
+    assert_parity(y, ref, f"append + decode {variant}")
+
+
+def test_append_skips_sequences_it_cannot_place():
+    """A newest token whose block-table entry is out of the pool, or whose
+    length exceeds the table, writes nothing; the other sequences are written."""
+    w = custom(batch=3, num_q_heads=8, num_kv_heads=4, head_dim=128, page_size=16, ctx=(5, 20, 9))
+    inp = make_inputs(w, seed=72)
+    d = to_device(inp)
+    bt = d.block_tables.clone()
+    bt[1, 1] = -1                                  # sequence 1's newest page: not a page
+    ctx = d.context_lens.clone()
+    ctx[2] = 16 * bt.shape[1] + 1                  # sequence 2: past its table
+    k, v = d.k[0].clone(), d.v[0].clone()
+    k0, v0 = bits(k), bits(v)
+    kn = torch.ones((3, 4, 128), dtype=torch.bfloat16, device="cuda")
+    pa.cache_append(kn, kn, k, v, bt, ctx)
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.cache_append(inp.k[0], inp.v[0], inp.block_tables[:1], inp.context_lens[:1],
+                                       bits(kn)[:1].reshape(1, 4, 128), bits(kn)[:1].reshape(1, 4, 128))
+    assert np.array_equal(bits(k).reshape(k_ref.shape), k_ref)
+    assert np.array_equal(bits(v).reshape(v_ref.shape), v_ref)
+    assert not np.array_equal(bits(k), k0)
