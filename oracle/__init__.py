@@ -71,6 +71,10 @@ def _load():
     lib.pa_oracle_f64_window.restype = i32
     lib.pa_oracle_f64_pairs_window.argtypes = common + [i64, p, i64, p, i32]
     lib.pa_oracle_f64_pairs_window.restype = i32
+    lib.pa_oracle_f64_typed.argtypes = common + [i32, i32, i64, p, i32, i32]
+    lib.pa_oracle_f64_typed.restype = i32
+    lib.pa_oracle_decode.argtypes = [p, i32, i64, p]
+    lib.pa_oracle_decode.restype = i32
     lib.pa_oracle_num_mutants.argtypes = []
     lib.pa_oracle_num_mutants.restype = i32
     _lib = lib
@@ -85,13 +89,30 @@ def default_threads() -> int:
     return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
 
 
+# Storage types: bf16 as uint16 bit patterns, IEEE binary16 as numpy float16,
+# binary32 as numpy float32 (codes shared with the C oracle).
+DTYPE_CODES = {np.dtype(np.uint16): 1, np.dtype(np.float32): 3, np.dtype(np.float16): 4}
+
+
+def dtype_code(a) -> int:
+    code = DTYPE_CODES.get(np.asarray(a).dtype)
+    if code is None:
+        raise OracleError(f"unsupported element type {np.asarray(a).dtype} "
+                          "(uint16 = bf16 bits, float16, float32)")
+    return code
+
+
 def _prep(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads):
     q = np.asarray(q)
-    if q.dtype != np.uint16 or q.ndim != 3 or q.strides[2] != 2:
-        raise OracleError("q must be uint16 bf16 bits [B, Hq, D] with contiguous D")
+    dtype_code(q)
+    if q.ndim != 3 or q.strides[2] != q.itemsize:
+        raise OracleError("q must be [B, Hq, D] with contiguous D")
+    dtype_code(k_cache)
     for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
-        if c.dtype != np.uint16 or c.ndim != 4 or c.strides[3] != 2:
-            raise OracleError(f"{name} must be uint16 bf16 bits [NP, P, Hkv, D], D contiguous")
+        if c.ndim != 4 or c.strides[3] != c.itemsize:
+            raise OracleError(f"{name} must be [NP, P, Hkv, D], D contiguous")
+    if k_cache.dtype != v_cache.dtype:
+        raise OracleError("k_cache and v_cache must share their element type")
     if k_cache.shape != v_cache.shape or k_cache.strides != v_cache.strides:
         raise OracleError("k_cache and v_cache must share shape and strides")
     B, Hq, D = q.shape
@@ -102,8 +123,8 @@ def _prep(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads):
     ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
     if bt.ndim != 2 or bt.shape[0] != B or ctx.shape != (B,):
         raise OracleError("block_tables must be [B, MaxBlk] and context_lens [B]")
-    st = [s // 2 for s in k_cache.strides[:3]]
-    qst = [s // 2 for s in q.strides[:2]]
+    st = [s // k_cache.itemsize for s in k_cache.strides[:3]]
+    qst = [s // q.itemsize for s in q.strides[:2]]
     return q, bt, ctx, (B, Hq, D, NP, P, Hkv), st, qst
 
 
@@ -124,7 +145,10 @@ def attention(q, k_cache, v_cache, block_tables, context_lens, scale,
     n = threads or default_threads()
     args = [_ptr(q), qst[0], qst[1], _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], NP,
             _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale)]
-    if window:
+    qt, kt = dtype_code(q), dtype_code(k_cache)
+    if qt != 1 or kt != 1:
+        rc = lib.pa_oracle_f64_typed(*args, qt, kt, int(window), _ptr(out), n, mutant)
+    elif window:
         rc = lib.pa_oracle_f64_window(*args, int(window), _ptr(out), n, mutant)
     elif mutant:
         rc = lib.pa_oracle_f64_mutant(*args, _ptr(out), n, mutant)
@@ -151,6 +175,16 @@ def attention_pairs(q, k_cache, v_cache, block_tables, context_lens, scale,
     if rc != 0:
         raise OracleError(f"oracle returned {rc}")
     return out
+
+
+def decode_elements(a) -> np.ndarray:
+    """The oracle's fp64 reading of every element of ``a`` (for its tests)."""
+    a = np.ascontiguousarray(a)
+    out = np.zeros(a.size, dtype=np.float64)
+    rc = _load().pa_oracle_decode(_ptr(a), dtype_code(a), a.size, _ptr(out))
+    if rc != 0:
+        raise OracleError(f"oracle returned {rc}")
+    return out.reshape(a.shape)
 
 
 def num_mutants() -> int:

@@ -29,6 +29,15 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def widen(a) -> np.ndarray:
+    """Exact fp64 values of an array: uint16 holds bf16 bit patterns, numpy
+    float16 / float32 widen with numpy's own conversion."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
 def _dense_kv(pool, bt_row, L, P):
     n = -(-L // P)
     pages = pool[np.asarray(bt_row[:n], dtype=np.int64)]   # [n, P, Hkv, D]
@@ -38,9 +47,9 @@ def _dense_kv(pool, bt_row, L, P):
 def dense(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, window=0):
     """[B, Hq, D] fp64 via dense per-sequence K/V and a library softmax.
     ``window`` > 0 keeps only the last ``window`` rows of each sequence."""
-    qf = bf16_bits_to_f64(q)
-    kf = bf16_bits_to_f64(k_cache)
-    vf = bf16_bits_to_f64(v_cache)
+    qf = widen(q)
+    kf = widen(k_cache)
+    vf = widen(v_cache)
     B, Hq, D = qf.shape
     P = kf.shape[1]
     qg = Hq // num_kv_heads

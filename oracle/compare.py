@@ -1,4 +1,4 @@
-"""Comparator for bf16 outputs against an fp64 (or bf16) reference.
+"""Comparator for bf16 / fp16 / fp32 outputs against an fp64 reference.
 
 Test infrastructure.  Reports, over one whole output tensor:
 
@@ -7,10 +7,10 @@ Test infrastructure.  Reports, over one whole output tensor:
                  "head_dim=128 decode arm", section "Correctness"; the pages do
                  not define NMSE, this is the plain reading);
 * ``max_abs``  = max |y - r|;
-* ``bitwise``  = percentage of elements whose bf16 bits equal the reference
-                 rounded to bf16 (round to nearest, ties to even);
-* ``n_big``    = count of |r| >= 4, where the bf16 half-ULP (2^-6 = 0.0156)
-                 alone exceeds a 1e-2 max-abs bound;
+* ``bitwise``  = percentage of elements whose bits equal the reference
+                 rounded to the output type (round to nearest, ties to even);
+* ``n_big``    = count of |r| where the output type's half-ULP alone exceeds a
+                 1e-2 max-abs bound (bf16: |r| >= 4; fp16: |r| >= 32);
 * ``worst``    = flat index of the largest |y - r|.
 
 ``self_test`` repeats the pages' comparator self-test (page 3, PR
@@ -65,23 +65,42 @@ class Report:
                 f"bitwise={self.bitwise:.4f}% n_big={self.n_big} worst={self.worst} n={self.n}")
 
 
+# |r| at and above which the half-ULP of the output type alone exceeds the
+# 1e-2 max-abs bound: bf16 (2^-9 relative) from 4, binary16 (2^-11) from 32.
+_BIG = {"bf16": 4.0, "f16": 32.0, "f32": float("inf")}
+
+
 def compare(y_bits, ref) -> Report:
-    """``y_bits``: bf16 bits of the output under test.  ``ref``: fp64 values,
-    or bf16 bits (uint16) of another bf16 output."""
-    y_bits = np.asarray(y_bits, dtype=np.uint16).ravel()
+    """``y_bits``: the output under test -- bf16 bit patterns (uint16), or a
+    numpy float16 / float32 array.  ``ref``: fp64 values, or an output of the
+    same kind.  ``bitwise`` compares with the reference rounded to the
+    output's type (round to nearest, ties to even; numpy's own conversion for
+    float16 / float32)."""
+    y_arr = np.asarray(y_bits)
+    kind = {np.dtype(np.float16): "f16", np.dtype(np.float32): "f32"}.get(y_arr.dtype, "bf16")
     ref = np.asarray(ref)
-    if ref.dtype == np.uint16:
-        r_bits = ref.ravel()
-        r = bf16_bits_to_f64(r_bits)
+    if kind == "bf16":
+        y_bits = np.asarray(y_arr, dtype=np.uint16).ravel()
+        if ref.dtype == np.uint16:
+            r_bits = ref.ravel()
+            r = bf16_bits_to_f64(r_bits)
+        else:
+            r = ref.astype(np.float64).ravel()
+            r_bits = f64_to_bf16_bits(r)
+        y = bf16_bits_to_f64(y_bits)
     else:
+        y_bits = y_arr.ravel()
+        y = y_bits.astype(np.float64)
         r = ref.astype(np.float64).ravel()
-        r_bits = f64_to_bf16_bits(r)
-    if r.shape != y_bits.shape:
-        raise ValueError(f"shape mismatch {y_bits.shape} vs {r.shape}")
-    y = bf16_bits_to_f64(y_bits)
+        r_bits = r.astype(y_arr.dtype)
+        uint = np.uint16 if kind == "f16" else np.uint32
+        y_bits, r_bits = y_bits.view(uint), r_bits.view(uint)
+    if r.shape != y.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {r.shape}")
     n = y.size
     if n == 0:
         return Report(0.0, 0.0, 100.0, 0, -1, 0)
+    big = int(np.sum(np.abs(r) >= _BIG[kind]))
     d = y - r
     den = float(np.sum(r * r))
     num = float(np.sum(d * d))
@@ -89,11 +108,9 @@ def compare(y_bits, ref) -> Report:
     ad = np.abs(d)
     if not np.all(np.isfinite(ad)):
         worst = int(np.argmax(~np.isfinite(ad)))
-        return Report(float("inf"), float("inf"), float(np.mean(y_bits == r_bits) * 100),
-                      int(np.sum(np.abs(r) >= 4)), worst, n)
+        return Report(float("inf"), float("inf"), float(np.mean(y_bits == r_bits) * 100), big, worst, n)
     worst = int(np.argmax(ad))
-    return Report(nmse, float(ad[worst]), float(np.mean(y_bits == r_bits) * 100.0),
-                  int(np.sum(np.abs(r) >= 4.0)), worst, n)
+    return Report(nmse, float(ad[worst]), float(np.mean(y_bits == r_bits) * 100.0), big, worst, n)
 
 
 def bump_ulp(bits, offsets, ulps: int = 1) -> np.ndarray:

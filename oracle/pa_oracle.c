@@ -36,8 +36,10 @@
  * in ascending t and ascending i inside one (b, h) pair, so the result does
  * not depend on the number of threads.
  *
- * Every input is read as exact bf16 bits widened to fp64.  Block-table
- * entries of used pages are range-checked; bad input returns an error code.
+ * Every input is read as the exact value of its storage type widened to
+ * fp64: bf16, IEEE binary16 or binary32 (element types of Q and of the K/V
+ * pools are given separately).  Block-table entries of used pages are
+ * range-checked; bad input returns an error code.
  *
  * The "mutant" argument exists only so that a test can plant a known mistake
  * in the oracle and show that the pins catch it.  0 is the definition.
@@ -53,11 +55,16 @@
 #define ORC_EPAGE -2
 #define ORC_ENOMEM -3
 
+#define ORC_BF16 1
+#define ORC_F32 3
+#define ORC_F16 4
+
 typedef struct {
-    const uint16_t* q;
+    const void* q;
     int64_t q_sb, q_sh;                 /* element strides of q [B][Hq][D]   */
-    const uint16_t* k;
-    const uint16_t* v;
+    const void* k;
+    const void* v;
+    int q_dtype, kv_dtype;              /* ORC_BF16 / ORC_F16 / ORC_F32      */
     int64_t s_page, s_slot, s_head;     /* element strides of the NHD pools  */
     int64_t num_pages;
     const int32_t* bt;
@@ -88,6 +95,25 @@ static double bf16_bits_to_f64(uint16_t bits)
     return (double)f;
 }
 
+/* IEEE 754 binary16: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+static double f16_bits_to_f64(uint16_t h)
+{
+    int e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);                  /* zero, subnormal */
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + m), e - 25);             /* (1 + m/2^10) 2^(e-15) */
+    return (h & 0x8000) ? -v : v;
+}
+
+/* Element idx of an array of the given storage type, widened exactly. */
+static double elem(const void* base, int64_t idx, int dtype)
+{
+    if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+    if (dtype == ORC_F16) return f16_bits_to_f64(((const uint16_t*)base)[idx]);
+    return bf16_bits_to_f64(((const uint16_t*)base)[idx]);
+}
+
 /* One output row o[b][h][0..D) following the definition above. */
 static int attend_row(const orc_args* a, int b, int h, double* o)
 {
@@ -105,26 +131,27 @@ static int attend_row(const orc_args* a, int b, int h, double* o)
     int64_t t0 = (a->window > 0 && L > a->window) ? L - a->window : 0;
     if (a->mutant == 9 && a->window > 0 && L > a->window) t0 += 1;   /* window one short */
 
-    const uint16_t* qrow = a->q + (int64_t)b * a->q_sb + (int64_t)h * a->q_sh;
+    const int64_t qoff = (int64_t)b * a->q_sb + (int64_t)h * a->q_sh;
     double* x = (double*)malloc((size_t)L * sizeof(double));
-    const uint16_t** vrows = (const uint16_t**)malloc((size_t)L * sizeof(void*));
-    if (!x || !vrows) { free(x); free(vrows); return ORC_ENOMEM; }
+    int64_t* voff = (int64_t*)malloc((size_t)L * sizeof(int64_t));
+    const void** vbase = (const void**)malloc((size_t)L * sizeof(void*));
+    if (!x || !voff || !vbase) { free(x); free(voff); free(vbase); return ORC_ENOMEM; }
 
     for (int64_t t = t0; t < L; ++t) {
         int64_t lp = t / a->P, slot = t % a->P;
         if (a->mutant == 2) slot = (t + 1) % a->P;        /* off-by-one slot */
-        if (lp >= a->max_blk) { free(x); free(vrows); return ORC_EPAGE; }
+        if (lp >= a->max_blk) { free(x); free(voff); free(vbase); return ORC_EPAGE; }
         int64_t page = a->bt[(int64_t)b * a->max_blk + lp];
         if (a->mutant == 8) page = a->bt[lp];             /* batch row lost  */
-        if (page < 0 || page >= a->num_pages) { free(x); free(vrows); return ORC_EPAGE; }
+        if (page < 0 || page >= a->num_pages) { free(x); free(voff); free(vbase); return ORC_EPAGE; }
         int64_t off = page * a->s_page + slot * a->s_slot + (int64_t)g * a->s_head;
-        const uint16_t* krow = a->k + off;
-        vrows[t] = a->v + off;
-        if (a->mutant == 5) vrows[t] = a->k + off; /* K used in place of V    */
+        voff[t] = off;
+        vbase[t] = a->v;
+        if (a->mutant == 5) vbase[t] = a->k;               /* K used in place of V */
         double dot = 0.0;
         for (int i = 0; i < D; ++i) {
-            double qi = bf16_bits_to_f64(qrow[i]);
-            double ki = bf16_bits_to_f64(krow[i]);
+            double qi = elem(a->q, qoff + i, a->q_dtype);
+            double ki = elem(a->k, off + i, a->kv_dtype);
             if (a->mutant == 6 && i == D - 1) ki = 0.0;   /* dropped term    */
             dot += qi * ki;
         }
@@ -142,14 +169,13 @@ static int attend_row(const orc_args* a, int b, int h, double* o)
     }
     int64_t t_end = L;
     if (a->mutant == 7) t_end = L - 1;                    /* last token lost */
-    for (int64_t t = t0; t < t_end; ++t) {
-        const uint16_t* vrow = vrows[t];
-        for (int i = 0; i < D; ++i) o[i] += x[t] * bf16_bits_to_f64(vrow[i]);
-    }
+    for (int64_t t = t0; t < t_end; ++t)
+        for (int i = 0; i < D; ++i) o[i] += x[t] * elem(vbase[t], voff[t] + i, a->kv_dtype);
     for (int i = 0; i < D; ++i) o[i] /= Z;
 
     free(x);
-    free(vrows);
+    free(voff);
+    free(vbase);
     return ORC_OK;
 }
 
@@ -207,13 +233,15 @@ static int run(orc_args* a, int n_threads)
 }
 
 static void fill(orc_args* a,
-                 const uint16_t* q, int64_t q_sb, int64_t q_sh,
-                 const uint16_t* k, const uint16_t* v,
+                 const void* q, int64_t q_sb, int64_t q_sh,
+                 const void* k, const void* v,
                  int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
                  const int32_t* bt, int64_t max_blk, const int32_t* ctx,
                  int B, int Hq, int Hkv, int D, int P, float scale)
 {
     memset(a, 0, sizeof *a);
+    a->q_dtype = ORC_BF16;
+    a->kv_dtype = ORC_BF16;
     a->q = q; a->q_sb = q_sb; a->q_sh = q_sh;
     a->k = k; a->v = v;
     a->s_page = s_page; a->s_slot = s_slot; a->s_head = s_head;
@@ -274,6 +302,41 @@ int pa_oracle_f64_window(const uint16_t* q, int64_t q_sb, int64_t q_sh,
     a.window = window;
     a.mutant = mutant;
     return run(&a, n_threads);
+}
+
+/* Every (b, h) row, with element types for Q and for the K/V pools
+ * (ORC_BF16 = 1, ORC_F32 = 3, ORC_F16 = 4), a sliding window (0 = none) and
+ * an optional planted mistake (0 = none). */
+int pa_oracle_f64_typed(const void* q, int64_t q_sb, int64_t q_sh,
+                        const void* k, const void* v,
+                        int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                        const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                        int B, int Hq, int Hkv, int D, int P, float scale,
+                        int q_dtype, int kv_dtype, int64_t window, double* out, int n_threads, int mutant)
+{
+    orc_args a;
+    if (window < 0) return ORC_EINVAL;
+    for (int i = 0; i < 2; ++i) {
+        int t = i ? kv_dtype : q_dtype;
+        if (t != ORC_BF16 && t != ORC_F16 && t != ORC_F32) return ORC_EINVAL;
+    }
+    fill(&a, q, q_sb, q_sh, k, v, s_page, s_slot, s_head, num_pages, bt, max_blk, ctx,
+         B, Hq, Hkv, D, P, scale);
+    a.q_dtype = q_dtype;
+    a.kv_dtype = kv_dtype;
+    a.out = out;
+    a.n_items = (int64_t)B * Hq;
+    a.window = window;
+    a.mutant = mutant;
+    return run(&a, n_threads);
+}
+
+/* Decodes of one element type over n bit patterns (tests of the decoder). */
+int pa_oracle_decode(const void* bits, int dtype, int64_t n, double* out)
+{
+    if (dtype != ORC_BF16 && dtype != ORC_F16 && dtype != ORC_F32) return ORC_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = elem(bits, i, dtype);
+    return ORC_OK;
 }
 
 /* Selected rows with a sliding window (see above). */

@@ -19,6 +19,11 @@ Each pin follows something the source pages or plain mathematics fix:
 * every planted mistake in the oracle (wrong head map, off-by-one slot, lost
   scale, flipped sign, K read for V, dropped term, lost token, lost batch
   row, window one token short) is caught by the brute-force pin;
+* element types (the fp16/fp32 variants the pages list as owed -- page 2,
+  "Not claimed", the dtype gap): the oracle's binary16 decoding equals
+  numpy's on all 65536 bit patterns, bf16 equals the bit-shift widening,
+  fp16 / fp32 / mixed inputs match the dense brute force, and the same values
+  stored as bf16, fp16 or fp32 give bit-identical results;
 * KV-cache append writes exactly the newest token's K/V rows: every other
   byte is unchanged, the rows read back through the block table, and
   appending into a fresh one-token sequence makes attention return v_new;
@@ -327,6 +332,62 @@ def test_window_equals_truncated_sequence(W, P):
 
 
 # --------------------------------------------------------------------------
+# element types
+# --------------------------------------------------------------------------
+def test_binary16_decoding_matches_numpy_on_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode_elements(bits.view(np.float16))
+    want = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))   # -0.0 stays -0.0
+
+
+def test_bf16_and_f32_decoding():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode_elements(bits)
+    want = brute.bf16_bits_to_f64(bits)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(want)], want[~np.isnan(want)])
+    f = np.array([0.0, -0.0, 1.0, -2.5, 3.4028235e38, 1.4e-45, np.inf, -np.inf, 0.1], dtype=np.float32)
+    assert np.array_equal(oracle.decode_elements(f), f.astype(np.float64))
+
+
+def retype(c, q_dtype, kv_dtype, rng):
+    """The case with fresh N(0,1) values stored in the given types."""
+    def draw(shape, dt):
+        x = rng.standard_normal(shape).astype(np.float32)
+        return round_bf16(x) if dt == "bf16" else x.astype(np.float16 if dt == "f16" else np.float32)
+    return dict(c, q=draw(c["q"].shape, q_dtype), k_cache=draw(c["k_cache"].shape, kv_dtype),
+                v_cache=draw(c["v_cache"].shape, kv_dtype))
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", [("f16", "f16"), ("f32", "f32"), ("f32", "bf16"),
+                                              ("f32", "f16"), ("bf16", "f16")])
+def test_typed_inputs_match_dense_bruteforce(q_dtype, kv_dtype):
+    rng = np.random.default_rng(80)
+    c = retype(random_case(rng, 3, 8, 2, 64, 4, [1, 9, 30]), q_dtype, kv_dtype, rng)
+    assert rel_err(run_oracle(c), run_dense(c)) <= 1e-12
+    assert rel_err(run_oracle(c, window=5), run_dense(c, 5)) <= 1e-12
+
+
+def test_same_values_in_every_storage_type_give_identical_bits():
+    """bf16 values are exact in fp32, and (away from fp16's underflow range,
+    here a scaled grid of small integers) in fp16: the oracle reads the same
+    numbers whatever the storage, so the results agree bit for bit."""
+    rng = np.random.default_rng(81)
+    c = random_case(rng, 3, 8, 2, 32, 4, [2, 9, 30])
+    def grid(shape):                       # multiples of 1/64 in [-4, 4]: exact everywhere
+        return (rng.integers(-256, 257, shape) / 64.0).astype(np.float32)
+    vals = {k: grid(c[k].shape) for k in ("q", "k_cache", "v_cache")}
+    ref = run_oracle(dict(c, **{k: round_bf16(v) for k, v in vals.items()}))
+    for dt in (np.float16, np.float32):
+        out = run_oracle(dict(c, **{k: v.astype(dt) for k, v in vals.items()}))
+        assert np.array_equal(out, ref)
+
+
+# --------------------------------------------------------------------------
 # KV-cache append
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("P", [1, 7, 16])
@@ -413,6 +474,27 @@ def test_comparator_selftest_matches_pages():
     assert bad.worst in g["offsets"]
     gross = compare.compare(round_bf16(rng.standard_normal(2048).astype(np.float32)), ref)
     assert not gross.ok()
+
+
+def test_comparator_on_fp16_and_fp32_outputs():
+    """The pages' self-test shape on binary16 and binary32 outputs: exact
+    copies are 100% bitwise, three 1-ULP changes in 2048 give 99.8535%."""
+    from oracle.compare import compare
+    rng = np.random.default_rng(90)
+    ref = rng.standard_normal(2048)
+    for dt, ui in ((np.float16, np.uint16), (np.float32, np.uint32)):
+        y = ref.astype(dt)
+        r = compare(y, ref)
+        assert r.bitwise == 100.0 and r.ok()
+        bad = y.copy().view(ui)
+        for o in (5, 1024, 2047):
+            bad[o] += 1
+        r = compare(bad.view(dt), ref)
+        assert abs(r.bitwise - 2045 / 2048 * 100) < 1e-9
+        assert r.ok()
+        gross = y.copy()
+        gross[:100] *= -1
+        assert not compare(gross, ref).ok()
 
 
 def test_bf16_rounding_helpers_agree_with_torch():

@@ -1,6 +1,6 @@
 """Seeded synthetic inputs for decode paged attention.
 
-This module holds random draws, the bf16 rounding of those draws and the
+This module holds random draws, their rounding to a storage type and the
 construction of block tables -- nothing of the attention arithmetic.  The
 oracle tests, the GPU parity tests and the benchmark all take their inputs
 from here, so both sides see the same bytes.
@@ -32,8 +32,9 @@ Recipe (NumPy PCG64 ``default_rng(seed)``, draws in this order):
    sequences' pages interleave at random across the pool;
 3. Q ``[n_q, B, Hq, D]`` (n_q = layers x tokens), then for each layer the K
    values and then the V values of the *used* pages, in logical order
-   (sequence-major), each ``standard_normal`` fp32 rounded to bf16 (nearest,
-   ties to even).  Unused pool pages hold zeros (NaN in poison mode);
+   (sequence-major), each ``standard_normal`` fp32 rounded to the storage type
+   (bf16 by default, or fp16 / kept fp32; nearest, ties to even).  Unused
+   pool pages hold zeros (NaN in poison mode);
 4. ``hd256_gqa4`` only: ``rng.random(sum L) < 0.01`` over logical tokens marks
    the tokens whose K rows (every KV head) are multiplied by 4 (exact in bf16).
 
@@ -201,47 +202,68 @@ class Inputs:
         return self.q[i], self.k[layer], self.v[layer]
 
 
-def poison(w: Workload, lay: Layout, k: np.ndarray, v: np.ndarray) -> None:
-    """Overwrite everything a correct kernel must not read with bf16 NaN."""
+def poison(w: Workload, lay: Layout, k: np.ndarray, v: np.ndarray, dtype: str = "bf16") -> None:
+    """Overwrite everything a correct kernel must not read with NaN."""
+    nan = _NAN[dtype]
     used = np.zeros(lay.num_pages, dtype=bool)
     used[lay.used_pages] = True
-    k[:, ~used] = BF16_NAN
-    v[:, ~used] = BF16_NAN
+    k[:, ~used] = nan
+    v[:, ~used] = nan
     P = w.page_size
     for b in range(w.batch):
         L = int(lay.context_lens[b])
         if L % P:
             last = lay.block_tables[b, (L - 1) // P]
-            k[:, last, L % P:] = BF16_NAN
-            v[:, last, L % P:] = BF16_NAN
+            k[:, last, L % P:] = nan
+            v[:, last, L % P:] = nan
 
 
-def make_inputs(w: Workload | str, seed: int = 0, poison_unused: bool = False) -> Inputs:
-    """Host (NumPy) inputs following the recipe in the module docstring."""
+# Storage types of generated tensors: bf16 as uint16 bit patterns, fp16 and
+# fp32 as numpy float16 / float32.
+STORAGE = {"bf16": np.uint16, "f16": np.float16, "f32": np.float32}
+_NAN = {"bf16": BF16_NAN, "f16": np.float16(np.nan), "f32": np.float32(np.nan)}
+
+
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 draws stored as ``dtype`` (round to nearest even)."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    return x.astype(STORAGE[dtype])
+
+
+def make_inputs(w: Workload | str, seed: int = 0, poison_unused: bool = False,
+                dtype: str = "bf16", q_dtype: str | None = None) -> Inputs:
+    """Host (NumPy) inputs following the recipe in the module docstring.
+    ``dtype`` is the storage type of K and V (and of Q unless ``q_dtype``
+    says otherwise); the draws are the same fp32 values whatever the type."""
     if isinstance(w, str):
         w = WORKLOADS[w]
+    q_dtype = q_dtype or dtype
     rng = np.random.default_rng(seed)
     lay = make_layout(w, rng)
     B, Hq, Hkv, D, P = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
-    q = round_bf16(rng.standard_normal((w.calls, B, Hq, D), dtype=np.float32))
+    q = encode(rng.standard_normal((w.calls, B, Hq, D), dtype=np.float32), q_dtype)
     n_used = lay.used_pages.size
-    k = np.zeros((w.layers, lay.num_pages, P, Hkv, D), dtype=np.uint16)
+    k = np.zeros((w.layers, lay.num_pages, P, Hkv, D), dtype=STORAGE[dtype])
     v = np.zeros_like(k)
     for layer in range(w.layers):
-        k[layer, lay.used_pages] = round_bf16(
-            rng.standard_normal((n_used, P, Hkv, D), dtype=np.float32))
-        v[layer, lay.used_pages] = round_bf16(
-            rng.standard_normal((n_used, P, Hkv, D), dtype=np.float32))
+        xk = rng.standard_normal((n_used, P, Hkv, D), dtype=np.float32)
+        xv = rng.standard_normal((n_used, P, Hkv, D), dtype=np.float32)
+        k[layer, lay.used_pages] = encode(xk, dtype)
+        v[layer, lay.used_pages] = encode(xv, dtype)
     spikes = _spikes(w, lay, rng)
     lay.spike_tokens = spikes
     if spikes.any():
         pg, sl = _token_slots(w, lay)
         for layer in range(w.layers):
             rows = k[layer, pg[spikes], sl[spikes]]               # [n, Hkv, D]
-            f = (rows.astype(np.uint32) << 16).view(np.float32) * np.float32(4.0)
-            k[layer, pg[spikes], sl[spikes]] = round_bf16(f)      # exact (x4)
+            if dtype == "bf16":
+                f = (rows.astype(np.uint32) << 16).view(np.float32) * np.float32(4.0)
+                k[layer, pg[spikes], sl[spikes]] = round_bf16(f)  # exact (x4)
+            else:
+                k[layer, pg[spikes], sl[spikes]] = rows * STORAGE[dtype](4.0)   # exact (x4)
     if poison_unused:
-        poison(w, lay, k, v)
+        poison(w, lay, k, v, dtype)
     return Inputs(w, q, k, v, lay)
 
 
@@ -271,7 +293,10 @@ class DeviceInputs:
 def to_device(inp: Inputs, device="cuda") -> DeviceInputs:
     import torch
     def bf(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:                    # bf16 bit patterns
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(a).to(device)       # float16 / float32
     return DeviceInputs(inp.w, bf(inp.q), bf(inp.k), bf(inp.v),
                         torch.from_numpy(inp.block_tables).to(device),
                         torch.from_numpy(inp.context_lens).to(device), inp.layout)
