@@ -157,8 +157,11 @@ def launch_info(st):
     return kernel, (merge if st["merge_launches"] else None), launch
 
 
-# Extra per-config lines: the sliding-window variant on two workloads.
-WINDOWED = (("long_ctx_gqa8", 4096), ("hd256_gqa4", 1024))
+# Extra per-config lines: (workload, window, K/V element type).  The window
+# on two workloads, an fp16 cache, an fp32 cache and head_dim 512.
+EXTRA = (("long_ctx_gqa8", 4096, "bf16"), ("hd256_gqa4", 1024, "bf16"),
+         ("long_ctx_gqa8", 0, "f16"), ("batch16", 0, "f32"), ("hd512_gqa4", 0, "bf16"))
+ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 
 
 def per_config(pa, knobs, torch, workloads_mod):
@@ -168,24 +171,22 @@ def per_config(pa, knobs, torch, workloads_mod):
     the attended tokens only."""
     import numpy as np
     res = {}
-    runs = [(name, 0) for name in workloads_mod.ORDER] + list(WINDOWED)
-    for name, window in runs:
+    runs = [(name, 0, "bf16") for name in workloads_mod.ORDER] + list(EXTRA)
+    for name, window, dt in runs:
         w = workloads_mod.WORKLOADS[name]
         if name == "long_ctx_gqa8":
-            d = workloads_mod.device_inputs(w, seed=0)
+            d = workloads_mod.device_inputs(w, seed=0, dtype=dt)
         else:
-            d = workloads_mod.to_device(workloads_mod.make_inputs(w, seed=0))
+            d = workloads_mod.to_device(workloads_mod.make_inputs(w, seed=0, dtype=dt))
         lens = d.layout.context_lens
         kn = dict(knobs, window=window)
-        if window:
-            kvb = int(np.minimum(lens.astype(np.int64), window).sum()) * w.num_kv_heads * w.head_dim * 4
-        else:
-            kvb = workloads_mod.kv_bytes(w, lens)
+        kvb = workloads_mod.kv_bytes(w, lens, window, ELEM_BYTES[dt])
         n_calls = w.calls if w.calls > 1 else 1
         calls = [make_call(pa, d, i, kn)[0] for i in range(n_calls)]
         entry = {"kv_bytes_per_call": kvb, "calls": n_calls}
         if window:
             entry["window"] = window
+        entry["kv_dtype"] = dt
         if name == "long_ctx_gqa8":
             ms = event_time_ms(calls[0], 3, torch)
             ms = event_time_ms(calls[0], 10, torch) / 10
@@ -221,7 +222,7 @@ def per_config(pa, knobs, torch, workloads_mod):
                 gbs = kvb / (entry[key] * 1e-6) / 1e9
                 entry[key.replace("us_per_call", "kv_GBps")] = round(gbs, 1)
                 entry[key.replace("us_per_call", "hbm_frac")] = round(gbs / HBM_PEAK_GBS, 4)
-        key = f"{name}_w{window}" if window else name
+        key = name + (f"_w{window}" if window else "") + (f"_{dt}" if dt != "bf16" else "")
         res[key] = entry
         log(f"[per_config] {key}: {entry}")
         del d, calls

@@ -56,6 +56,7 @@ extern "C" {
 #define PA_DTYPE_BF16  1
 #define PA_DTYPE_INT32 2
 #define PA_DTYPE_FP32  3
+#define PA_DTYPE_F16   4   /* IEEE binary16 */
 
 /*
  * A strided view of device memory.  shape[] and stride[] are in elements;
@@ -190,7 +191,10 @@ typedef struct pa_opts {
 /*
  * Bytes of workspace pa_decode_ex needs for a call with these sizes and
  * options (0 when the call does not split).  max_blocks_per_seq is
- * block_tables.shape[1].  Returns 0 on bad arguments as well.
+ * block_tables.shape[1].  With the automatic variant the kernel depends on
+ * the K/V element type, which is not an argument here: the result is then
+ * the larger of the two plans, enough for any element type.  Returns 0 on
+ * bad arguments as well.
  */
 size_t pa_decode_workspace_bytes(int64_t num_seqs, int num_q_heads, int num_kv_heads,
                                  int head_dim, int64_t max_blocks_per_seq, int page_size,

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
 
 PA_OK, PA_EINVAL, PA_ENOTSUP, PA_EALIGN, PA_ENODEV, PA_ENOMEM, PA_EHIP = range(7)
-PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32 = 1, 2, 3
+PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32, PA_DTYPE_F16 = 1, 2, 3, 4
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 VARIANTS = {"auto": PA_VARIANT_AUTO, "valu": PA_VARIANT_VALU, "mfma": PA_VARIANT_MFMA}
 PA_SCHEDULE_AUTO, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED = 0, 1, 2
@@ -123,7 +123,7 @@ def _check(rc: int, where: str):
 def _dtype_code(t) -> int:
     import torch
     return {torch.bfloat16: PA_DTYPE_BF16, torch.int32: PA_DTYPE_INT32,
-            torch.float32: PA_DTYPE_FP32}.get(t.dtype, 0)
+            torch.float32: PA_DTYPE_FP32, torch.float16: PA_DTYPE_F16}.get(t.dtype, 0)
 
 
 def tensor_desc(t) -> PaTensor:
@@ -252,13 +252,14 @@ def pa_release() -> None:
 # ------------------------------------------------------------------ convenience
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None, *,
            variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0,
-           window: int = 0, workspace=None, stream=None):
+           window: int = 0, workspace=None, stream=None, out_dtype=None):
     """Decode paged attention on torch tensors.
 
-    q [B, Hq, D] bf16; k_cache/v_cache [NP, P, Hkv, D] bf16 (NHD pool);
+    q [B, Hq, D]; k_cache/v_cache [NP, P, Hkv, D] (NHD pool) -- each bf16, fp16
+    or fp32 (K and V alike); out defaults to q's type (``out_dtype`` overrides);
     block_tables [B, MaxBlk] int32; context_lens [B] int32; scale defaults to
     1/sqrt(D); ``window`` > 0 attends to each sequence's last ``window``
-    tokens only.  Returns out [B, Hq, D] bf16.  The split-KV workspace comes
+    tokens only.  Returns out [B, Hq, D].  The split-KV workspace comes
     zero-filled from torch's caching allocator unless one is given (a given
     one must start with 256 zero bytes; see pa_decode_ex).
     """
@@ -268,7 +269,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     opts = make_opts(variant, partition_tokens, schedule, shares, window)
     if workspace is None:
         n = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], P, opts)

@@ -43,7 +43,11 @@ struct Counters {
 struct Geometry {
     int64_t B, Hq, Hkv, D, P, NP, max_blk;
     int qg;
+    int q_dtype, kv_dtype, out_dtype;
 };
+
+inline bool float_type(int32_t dt) { return dt == PA_DTYPE_BF16 || dt == PA_DTYPE_F16 || dt == PA_DTYPE_FP32; }
+inline int elem_size(int32_t dt) { return dt == PA_DTYPE_FP32 ? 4 : 2; }
 
 struct Plan {
     int variant;        // PA_VARIANT_VALU / PA_VARIANT_MFMA
@@ -77,13 +81,16 @@ constexpr int64_t kLeanMaxUnits = (int64_t)kLeanMaxShares * (1 + pa::kLeanDynPer
 constexpr int64_t kLeanAutoMinTiles = 262144;
 
 constexpr size_t kAlign = 256;
+constexpr int32_t kAnyFloat = 0;              // check_tensor: any of the float element types
 constexpr int kMaxDevices = 64;               // CU-count cache entries
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_tensor(const pa_tensor* t, const char* name, int32_t dtype, int ndim) {
     if (!t) return fail(PA_EINVAL, "%s: descriptor is NULL", name);
-    if (t->dtype != dtype) return fail(PA_EINVAL, "%s: dtype %d, expected %d", name, t->dtype, dtype);
+    if (dtype == kAnyFloat ? !float_type(t->dtype) : t->dtype != dtype)
+        return fail(PA_EINVAL, "%s: dtype %d, expected %s", name, t->dtype,
+                    dtype == kAnyFloat ? "bf16, fp16 or fp32" : (dtype == PA_DTYPE_INT32 ? "int32" : "bf16"));
     if (t->ndim != ndim) return fail(PA_EINVAL, "%s: ndim %d, expected %d", name, t->ndim, ndim);
     for (int i = 0; i < ndim; ++i) {
         if (t->shape[i] < 0) return fail(PA_EINVAL, "%s: negative shape[%d]", name, i);
@@ -100,10 +107,11 @@ int check_tensor(const pa_tensor* t, const char* name, int32_t dtype, int ndim) 
 int check_rows16(const pa_tensor* t, const char* name, int n_outer) {
     if (!t->data) return PA_OK;   // empty tensor (checked by check_tensor)
     if (!aligned16(t->data)) return fail(PA_EALIGN, "%s: base pointer not 16-byte aligned", name);
+    const int per16 = 16 / elem_size(t->dtype);   // elements per 16 bytes
     for (int i = 0; i < n_outer; ++i)
-        if (t->shape[i] > 1 && (t->stride[i] % 8) != 0)
-            return fail(PA_EALIGN, "%s: stride[%d]=%lld is not a multiple of 8 elements", name, i,
-                        (long long)t->stride[i]);
+        if (t->shape[i] > 1 && (t->stride[i] % per16) != 0)
+            return fail(PA_EALIGN, "%s: stride[%d]=%lld is not a multiple of %d elements (16 bytes)", name, i,
+                        (long long)t->stride[i], per16);
     return PA_OK;
 }
 
@@ -111,12 +119,13 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
              const pa_tensor* ctx, float scale, int num_q_heads, int num_kv_heads, int head_dim,
              int page_size, const pa_tensor* out, const pa_opts* opts, Geometry& geo) {
     int rc;
-    if ((rc = check_tensor(q, "q", PA_DTYPE_BF16, 3))) return rc;
-    if ((rc = check_tensor(k, "k_cache", PA_DTYPE_BF16, 4))) return rc;
-    if ((rc = check_tensor(v, "v_cache", PA_DTYPE_BF16, 4))) return rc;
+    if ((rc = check_tensor(q, "q", kAnyFloat, 3))) return rc;
+    if ((rc = check_tensor(k, "k_cache", kAnyFloat, 4))) return rc;
+    if ((rc = check_tensor(v, "v_cache", kAnyFloat, 4))) return rc;
     if ((rc = check_tensor(bt, "block_tables", PA_DTYPE_INT32, 2))) return rc;
     if ((rc = check_tensor(ctx, "context_lens", PA_DTYPE_INT32, 1))) return rc;
-    if ((rc = check_tensor(out, "out", PA_DTYPE_BF16, 3))) return rc;
+    if ((rc = check_tensor(out, "out", kAnyFloat, 3))) return rc;
+    if (k->dtype != v->dtype) return fail(PA_EINVAL, "k_cache and v_cache element types differ");
     if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
     if (page_size < 1) return fail(PA_EINVAL, "page_size %d < 1", page_size);
     if (num_q_heads < 1 || num_kv_heads < 1) return fail(PA_EINVAL, "head counts must be >= 1");
@@ -150,7 +159,8 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
             return fail(PA_EINVAL, "shares %d outside 0..%d", opts->shares, kLeanMaxShares);
         if (opts->window < 0) return fail(PA_EINVAL, "window %d < 0", opts->window);
     }
-    if (head_dim != 128 && head_dim != 256) return fail(PA_ENOTSUP, "head_dim %d (supported: 128, 256)", head_dim);
+    if (head_dim != 128 && head_dim != 256 && head_dim != 512)
+        return fail(PA_ENOTSUP, "head_dim %d (supported: 128, 256, 512)", head_dim);
     const int qg = num_q_heads / num_kv_heads;
     if (qg != 1 && qg != 2 && qg != 4 && qg != 8 && qg != 16)
         return fail(PA_ENOTSUP, "Hq/Hkv = %d (supported: 1, 2, 4, 8, 16)", qg);
@@ -164,7 +174,8 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
     if ((rc = check_rows16(out, "out", 2))) return rc;
     if ((reinterpret_cast<uintptr_t>(bt->data) & 3u) || (reinterpret_cast<uintptr_t>(ctx->data) & 3u))
         return fail(PA_EALIGN, "block_tables/context_lens not 4-byte aligned");
-    geo = Geometry{B, num_q_heads, num_kv_heads, head_dim, page_size, k->shape[0], bt->shape[1], qg};
+    geo = Geometry{B, num_q_heads, num_kv_heads, head_dim, page_size, k->shape[0], bt->shape[1], qg,
+                   q->dtype, k->dtype, out->dtype};
     return PA_OK;
 }
 
@@ -174,11 +185,11 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     if (opts && opts->variant)
         pl.variant = opts->variant;
     else
-        pl.variant = pa::mfma_supported((int)g.D, qw_mfma) ? PA_VARIANT_MFMA : PA_VARIANT_VALU;
+        pl.variant = pa::mfma_supported((int)g.D, qw_mfma, g.kv_dtype) ? PA_VARIANT_MFMA : PA_VARIANT_VALU;
     if (pl.variant == PA_VARIANT_MFMA)
         pl.qw = qw_mfma;                        // one 16-column MFMA tile of queries
     else
-        pl.qw = g.qg < 8 ? g.qg : 8;
+        pl.qw = std::min(g.qg, g.D == 512 ? 2 : 8);   // query rows that fit the VALU registers
     // Tokens a sequence's work can span: the block table's capacity, or with
     // a window of W the W tokens plus up to 15 before them (work starts on a
     // 16-token tile boundary).
@@ -297,8 +308,11 @@ int cu_count(int dev) {
 }
 
 int check_plan(const Geometry& g, const Plan& pl, const pa_opts* opts) {
-    if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw))
-        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
+    if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw, g.kv_dtype))
+        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d, K/V dtype %d (D 128/256, "
+                    "bf16 or fp16 K/V)", (long long)g.D, g.qg, g.kv_dtype);
+    if (pl.variant == PA_VARIANT_VALU && !pa::valu_supported((int)g.D, pl.qw, g.kv_dtype))
+        return fail(PA_ENOTSUP, "vector-ALU variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
     if (opts && opts->schedule == PA_SCHEDULE_BALANCED && !pl.lean)
         return fail(PA_ENOTSUP, "balanced schedule needs the MFMA variant and at most %d sequences",
                     kLeanMaxBatch);
@@ -309,21 +323,23 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
            const pa_tensor* ctx, float scale, const pa_tensor* out, void* stream,
            const Geometry& g, const Plan& pl, const pa_opts* opts, void* ws, int dev) {
     pa::DecodeParams p{};
-    p.q = static_cast<const uint16_t*>(q->data);
+    p.q = q->data;
+    p.q_dtype = g.q_dtype;
+    p.out_dtype = g.out_dtype;
     p.q_sb = q->stride[0];
     p.q_sh = q->stride[1];
-    p.k = static_cast<const uint16_t*>(k->data);
+    p.k = k->data;
     p.k_sp = k->stride[0];
     p.k_ss = k->stride[1];
     p.k_sh = k->stride[2];
-    p.v = static_cast<const uint16_t*>(v->data);
+    p.v = v->data;
     p.v_sp = v->stride[0];
     p.v_ss = v->stride[1];
     p.v_sh = v->stride[2];
     p.bt = static_cast<const int32_t*>(bt->data);
     p.bt_sb = bt->stride[0];
     p.ctx = static_cast<const int32_t*>(ctx->data);
-    p.out = static_cast<uint16_t*>(out->data);
+    p.out = out->data;
     p.o_sb = out->stride[0];
     p.o_sh = out->stride[1];
     p.part_o = pl.split ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.o_offset) : nullptr;
@@ -355,7 +371,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
         // (measured: 272 shares on 256 CUs run 1.33x longer than 256), and
         // a second share per CU brings no more bandwidth.
         const int n_wg = pl.n_part_fixed ? pl.n_part : std::min(pl.n_part, cu_count(dev));
-        e = pa::launch_mfma_lean(p, (int)g.D, n_wg, s);
+        e = pa::launch_mfma_lean(p, (int)g.D, g.kv_dtype, n_wg, s);
         if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma, balanced) launch: %s", hipGetErrorString(e));
         g_stats.mfma++;
         g_stats.lean++;
@@ -369,11 +385,11 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
         return PA_OK;
     }
     if (pl.variant == PA_VARIANT_MFMA) {
-        e = pa::launch_mfma(p, (int)g.D, pl.qw, pl.split, s);
+        e = pa::launch_mfma(p, (int)g.D, g.kv_dtype, pl.qw, pl.split, s);
         if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma) launch: %s", hipGetErrorString(e));
         g_stats.mfma++;
     } else {
-        e = pa::launch_valu(p, (int)g.D, pl.qw, pl.split, s);
+        e = pa::launch_valu(p, (int)g.D, g.kv_dtype, pl.qw, pl.split, s);
         if (e != hipSuccess) return fail(PA_EHIP, "decode (valu) launch: %s", hipGetErrorString(e));
         g_stats.valu++;
     }
@@ -435,15 +451,18 @@ int validate_append(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* k
                     const pa_tensor* bt, const pa_tensor* ctx, int num_kv_heads, int head_dim,
                     int page_size) {
     int rc;
-    if ((rc = check_tensor(kn, "k_new", PA_DTYPE_BF16, 3))) return rc;
-    if ((rc = check_tensor(vn, "v_new", PA_DTYPE_BF16, 3))) return rc;
-    if ((rc = check_tensor(k, "k_cache", PA_DTYPE_BF16, 4))) return rc;
-    if ((rc = check_tensor(v, "v_cache", PA_DTYPE_BF16, 4))) return rc;
+    if ((rc = check_tensor(kn, "k_new", kAnyFloat, 3))) return rc;
+    if ((rc = check_tensor(vn, "v_new", kAnyFloat, 3))) return rc;
+    if ((rc = check_tensor(k, "k_cache", kAnyFloat, 4))) return rc;
+    if ((rc = check_tensor(v, "v_cache", kAnyFloat, 4))) return rc;
+    if (kn->dtype != k->dtype || vn->dtype != k->dtype || v->dtype != k->dtype)
+        return fail(PA_EINVAL, "k_new, v_new, k_cache and v_cache must share their element type");
     if ((rc = check_tensor(bt, "block_tables", PA_DTYPE_INT32, 2))) return rc;
     if ((rc = check_tensor(ctx, "context_lens", PA_DTYPE_INT32, 1))) return rc;
     if (page_size < 1) return fail(PA_EINVAL, "page_size %d < 1", page_size);
     if (num_kv_heads < 1) return fail(PA_EINVAL, "num_kv_heads must be >= 1");
-    if (head_dim < 8 || head_dim % 8) return fail(PA_ENOTSUP, "head_dim %d is not a multiple of 8", head_dim);
+    if (head_dim < 8 || head_dim * elem_size(k->dtype) % 16)
+        return fail(PA_ENOTSUP, "head_dim %d: rows are not whole 16-byte chunks", head_dim);
     const int64_t B = kn->shape[0];
     for (int i = 0; i < 3; ++i)
         if (vn->shape[i] != kn->shape[i]) return fail(PA_EINVAL, "k_new and v_new shapes differ");
@@ -490,26 +509,27 @@ int pa_cache_append(const pa_tensor* k_new, const pa_tensor* v_new, const pa_ten
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(PA_ENODEV, "no HIP device");
     pa::AppendParams a{};
-    a.k_new = static_cast<const uint16_t*>(k_new->data);
-    a.v_new = static_cast<const uint16_t*>(v_new->data);
-    a.kn_sb = k_new->stride[0];
-    a.kn_sh = k_new->stride[1];
-    a.vn_sb = v_new->stride[0];
-    a.vn_sh = v_new->stride[1];
-    a.k = static_cast<uint16_t*>(k_cache->data);
-    a.v = static_cast<uint16_t*>(v_cache->data);
-    a.k_sp = k_cache->stride[0];
-    a.k_ss = k_cache->stride[1];
-    a.k_sh = k_cache->stride[2];
-    a.v_sp = v_cache->stride[0];
-    a.v_ss = v_cache->stride[1];
-    a.v_sh = v_cache->stride[2];
+    const int es = elem_size(k_cache->dtype);     // strides become byte strides
+    a.k_new = static_cast<const char*>(k_new->data);
+    a.v_new = static_cast<const char*>(v_new->data);
+    a.kn_sb = k_new->stride[0] * es;
+    a.kn_sh = k_new->stride[1] * es;
+    a.vn_sb = v_new->stride[0] * es;
+    a.vn_sh = v_new->stride[1] * es;
+    a.k = static_cast<char*>(k_cache->data);
+    a.v = static_cast<char*>(v_cache->data);
+    a.k_sp = k_cache->stride[0] * es;
+    a.k_ss = k_cache->stride[1] * es;
+    a.k_sh = k_cache->stride[2] * es;
+    a.v_sp = v_cache->stride[0] * es;
+    a.v_ss = v_cache->stride[1] * es;
+    a.v_sh = v_cache->stride[2] * es;
     a.bt = static_cast<const int32_t*>(block_tables->data);
     a.bt_sb = block_tables->stride[0];
     a.ctx = static_cast<const int32_t*>(context_lens->data);
     a.B = (int)k_new->shape[0];
     a.Hkv = num_kv_heads;
-    a.D = head_dim;
+    a.row_bytes = head_dim * es;
     a.P = page_size;
     a.max_blk = (int)block_tables->shape[1];
     a.num_pages = (int)k_cache->shape[0];
@@ -559,9 +579,17 @@ size_t pa_decode_workspace_bytes(int64_t num_seqs, int num_q_heads, int num_kv_h
         head_dim < 1 || max_blocks_per_seq < 0 || page_size < 1)
         return 0;
     if (opts && opts->partition_tokens < 0) return 0;
+    // The automatic variant depends on the K/V element type, which this
+    // function is not told: return the larger of the two plans it can pick.
     Geometry g{num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, 1, max_blocks_per_seq,
-               num_q_heads / num_kv_heads};
-    return make_plan(g, opts).ws_bytes;
+               num_q_heads / num_kv_heads, PA_DTYPE_BF16, PA_DTYPE_BF16, PA_DTYPE_BF16};
+    size_t bytes = make_plan(g, opts).ws_bytes;
+    if (!opts || opts->variant == PA_VARIANT_AUTO) {
+        Geometry g32 = g;
+        g32.kv_dtype = PA_DTYPE_FP32;           // no MFMA path: the vector-ALU plan
+        bytes = std::max(bytes, make_plan(g32, opts).ws_bytes);
+    }
+    return bytes;
 }
 
 int pa_get_stats(pa_stats* s) {

@@ -2,8 +2,9 @@
 // has its K and V rows (all KV heads) written into its page slot of the NHD
 // pools, the step that precedes decode attention in a decode step.
 //
-// One workgroup per sequence; each thread moves 16-byte chunks, so a row of
-// Hkv * D bf16 is written by whole-line vector stores.  The work is a few
+// One workgroup per sequence; each thread moves 16-byte chunks, so a token's
+// Hkv rows are written by whole-line vector stores, whatever the element
+// type (bf16, fp16 or fp32: the copy is byte-exact).  The work is a few
 // KB per sequence: the kernel is bound by launch and memory latency, not by
 // bandwidth.
 #include "pa_device.h"
@@ -19,22 +20,23 @@ __global__ __launch_bounds__(256) void pa_cache_append_kernel(AppendParams a) {
     const int lp = t / a.P, slot = t - lp * a.P;
     const int page = a.bt[(int64_t)b * a.bt_sb + lp];
     if (page < 0 || page >= a.num_pages) return;    // not a page of the pool: no write
-    const int chunks = a.Hkv * (a.D / 8);           // 16-byte chunks per row (K or V)
+    const int per_head = a.row_bytes / 16;          // 16-byte chunks per head row
+    const int chunks = a.Hkv * per_head;            // per token (K or V)
     for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
         const bool is_v = c >= chunks;
         const int cc = is_v ? c - chunks : c;
-        const int g = cc / (a.D / 8), d = (cc - g * (a.D / 8)) * 8;
-        const uint16_t* src = is_v ? a.v_new + (int64_t)b * a.vn_sb + (int64_t)g * a.vn_sh + d
-                                   : a.k_new + (int64_t)b * a.kn_sb + (int64_t)g * a.kn_sh + d;
-        uint16_t* dst = is_v ? a.v + (int64_t)page * a.v_sp + (int64_t)slot * a.v_ss + (int64_t)g * a.v_sh + d
-                             : a.k + (int64_t)page * a.k_sp + (int64_t)slot * a.k_ss + (int64_t)g * a.k_sh + d;
+        const int g = cc / per_head, off = (cc - g * per_head) * 16;
+        const char* src = is_v ? a.v_new + (int64_t)b * a.vn_sb + (int64_t)g * a.vn_sh + off
+                               : a.k_new + (int64_t)b * a.kn_sb + (int64_t)g * a.kn_sh + off;
+        char* dst = is_v ? a.v + (int64_t)page * a.v_sp + (int64_t)slot * a.v_ss + (int64_t)g * a.v_sh + off
+                         : a.k + (int64_t)page * a.k_sp + (int64_t)slot * a.k_ss + (int64_t)g * a.k_sh + off;
         *reinterpret_cast<u32x4*>(dst) = load16(src);
     }
 }
 
 hipError_t launch_append(const AppendParams& a, hipStream_t s) {
     if (a.B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(pa_cache_append_kernel, dim3(a.B), dim3(a.Hkv * a.D / 8 >= 256 ? 256 : 128), 0, s, a);
+    hipLaunchKernelGGL(pa_cache_append_kernel, dim3(a.B), dim3(a.Hkv * a.row_bytes / 16 >= 256 ? 256 : 128), 0, s, a);
     return hipGetLastError();
 }
 

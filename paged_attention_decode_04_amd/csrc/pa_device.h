@@ -7,15 +7,19 @@
 
 namespace pa {
 
+// Element types (the ABI's PA_DTYPE_* codes).
+constexpr int kDtBF16 = 1, kDtF32 = 3, kDtF16 = 4;
+
 // Everything a decode kernel needs, passed by value (kernarg segment).
-// Strides are in elements.
+// Strides are in elements of each tensor's own type.
 struct DecodeParams {
-    const uint16_t* q;      int64_t q_sb, q_sh;             // [B][Hq][D]
-    const uint16_t* k;      int64_t k_sp, k_ss, k_sh;       // [NP][P][Hkv][D]
-    const uint16_t* v;      int64_t v_sp, v_ss, v_sh;
+    const void*     q;      int64_t q_sb, q_sh;             // [B][Hq][D], type q_dtype
+    const void*     k;      int64_t k_sp, k_ss, k_sh;       // [NP][P][Hkv][D], the kernel's KV type
+    const void*     v;      int64_t v_sp, v_ss, v_sh;
     const int32_t*  bt;     int64_t bt_sb;                  // [B][MaxBlk]
     const int32_t*  ctx;                                    // [B]
-    uint16_t*       out;    int64_t o_sb, o_sh;             // [B][Hq][D]
+    void*           out;    int64_t o_sb, o_sh;             // [B][Hq][D], type out_dtype
+    int             q_dtype, out_dtype;
     float*          part_o;                                 // [B][Hq][n_part][D]
     float*          part_lse;                               // [B][Hq][n_part]
     int   B, Hq, Hkv, P, max_blk, num_pages;
@@ -30,15 +34,16 @@ struct DecodeParams {
     float scale_log2;                                       // scale * log2(e)
 };
 
-// KV-cache append: newest token of each sequence into its page slot.
+// KV-cache append: newest token of each sequence into its page slot.  Byte
+// pointers and byte strides: the copy does not depend on the element type.
 struct AppendParams {
-    const uint16_t* k_new; const uint16_t* v_new;           // [B, Hkv, D]
-    int64_t kn_sb, kn_sh, vn_sb, vn_sh;                     // their batch and head strides
-    uint16_t* k; uint16_t* v;                               // pools [NP, P, Hkv, D]
-    int64_t k_sp, k_ss, k_sh, v_sp, v_ss, v_sh;
+    const char* k_new; const char* v_new;                   // [B, Hkv, D]
+    int64_t kn_sb, kn_sh, vn_sb, vn_sh;                     // their batch and head strides (bytes)
+    char* k; char* v;                                       // pools [NP, P, Hkv, D]
+    int64_t k_sp, k_ss, k_sh, v_sp, v_ss, v_sh;             // bytes
     const int32_t* bt; int64_t bt_sb;
     const int32_t* ctx;
-    int B, Hkv, D, P, max_blk, num_pages;
+    int B, Hkv, row_bytes, P, max_blk, num_pages;           // row_bytes = D * element size
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -59,6 +64,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// IEEE binary16 halves of a dword, and fp32 -> binary16 (round to nearest even).
+__device__ __forceinline__ float f16lo(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -84,14 +101,102 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+template <typename T>
+__device__ __forceinline__ u32x4 load16(const T* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
 // Streaming load: K/V rows are read once per call, keep them out of the way.
-__device__ __forceinline__ u32x4 load16_nt(const uint16_t* p) {
+template <typename T>
+__device__ __forceinline__ u32x4 load16_nt(const T* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+
+// 8 consecutive elements of an array of element type dt, as floats (the
+// element offset is a multiple of 8, so every load is 16-byte aligned).
+__device__ __forceinline__ void load8f(const void* base, int dt, int64_t off, float (&f)[8]) {
+    if (dt == kDtF32) {
+        const float* fp = static_cast<const float*>(base) + off;
+        const u32x4 a = load16(fp), b = load16(fp + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = __uint_as_float(a[i]);
+            f[4 + i] = __uint_as_float(b[i]);
+        }
+        return;
+    }
+    const u32x4 w = load16(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = dt == kDtF16 ? f16lo(w[i]) : bf16lo(w[i]);
+        f[2 * i + 1] = dt == kDtF16 ? f16hi(w[i]) : bf16hi(w[i]);
+    }
+}
+
+// 8 floats stored at element offset off of an array of type dt (rounded to
+// nearest even for the 16-bit types); off is a multiple of 8.
+__device__ __forceinline__ void store8(void* base, int dt, int64_t off, const float (&v)[8]) {
+    if (dt == kDtF32) {
+        float* fp = static_cast<float*>(base) + off;
+        *reinterpret_cast<float4*>(fp) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(fp + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        return;
+    }
+    u32x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        pk[i] = dt == kDtF16 ? pack_f16x2(v[2 * i], v[2 * i + 1]) : pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + off) = pk;
+}
+
+// 2 floats at element offset off (even) of an array of type dt.
+__device__ __forceinline__ void store2(void* base, int dt, int64_t off, float a, float b) {
+    if (dt == kDtF32) {
+        *reinterpret_cast<float2*>(static_cast<float*>(base) + off) = make_float2(a, b);
+        return;
+    }
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + off) =
+        dt == kDtF16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
+}
+
+// 16-bit KV element types on the matrix cores: the Q.K and P.V MFMAs and
+// the packing of P (and of a converted Q) into that type.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct KvBF16 {
+    static constexpr int code = kDtBF16;
+    __device__ static __forceinline__ f32x4 mma_qk(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4 mma_pv(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                        __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+    __device__ static __forceinline__ float lo(uint32_t u) { return bf16lo(u); }
+    __device__ static __forceinline__ float hi(uint32_t u) { return bf16hi(u); }
+};
+
+struct KvF16 {
+    static constexpr int code = kDtF16;
+    __device__ static __forceinline__ f32x4 mma_qk(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                     __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4 mma_pv(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                    __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+    __device__ static __forceinline__ float lo(uint32_t u) { return f16lo(u); }
+    __device__ static __forceinline__ float hi(uint32_t u) { return f16hi(u); }
+};
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -115,14 +220,15 @@ __device__ __forceinline__ void page_slot(const DecodeParams& p, int t, int& lp,
 }
 
 // Log-sum-exp merge of n split partials (o_p fp32 rows of D, lse_p base 2)
-// at slots first, first + step, ... into one bf16 output row, by 64 threads
+// at slots first, first + step, ... into the output row at element offset
+// out_off (in the output's type), by 64 threads
 // holding D / 64 elements each.  Partials are read four at a time with
 // their lse and o rows together, so a merge of up to four costs one round
 // trip to memory; the running maximum rescales between batches.  n == 0
 // writes zeros.
 template <int D>
 __device__ __forceinline__ void merge_partials(const DecodeParams& p, int64_t first, int64_t step, int n,
-                                               uint16_t* orow) {
+                                               int64_t out_off) {
     constexpr int EPT = D / 64;
     typedef float vec_t __attribute__((ext_vector_type(EPT)));
     const int t = threadIdx.x;
@@ -154,8 +260,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int64_t fi
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-    for (int e = 0; e < EPT; e += 2)
-        *reinterpret_cast<uint32_t*>(orow + t * EPT + e) = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
+    for (int e = 0; e < EPT; e += 2) store2(p.out, p.out_dtype, out_off + t * EPT + e, o[e] * inv, o[e + 1] * inv);
 }
 
 }  // namespace pa

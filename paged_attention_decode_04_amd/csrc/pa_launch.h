@@ -13,18 +13,20 @@ inline size_t pages_lds_bytes(const DecodeParams& p) {
     return sizeof(int) * (size_t)((p.part_tokens + p.P - 1) / p.P + 1);
 }
 
-// Vector-ALU decode kernel; qw = query heads per workgroup (1, 2, 4 or 8).
-hipError_t launch_valu(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s);
+// Vector-ALU decode kernel; qw = query heads per workgroup (1, 2, 4 or 8;
+// 1 or 2 at head_dim 512); K/V of type kv_dtype (bf16, fp16 or fp32).
+hipError_t launch_valu(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s);
+bool valu_supported(int head_dim, int qw, int kv_dtype);
 
-// Matrix-core decode kernel (16 query rows per MFMA tile).
-hipError_t launch_mfma(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s);
-bool mfma_supported(int head_dim, int qw);
+// Matrix-core decode kernel (16 query rows per MFMA tile); bf16 or fp16 K/V.
+hipError_t launch_mfma(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s);
+bool mfma_supported(int head_dim, int qw, int kv_dtype);
 
 // Matrix-core decode over a balanced schedule (the sequence-major list of
 // (sequence, query block, 16-token tile) cut into one static unit per
 // workgroup and dynamic units taken from a counter), followed by the merge
 // of the units' partials.
-hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int n_wg, hipStream_t s);
+hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int kv_dtype, int n_wg, hipStream_t s);
 constexpr int kLeanTokensPerFill = 4096;     // tokens whose page ids one LDS fill holds
 // Page-id LDS entries of the balanced schedule: a run of kLeanTokensPerFill
 // tokens spans at most ceil(kLeanTokensPerFill / P) + 1 pages.

@@ -37,11 +37,6 @@
 
 namespace pa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kMBlock = 256;
 constexpr int kMWaves = kMBlock / 64;
 constexpr int kTile = 16;                       // tokens per MFMA tile
@@ -100,8 +95,10 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pa
         const int lp = tb >> p.p_shift;
         const int page = __builtin_amdgcn_readfirstlane(s_pages[lp - pg0]);
         const int slot0 = tb - (lp << p.p_shift);
-        const uint16_t* kt = p.k + (int64_t)page * p.k_sp + (int64_t)g * p.k_sh + (int64_t)slot0 * p.k_ss;
-        const uint16_t* vt = p.v + (int64_t)page * p.v_sp + (int64_t)g * p.v_sh + (int64_t)slot0 * p.v_ss;
+        const uint16_t* kt = static_cast<const uint16_t*>(p.k) + (int64_t)page * p.k_sp + (int64_t)g * p.k_sh +
+                             (int64_t)slot0 * p.k_ss;
+        const uint16_t* vt = static_cast<const uint16_t*>(p.v) + (int64_t)page * p.v_sp + (int64_t)g * p.v_sh +
+                             (int64_t)slot0 * p.v_ss;
         const int ks = (int)p.k_ss, vs = (int)p.v_ss;
         if (tb + kTile <= te && tb >= t_min) {  // full tile (wave-uniform)
 #pragma unroll
@@ -131,13 +128,14 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, const int* s_pa
 #pragma unroll
         for (int i = 0; i < KK; ++i) {
             const int tk = clampi(tb + k_row<D, HALF>(i, n), t_min, te - 1);
-            f.k[i] = load16_nt(p.k + row_offset(p, s_pages, pg0, tk, p.k_sp, p.k_ss, gk) +
+            f.k[i] = load16_nt(static_cast<const uint16_t*>(p.k) + row_offset(p, s_pages, pg0, tk, p.k_sp, p.k_ss, gk) +
                                k_col<D, HALF>(i, n, q));
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int tv = clampi(tb + 4 * q + jj, t_min, te - 1);
-            const uint16_t* vr = p.v + row_offset(p, s_pages, pg0, tv, p.v_sp, p.v_ss, gv) + 8 * n;
+            const uint16_t* vr = static_cast<const uint16_t*>(p.v) + row_offset(p, s_pages, pg0, tv, p.v_sp, p.v_ss, gv) +
+                                 8 * n;
 #pragma unroll
             for (int hh = 0; hh < TileFrag<D>::VH; ++hh) f.v[jj][hh] = load16_nt(vr + 128 * hh);
         }
@@ -173,7 +171,7 @@ __device__ __forceinline__ float xsum32(float x) {
 }
 
 // One 16-token tile: logits on MFMA, online-softmax update, O^T += V^T P^T.
-template <int D, bool HALF>
+template <int D, bool HALF, typename KV>
 __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<D>& cur,
                                           const u32x4 (&qop)[D / 32], int tb, int t_min, int te,
                                           int q, bool col_live, f32x4 (&o)[D / 16], float& m_run,
@@ -188,10 +186,8 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
         f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KH; ++kk) {
-            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[kk]),
-                                                         __builtin_bit_cast(bf16x8, qop[kk]), c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[KH + kk]),
-                                                         __builtin_bit_cast(bf16x8, qop[kk]), c1, 0, 0, 0);
+            c0 = KV::mma_qk(cur.k[kk], qop[kk], c0);
+            c1 = KV::mma_qk(cur.k[KH + kk], qop[kk], c1);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -209,8 +205,7 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
         s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[kk]),
-                                                        __builtin_bit_cast(bf16x8, qop[kk]), s, 0, 0, 0);
+            s = KV::mma_qk(cur.k[kk], qop[kk], s);
     }
     float sv[4];
     float mt = -INFINITY;
@@ -236,11 +231,11 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - m_run);
-    // P.V takes P in bf16; the normaliser sums the same rounded weights, so
+    // P.V takes P in the KV type; the normaliser sums the same rounded weights, so
     // the output stays an exact weighted mean of V rows (weights off by at
     // most 2^-9 relative) rather than picking up the rounding as a bias.
-    const u32x2 pb = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-    l_run += (bf16lo(pb[0]) + bf16hi(pb[0])) + (bf16lo(pb[1]) + bf16hi(pb[1]));
+    const u32x2 pb = {KV::pack2(pr[0], pr[1]), KV::pack2(pr[2], pr[3])};
+    l_run += (KV::lo(pb[0]) + KV::hi(pb[0])) + (KV::lo(pb[1]) + KV::hi(pb[1]));
 
     // O^T += V^T . P^T, V transposed in registers (4 tokens x 8 dims per lane)
 #pragma unroll
@@ -253,26 +248,36 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
             const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
             const u32x2 va = {__builtin_amdgcn_perm(cur.v[1][hh][x], cur.v[0][hh][x], sel),
                               __builtin_amdgcn_perm(cur.v[3][hh][x], cur.v[2][hh][x], sel)};
-            o[hh * 8 + mm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                __builtin_bit_cast(bf16x4, va), __builtin_bit_cast(bf16x4, pb), o[hh * 8 + mm], 0, 0, 0);
+            o[hh * 8 + mm] = KV::mma_pv(va, pb, o[hh * 8 + mm]);
         }
 }
 
 // Q^T as the B operand of query heads h0 .. h0 + qw - 1 of sequence b (same
-// k <-> dim map as the K rows of the layout).  Columns past qw are zero.
-template <int D, bool HALF>
+// k <-> dim map as the K rows of the layout), in the KV element type: a Q
+// stored in another type is converted (round to nearest even).  Columns
+// past qw are zero.
+template <int D, bool HALF, typename KV>
 __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int qw, int n, int q,
                                        u32x4 (&qop)[D / 32]) {
     const int qcol = HALF ? (n & 7) : n;
     const bool live = qcol < qw;
-    const uint16_t* qr = p.q + (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? qcol : 0)) * p.q_sh;
+    const int64_t qr = (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? qcol : 0)) * p.q_sh;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
         if (HALF && kk >= D / 64) {
             qop[kk] = u32x4{0u, 0u, 0u, 0u};            // unused in the split layout
             continue;
         }
-        u32x4 w = load16(qr + k_col<D, HALF>(kk, n, q));
+        const int64_t off = qr + k_col<D, HALF>(kk, n, q);
+        u32x4 w;
+        if (p.q_dtype == KV::code) {
+            w = load16(static_cast<const uint16_t*>(p.q) + off);
+        } else {
+            float f[8];
+            load8f(p.q, p.q_dtype, off, f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = KV::pack2(f[2 * i], f[2 * i + 1]);
+        }
         qop[kk] = live ? w : u32x4{0u, 0u, 0u, 0u};
     }
 }
@@ -283,7 +288,7 @@ __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int
 // is consumed; the steady-state loop issues its prefetches unconditionally
 // (each wait covers exactly the tile being consumed) and the last few tiles
 // drain in a short unrolled tail.  No data moves between buffers.
-template <int D, bool PAGE16, bool HALF, int NBUF>
+template <int D, bool PAGE16, bool HALF, int NBUF, typename KV>
 __device__ __forceinline__ void run_tiles(const DecodeParams& p, const int* s_pages, int pg0, int g,
                                           int n, int q, int wave, const LaneOffsets& lo,
                                           const u32x4 (&qop)[D / 32], bool col_live, int ts, int te,
@@ -302,7 +307,7 @@ __device__ __forceinline__ void run_tiles(const DecodeParams& p, const int* s_pa
             load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), t_min, te,
                                        fb[(i + NBUF - 1) % NBUF]);
             __builtin_amdgcn_sched_barrier(0);
-            tile_step<D, HALF>(p, fb[i], qop, tile_tb(k + i), t_min, te, q, col_live, o, m_run, l_run);
+            tile_step<D, HALF, KV>(p, fb[i], qop, tile_tb(k + i), t_min, te, q, col_live, o, m_run, l_run);
         }
     }
 #pragma unroll
@@ -311,7 +316,7 @@ __device__ __forceinline__ void run_tiles(const DecodeParams& p, const int* s_pa
             if (k + i + NBUF - 1 < n_my)
                 load_tile<D, PAGE16, HALF>(p, s_pages, pg0, g, n, q, lo, tile_tb(k + i + NBUF - 1), t_min, te,
                                            fb[(i + NBUF - 1) % NBUF]);
-            tile_step<D, HALF>(p, fb[i % NBUF], qop, tile_tb(k + i), t_min, te, q, col_live, o, m_run, l_run);
+            tile_step<D, HALF, KV>(p, fb[i % NBUF], qop, tile_tb(k + i), t_min, te, q, col_live, o, m_run, l_run);
         }
     }
 }
@@ -380,13 +385,6 @@ __device__ __forceinline__ void merge_waves(MergeLds<D>& lds, const f32x4 (&o)[D
     __syncthreads();
 }
 
-__device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float (&v)[8]) {
-    u32x4 pk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(dst) = pk;
-}
-
 __device__ __forceinline__ void store_f32x8(float* dst, const float (&v)[8]) {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -399,7 +397,7 @@ __device__ __forceinline__ void store_f32x8(float* dst, const float (&v)[8]) {
 // heads and sequences of the same partition index, so every XCD gets an even
 // share of each sequence's work, and partitions past a sequence's end (which
 // exit at once) come last.
-template <int D, bool SPLIT, bool PAGE16, bool HALF, int NBUF>
+template <int D, bool SPLIT, bool PAGE16, bool HALF, int NBUF, typename KV>
 __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p) {
     constexpr int KK = TileFrag<D>::KK;
     constexpr int NO = D / 16;                  // O^T accumulator tiles
@@ -437,7 +435,7 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     const int te = min(L, ts + p.part_tokens);
 
     u32x4 qop[KK];
-    load_q<D, HALF>(p, b, h0, qw, n, q, qop);
+    load_q<D, HALF, KV>(p, b, h0, qw, n, q, qop);
     const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
     __syncthreads();
 
@@ -449,7 +447,7 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     lo.k = k_row<D, HALF>(0, n) * (int)p.k_ss + k_col<D, HALF>(0, n, q);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) lo.v[jj] = (4 * q + jj) * (int)p.v_ss + 8 * n;
-    run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, ts, te, t_begin, o,
+    run_tiles<D, PAGE16, HALF, NBUF, KV>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, ts, te, t_begin, o,
                                      m_run, l_run);
     l_run = xsum32(xsum16(l_run));              // row sums over the four 16-lane rows
 
@@ -458,7 +456,7 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
                    [&](int jq, int d0, const float (&ov)[8], float lse) {
         const int h = h0 + jq;
         if constexpr (!SPLIT) {
-            store_bf16x8(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
+            store8(p.out, p.out_dtype, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
         } else {
             const int64_t slot = ((int64_t)b * p.Hq + h) * p.n_part + part;
             store_f32x8(p.part_o + slot * D + d0, ov);
@@ -528,7 +526,7 @@ struct LeanUnits {
     }
 };
 
-template <int D, bool PAGE16, bool HALF, int NBUF>
+template <int D, bool PAGE16, bool HALF, int NBUF, typename KV>
 __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodeParams p) {
     constexpr int KK = TileFrag<D>::KK;
     constexpr int NO = D / 16;
@@ -623,7 +621,7 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
             const int ts = t_base + t_lo * kTile, te = min(t_base + t_hi * kTile, L);
 
             u32x4 qop[KK];
-            load_q<D, HALF>(p, b, h0, qw, n, q, qop);
+            load_q<D, HALF, KV>(p, b, h0, qw, n, q, qop);
             const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
             f32x4 o[NO];
 #pragma unroll
@@ -645,7 +643,7 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
                 if (c0 != ts) __syncthreads();
                 fetch_pages(p, b, pg0, lp1, s_pages, tid);
                 __syncthreads();
-                run_tiles<D, PAGE16, HALF, NBUF>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, c0, c1,
+                run_tiles<D, PAGE16, HALF, NBUF, KV>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, c0, c1,
                                                  t_begin, o, m_run, l_run);
             }
             l_run = xsum32(xsum16(l_run));
@@ -653,7 +651,7 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
                            [&](int jq, int d0, const float (&ov)[8], float lse) {
                 const int h = h0 + jq;
                 if (whole) {
-                    store_bf16x8(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
+                    store8(p.out, p.out_dtype, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
                 } else {
                     const int64_t slot = ((int64_t)(G + u)) * qw + jq;
                     store_f32x8(p.part_o + slot * D + d0, ov);
@@ -682,8 +680,8 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_lean_kernel(DecodePara
             if (s_pref[bb + 1] != s_pref[bb]) continue;
             for (int idx = tid; idx < p.Hq * (D / 8); idx += kMBlock) {
                 const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                store_bf16x8(p.out + (int64_t)bb * p.o_sb + (int64_t)(idx / (D / 8)) * p.o_sh +
-                             (idx % (D / 8)) * 8, z);
+                store8(p.out, p.out_dtype, (int64_t)bb * p.o_sb + (int64_t)(idx / (D / 8)) * p.o_sh +
+                       (idx % (D / 8)) * 8, z);
             }
         }
     }
@@ -705,65 +703,75 @@ __global__ __launch_bounds__(64) void pa_lean_merge_kernel(DecodeParams p) {
     const int u0 = lu.unit_of(start), u1 = lu.unit_of(start + tiles_b - 1);
     if (u0 == u1) return;
     const int64_t G = (int64_t)b * n_qb + qb;
-    merge_partials<D>(p, (G + u0) * qw + jq, qw, u1 - u0 + 1,
-                      p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
+    merge_partials<D>(p, (G + u0) * qw + jq, qw, u1 - u0 + 1, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
 }
 
-bool mfma_supported(int head_dim, int qw) {
-    return (head_dim == 128 || head_dim == 256) && qw >= 1 && qw <= 16;
+bool mfma_supported(int head_dim, int qw, int kv_dtype) {
+    return (head_dim == 128 || head_dim == 256) && qw >= 1 && qw <= 16 &&
+           (kv_dtype == kDtBF16 || kv_dtype == kDtF16);
 }
 
-template <int D, bool SPLIT, bool PAGE16>
+template <int D, bool SPLIT, bool PAGE16, typename KV>
 static hipError_t launch_mfma_t(const DecodeParams& p, int qw, hipStream_t s) {
     dim3 grid((uint32_t)((int64_t)p.n_part * (p.Hq / qw) * p.B));
     constexpr int NBUF = D == 128 ? 3 : 2;
     if (qw <= 8)
-        hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16, true, NBUF>), grid, dim3(kMBlock),
+        hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16, true, NBUF, KV>), grid, dim3(kMBlock),
                            pages_lds_bytes(p), s, p);
     else
-        hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16, false, NBUF>), grid, dim3(kMBlock),
+        hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16, false, NBUF, KV>), grid, dim3(kMBlock),
                            pages_lds_bytes(p), s, p);
     return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_mfma_d(const DecodeParams& p, int qw, bool split, hipStream_t s) {
-    // Tiles start at multiples of 16 tokens (partitions at multiples of 64);
-    // in-page offsets must fit 32 bits.
-    const bool page16 = p.p_shift >= 4 && (int64_t)p.P * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) < (1ll << 30);
-    if (split) return page16 ? launch_mfma_t<D, true, true>(p, qw, s) : launch_mfma_t<D, true, false>(p, qw, s);
-    return page16 ? launch_mfma_t<D, false, true>(p, qw, s) : launch_mfma_t<D, false, false>(p, qw, s);
+// Tiles start at multiples of 16 tokens (partitions at multiples of 64); the
+// one-page-per-tile path also needs in-page offsets that fit 32 bits.
+static bool page16_ok(const DecodeParams& p) {
+    return p.p_shift >= 4 && (int64_t)p.P * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) < (1ll << 30);
 }
 
-template <int D, bool PAGE16, bool HALF>
+template <int D, typename KV>
+static hipError_t launch_mfma_d(const DecodeParams& p, int qw, bool split, hipStream_t s) {
+    const bool page16 = page16_ok(p);
+    if (split) return page16 ? launch_mfma_t<D, true, true, KV>(p, qw, s) : launch_mfma_t<D, true, false, KV>(p, qw, s);
+    return page16 ? launch_mfma_t<D, false, true, KV>(p, qw, s) : launch_mfma_t<D, false, false, KV>(p, qw, s);
+}
+
+template <int D, bool PAGE16, bool HALF, typename KV>
 static hipError_t launch_lean_t(const DecodeParams& p, int n_wg, hipStream_t s) {
     constexpr int NBUF = D == 128 ? 3 : 2;
     const size_t lds = sizeof(int) * (size_t)(p.lean_page_slots + p.B + 1);
-    hipLaunchKernelGGL((pa_decode_mfma_lean_kernel<D, PAGE16, HALF, NBUF>), dim3(n_wg), dim3(kMBlock), lds, s, p);
+    hipLaunchKernelGGL((pa_decode_mfma_lean_kernel<D, PAGE16, HALF, NBUF, KV>), dim3(n_wg), dim3(kMBlock), lds, s,
+                       p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pa_lean_merge_kernel<D>, dim3(p.Hq, p.B), dim3(64), 0, s, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename KV>
 static hipError_t launch_lean_d(const DecodeParams& p, int n_wg, hipStream_t s) {
-    const bool page16 = p.p_shift >= 4 && (int64_t)p.P * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) < (1ll << 30);
+    const bool page16 = page16_ok(p);
     const bool half = p.qw <= 8;
-    if (page16) return half ? launch_lean_t<D, true, true>(p, n_wg, s) : launch_lean_t<D, true, false>(p, n_wg, s);
-    return half ? launch_lean_t<D, false, true>(p, n_wg, s) : launch_lean_t<D, false, false>(p, n_wg, s);
+    if (page16)
+        return half ? launch_lean_t<D, true, true, KV>(p, n_wg, s) : launch_lean_t<D, true, false, KV>(p, n_wg, s);
+    return half ? launch_lean_t<D, false, true, KV>(p, n_wg, s) : launch_lean_t<D, false, false, KV>(p, n_wg, s);
 }
 
-hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int n_wg, hipStream_t s) {
-    if (!mfma_supported(head_dim, p.qw) || p.Hq % p.qw) return hipErrorInvalidValue;
-    if (head_dim == 128) return launch_lean_d<128>(p, n_wg, s);
-    return launch_lean_d<256>(p, n_wg, s);
+hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int kv_dtype, int n_wg, hipStream_t s) {
+    if (!mfma_supported(head_dim, p.qw, kv_dtype) || p.Hq % p.qw) return hipErrorInvalidValue;
+    if (kv_dtype == kDtF16)
+        return head_dim == 128 ? launch_lean_d<128, KvF16>(p, n_wg, s) : launch_lean_d<256, KvF16>(p, n_wg, s);
+    return head_dim == 128 ? launch_lean_d<128, KvBF16>(p, n_wg, s) : launch_lean_d<256, KvBF16>(p, n_wg, s);
 }
 
-hipError_t launch_mfma(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s) {
-    if (!mfma_supported(head_dim, qw) || p.Hq % qw) return hipErrorInvalidValue;
-    if (head_dim == 128) return launch_mfma_d<128>(p, qw, split, s);
-    return launch_mfma_d<256>(p, qw, split, s);
+hipError_t launch_mfma(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s) {
+    if (!mfma_supported(head_dim, qw, kv_dtype) || p.Hq % qw) return hipErrorInvalidValue;
+    if (kv_dtype == kDtF16)
+        return head_dim == 128 ? launch_mfma_d<128, KvF16>(p, qw, split, s)
+                               : launch_mfma_d<256, KvF16>(p, qw, split, s);
+    return head_dim == 128 ? launch_mfma_d<128, KvBF16>(p, qw, split, s)
+                           : launch_mfma_d<256, KvBF16>(p, qw, split, s);
 }
 
 }  // namespace pa

@@ -30,18 +30,54 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kRowsPerWave = 4;                 // 16 lanes per row
 constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
 
-template <int D, int U>
+// K/V element types on the vector ALUs: a 16-byte load holds PER elements;
+// lane c of a 16-lane row holds dims 8c .. 8c + 7 of every 128-dim block.
+struct VkBF16 {
+    using E = uint16_t;
+    static constexpr int PER = 8;
+    __device__ static __forceinline__ void to_f(u32x4 w, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16lo(w[i]);
+            f[2 * i + 1] = bf16hi(w[i]);
+        }
+    }
+};
+struct VkF16 {
+    using E = uint16_t;
+    static constexpr int PER = 8;
+    __device__ static __forceinline__ void to_f(u32x4 w, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = f16lo(w[i]);
+            f[2 * i + 1] = f16hi(w[i]);
+        }
+    }
+};
+struct VkF32 {
+    using E = float;
+    static constexpr int PER = 4;
+    __device__ static __forceinline__ void to_f(u32x4 w, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+    }
+};
+
+template <int D, int U, typename KV>
 struct RowFrag {
-    static constexpr int NCH = D / 128;         // 16-byte chunks per lane per row
-    u32x4 k[U][NCH];
-    u32x4 v[U][NCH];
+    static constexpr int NCH = D / 128;         // 128-dim blocks per row
+    static constexpr int LPC = 8 / KV::PER;     // 16-byte loads per block per lane
+    u32x4 k[U][NCH * LPC];
+    u32x4 v[U][NCH * LPC];
     bool valid[U];
 };
 
-template <int D, int U>
+template <int D, int U, typename KV>
 __device__ __forceinline__ void load_rows(const DecodeParams& p, const int* s_pages, int pg0,
                                           int g, int c, int t_first, int te, int ts, int t_min,
-                                          RowFrag<D, U>& f) {
+                                          RowFrag<D, U, KV>& f) {
+    using E = typename KV::E;
+    constexpr int LPC = RowFrag<D, U, KV>::LPC;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int t = t_first + u * kRowsPerBlock;
@@ -52,17 +88,19 @@ __device__ __forceinline__ void load_rows(const DecodeParams& p, const int* s_pa
         int lp, slot;
         page_slot(p, tt, lp, slot);
         const int64_t page = s_pages[lp - pg0];
-        const uint16_t* kp = p.k + page * p.k_sp + (int64_t)slot * p.k_ss + (int64_t)g * p.k_sh + c * 8;
-        const uint16_t* vp = p.v + page * p.v_sp + (int64_t)slot * p.v_ss + (int64_t)g * p.v_sh + c * 8;
+        const E* kp = static_cast<const E*>(p.k) + page * p.k_sp + (int64_t)slot * p.k_ss + (int64_t)g * p.k_sh + c * 8;
+        const E* vp = static_cast<const E*>(p.v) + page * p.v_sp + (int64_t)slot * p.v_ss + (int64_t)g * p.v_sh + c * 8;
 #pragma unroll
-        for (int ch = 0; ch < RowFrag<D, U>::NCH; ++ch) {
-            f.k[u][ch] = load16_nt(kp + ch * 128);
-            f.v[u][ch] = load16_nt(vp + ch * 128);
-        }
+        for (int ch = 0; ch < RowFrag<D, U, KV>::NCH; ++ch)
+#pragma unroll
+            for (int j = 0; j < LPC; ++j) {
+                f.k[u][ch * LPC + j] = load16_nt(kp + ch * 128 + j * KV::PER);
+                f.v[u][ch * LPC + j] = load16_nt(vp + ch * 128 + j * KV::PER);
+            }
     }
 }
 
-template <int D, int QW, int U, bool SPLIT>
+template <int D, int QW, int U, bool SPLIT, typename KV>
 __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) {
     constexpr int E = D / 16;                   // dims held per lane
     constexpr int NCH = E / 8;
@@ -96,19 +134,17 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
             s_pages[i] = clampi(btrow[pg0 + i], 0, p.num_pages - 1);
     }
 
-    // Q rows of the group, pre-scaled to base-2 logits.
+    // Q rows of the group (any element type), pre-scaled to base-2 logits.
     float qf[QW][E];
 #pragma unroll
     for (int j = 0; j < QW; ++j) {
-        const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)(h0 + j) * p.q_sh + c * 8;
+        const int64_t qrow = (int64_t)b * p.q_sb + (int64_t)(h0 + j) * p.q_sh + c * 8;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
-            const u32x4 w = load16(qrow + ch * 128);
+            float f[8];
+            load8f(p.q, p.q_dtype, qrow + ch * 128, f);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qf[j][ch * 8 + 2 * i] = bf16lo(w[i]) * p.scale_log2;
-                qf[j][ch * 8 + 2 * i + 1] = bf16hi(w[i]) * p.scale_log2;
-            }
+            for (int i = 0; i < 8; ++i) qf[j][ch * 8 + i] = f[i] * p.scale_log2;
         }
     }
     __syncthreads();
@@ -124,26 +160,25 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
 
     constexpr int TPI = kRowsPerBlock * U;      // tokens per iteration per workgroup
     const int my_row = wave * kRowsPerWave + row;
-    RowFrag<D, U> cur;
-    if (n_tok > 0) load_rows<D, U>(p, s_pages, pg0, g, c, ts + my_row, te, ts, t_begin, cur);
+    RowFrag<D, U, KV> cur;
+    if (n_tok > 0) load_rows<D, U, KV>(p, s_pages, pg0, g, c, ts + my_row, te, ts, t_begin, cur);
     for (int base = 0; base < n_tok; base += TPI) {
-        RowFrag<D, U> nxt;
+        RowFrag<D, U, KV> nxt;
         const bool more = base + TPI < n_tok;
-        if (more) load_rows<D, U>(p, s_pages, pg0, g, c, ts + base + TPI + my_row, te, ts, t_begin, nxt);
+        if (more) load_rows<D, U, KV>(p, s_pages, pg0, g, c, ts + base + TPI + my_row, te, ts, t_begin, nxt);
 
         float s[U][QW];
         float vf[U][E];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float kf[E];
+            constexpr int LPC = RowFrag<D, U, KV>::LPC;
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kf[ch * 8 + 2 * i] = bf16lo(cur.k[u][ch][i]);
-                    kf[ch * 8 + 2 * i + 1] = bf16hi(cur.k[u][ch][i]);
-                    vf[u][ch * 8 + 2 * i] = bf16lo(cur.v[u][ch][i]);
-                    vf[u][ch * 8 + 2 * i + 1] = bf16hi(cur.v[u][ch][i]);
+                for (int j = 0; j < LPC; ++j) {
+                    KV::to_f(cur.k[u][ch * LPC + j], &kf[ch * 8 + j * KV::PER]);
+                    KV::to_f(cur.v[u][ch * LPC + j], &vf[u][ch * 8 + j * KV::PER]);
                 }
 #pragma unroll
             for (int j = 0; j < QW; ++j) {
@@ -233,10 +268,7 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
         }
         const int h = h0 + j;
         if constexpr (!SPLIT) {
-            u32x4 pk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
-            *reinterpret_cast<u32x4*>(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0) = pk;
+            store8(p.out, p.out_dtype, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, o);
         } else {
             const int64_t slot = ((int64_t)b * p.Hq + h) * p.n_part + part;
             float* op = p.part_o + slot * D + d0;
@@ -255,40 +287,64 @@ __global__ __launch_bounds__(64) void pa_lse_merge_kernel(DecodeParams p) {
     int t_begin, t_base;
     window_bounds(p, L, t_begin, t_base);
     const int n_used = (L - t_base + p.part_tokens - 1) / p.part_tokens;
-    merge_partials<D>(p, ((int64_t)b * p.Hq + h) * p.n_part, 1, n_used,
-                      p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
+    merge_partials<D>(p, ((int64_t)b * p.Hq + h) * p.n_part, 1, n_used, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
 }
 
 // ------------------------------------------------------------------ launch
-template <int D, int QW, int U, bool SPLIT>
+template <int D, int QW, int U, bool SPLIT, typename KV>
 static hipError_t launch_valu_t(const DecodeParams& p, size_t lds, hipStream_t s) {
     dim3 grid(p.n_part, p.Hq / QW, p.B);
-    hipLaunchKernelGGL((pa_decode_valu_kernel<D, QW, U, SPLIT>), grid, dim3(kBlock), lds, s, p);
+    hipLaunchKernelGGL((pa_decode_valu_kernel<D, QW, U, SPLIT, KV>), grid, dim3(kBlock), lds, s, p);
     return hipGetLastError();
 }
 
-template <int D, int QW, int U>
+template <int D, int QW, int U, typename KV>
 static hipError_t launch_valu_s(const DecodeParams& p, bool split, size_t lds, hipStream_t s) {
-    return split ? launch_valu_t<D, QW, U, true>(p, lds, s) : launch_valu_t<D, QW, U, false>(p, lds, s);
+    return split ? launch_valu_t<D, QW, U, true, KV>(p, lds, s) : launch_valu_t<D, QW, U, false, KV>(p, lds, s);
 }
 
-template <int D>
+template <int D, typename KV>
 static hipError_t launch_valu_d(const DecodeParams& p, int qw, bool split, size_t lds, hipStream_t s) {
-    constexpr int U = D == 128 ? 2 : 1;
-    switch (qw) {
-        case 1: return launch_valu_s<D, 1, 2>(p, split, lds, s);
-        case 2: return launch_valu_s<D, 2, 2>(p, split, lds, s);
-        case 4: return launch_valu_s<D, 4, U>(p, split, lds, s);
-        case 8: return launch_valu_s<D, 8, U>(p, split, lds, s);
-        default: return hipErrorInvalidValue;
+    if constexpr (D == 512) {
+        // 32 dims per lane per query: at most two queries per workgroup fit
+        // the registers.
+        switch (qw) {
+            case 1: return launch_valu_s<D, 1, 1, KV>(p, split, lds, s);
+            case 2: return launch_valu_s<D, 2, 1, KV>(p, split, lds, s);
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        constexpr int U = D == 128 ? 2 : 1;
+        switch (qw) {
+            case 1: return launch_valu_s<D, 1, 2, KV>(p, split, lds, s);
+            case 2: return launch_valu_s<D, 2, 2, KV>(p, split, lds, s);
+            case 4: return launch_valu_s<D, 4, U, KV>(p, split, lds, s);
+            case 8: return launch_valu_s<D, 8, U, KV>(p, split, lds, s);
+            default: return hipErrorInvalidValue;
+        }
     }
 }
 
-hipError_t launch_valu(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s) {
+template <typename KV>
+static hipError_t launch_valu_k(const DecodeParams& p, int head_dim, int qw, bool split, hipStream_t s) {
     const size_t lds = pages_lds_bytes(p);
-    if (head_dim == 128) return launch_valu_d<128>(p, qw, split, lds, s);
-    if (head_dim == 256) return launch_valu_d<256>(p, qw, split, lds, s);
+    if (head_dim == 128) return launch_valu_d<128, KV>(p, qw, split, lds, s);
+    if (head_dim == 256) return launch_valu_d<256, KV>(p, qw, split, lds, s);
+    if (head_dim == 512) return launch_valu_d<512, KV>(p, qw, split, lds, s);
     return hipErrorInvalidValue;
+}
+
+bool valu_supported(int head_dim, int qw, int kv_dtype) {
+    const bool kv_ok = kv_dtype == kDtBF16 || kv_dtype == kDtF16 || kv_dtype == kDtF32;
+    if (head_dim == 512) return kv_ok && (qw == 1 || qw == 2);
+    return kv_ok && (head_dim == 128 || head_dim == 256) && (qw == 1 || qw == 2 || qw == 4 || qw == 8);
+}
+
+hipError_t launch_valu(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s) {
+    if (!valu_supported(head_dim, qw, kv_dtype)) return hipErrorInvalidValue;
+    if (kv_dtype == kDtF16) return launch_valu_k<VkF16>(p, head_dim, qw, split, s);
+    if (kv_dtype == kDtF32) return launch_valu_k<VkF32>(p, head_dim, qw, split, s);
+    return launch_valu_k<VkBF16>(p, head_dim, qw, split, s);
 }
 
 hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s) {
@@ -297,6 +353,8 @@ hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s) {
         hipLaunchKernelGGL(pa_lse_merge_kernel<128>, grid, dim3(64), 0, s, p);
     else if (head_dim == 256)
         hipLaunchKernelGGL(pa_lse_merge_kernel<256>, grid, dim3(64), 0, s, p);
+    else if (head_dim == 512)
+        hipLaunchKernelGGL(pa_lse_merge_kernel<512>, grid, dim3(64), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -69,7 +69,9 @@ def test_valid_arguments_pass():
 
 
 @pytest.mark.parametrize("mutate,code", [
-    (lambda a: a.update(q=a["q"].float()), pa.PA_EINVAL),
+    (lambda a: a.update(q=a["q"].double()), pa.PA_EINVAL),
+    (lambda a: a.update(v_cache=a["v_cache"].half()), pa.PA_EINVAL),   # K and V types differ
+    (lambda a: a.update(out=a["out"].to(torch.int32)), pa.PA_EINVAL),
     (lambda a: a.update(num_q_heads=15), pa.PA_EINVAL),
     (lambda a: a.update(scale=float("nan")), pa.PA_EINVAL),
     (lambda a: a.update(scale=float("inf")), pa.PA_EINVAL),
@@ -87,6 +89,28 @@ def test_bad_arguments_are_rejected(mutate, code):
     mutate(a)
     assert check(a) == code
     assert pa.last_error() != ""
+
+
+def test_element_types_and_head_sizes():
+    """bf16 / fp16 / fp32 for Q, K/V and out; head_dim 512 and fp32 K/V run
+    on the vector-ALU kernel, so asking for the MFMA variant there is
+    ENOTSUP."""
+    for qt in (torch.bfloat16, torch.float16, torch.float32):
+        for kt in (torch.bfloat16, torch.float16, torch.float32):
+            a = args()
+            a.update(q=a["q"].to(qt), k_cache=a["k_cache"].to(kt), v_cache=a["v_cache"].to(kt),
+                     out=a["out"].to(qt))
+            assert check(a) == pa.PA_OK, (qt, kt)
+    a = args()
+    a.update(k_cache=a["k_cache"].float(), v_cache=a["v_cache"].float())
+    assert check(a, pa.make_opts("mfma")) == pa.PA_ENOTSUP
+    assert check(a, pa.make_opts("valu")) == pa.PA_OK
+    assert check(args(D=512, Hq=16, Hkv=8)) == pa.PA_OK
+    assert check(args(D=512, Hq=16, Hkv=8), pa.make_opts("mfma")) == pa.PA_ENOTSUP
+    a = args()
+    big = torch.zeros(8, 16, 8, 130, dtype=torch.float32)[..., :128]   # fp32 rows 520 B apart
+    a.update(k_cache=big, v_cache=torch.zeros(8, 16, 8, 128))
+    assert check(a) == pa.PA_EALIGN
 
 
 def test_unsupported_geometry():
@@ -193,18 +217,23 @@ def test_workspace_bytes():
     assert n == HDR + rnd(slots * D * 4) + rnd(slots * 4) + rnd((B + 4) * 4)
     # the automatic choice: balanced for a large call (64 sequences of up to
     # 32768 tokens, 8 query blocks), partitions for a small one
-    big = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, None)
+    big = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, pa.make_opts("mfma"))
     slots = (64 * 8 + 1024 * 7) * 8
     assert big == HDR + rnd(slots * 128 * 4) + rnd(slots * 4) + rnd(68 * 4)
     assert big == pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16,
                                                pa.make_opts("mfma", 0, "balanced"))
-    small = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, None)
+    # the automatic variant covers both kernels (an fp32 cache takes the
+    # vector-ALU one): 8 query heads per workgroup, 1024-token partitions
+    auto = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, None)
+    valu = HDR + rnd(64 * 64 * 32 * 128 * 4) + rnd(64 * 64 * 32 * 4)
+    assert auto == max(big, valu)
+    small = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, pa.make_opts("mfma"))
     assert small == pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16,
                                                  pa.make_opts("mfma", 0, "partitions"))
     # a window bounds the span a sequence's work covers (W + 15 tokens): the
     # same large call with a 4096-token window falls below the balanced
     # threshold and splits into ceil(4111 / 4096) = 2 partitions of 4096
-    n = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, pa.make_opts(window=4096))
+    n = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, pa.make_opts("mfma", window=4096))
     assert n == HDR + rnd(64 * 64 * 2 * 128 * 4) + rnd(64 * 64 * 2 * 4)
     # setting partition_tokens alone selects the partition schedule
     n = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma", 64))

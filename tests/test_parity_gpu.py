@@ -33,6 +33,14 @@ def bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def host_out(t):
+    """An output tensor on the host: bf16 as uint16 bits, fp16 / fp32 as numpy
+    float16 / float32 (what the comparator takes)."""
+    if t.dtype == torch.bfloat16:
+        return bits(t)
+    return t.contiguous().cpu().numpy()
+
+
 def knobs(variant, tokens):
     """Split settings to sweep: partition sizes, or share counts when balanced."""
     if _MODE[variant][1] == "balanced":
@@ -40,10 +48,10 @@ def knobs(variant, tokens):
     return [dict(partition_tokens=T) for T in tokens]
 
 
-def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0):
+def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0, out_dtype=None):
     kernel, schedule = _MODE[variant]
     q, k, v = d.call(call)
-    out = torch.full_like(q, float("nan"))      # every row must be written
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype or q.dtype, device=q.device)   # every row must be written
     pa.pa_reset_stats()
     pa.decode(q, k, v, d.block_tables, d.context_lens, d.w.scale, out=out, variant=kernel,
               partition_tokens=partition_tokens, schedule=schedule, shares=shares, window=window)
@@ -57,7 +65,7 @@ def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0):
         assert s["balanced_calls"] == 1 and s["merge_launches"] == 1, s
         if shares:
             assert s["last_num_partitions"] == shares, s
-    return bits(out), s
+    return host_out(out), s
 
 
 def oracle_run(inp, call=0, window=0):
@@ -518,3 +526,79 @@ def test_append_skips_sequences_it_cannot_place():
     assert np.array_equal(bits(k).reshape(k_ref.shape), k_ref)
     assert np.array_equal(bits(v).reshape(v_ref.shape), v_ref)
     assert not np.array_equal(bits(k), k0)
+
+
+# ------------------------------------------------------------------ element types, head_dim 512
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+# (Q, K/V, out): the same type throughout, and fp32 activations over a 16-bit cache
+DTYPE_COMBOS = [("f16", "f16", "f16"), ("f32", "f32", "f32"), ("f32", "bf16", "f32"),
+                ("f32", "f16", "f32"), ("bf16", "f16", "bf16"), ("f16", "bf16", "f32")]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("qt,kt,ot", DTYPE_COMBOS)
+@pytest.mark.parametrize("D", [128, 256])
+def test_dtype_parity_poisoned(variant, qt, kt, ot, D):
+    if kt == "f32" and variant != "valu":
+        pytest.skip("fp32 K/V runs on the vector-ALU kernel only (MFMA asks ENOTSUP)")
+    w = custom(batch=5, num_q_heads=16, num_kv_heads=4, head_dim=D, page_size=16,
+               ctx=(1, 17, 300, 1000, 2500), pool_pages=300)
+    inp = make_inputs(w, seed=D + len(qt + kt), poison_unused=True, dtype=kt, q_dtype=qt)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for kn in knobs(variant, (0, 64)):
+        y, _ = gpu_run(d, variant=variant, out_dtype=TORCH_DT[ot], **kn)
+        assert np.all(np.isfinite(y.astype(np.float64) if ot != "bf16" else workloads_f32(y)))
+        assert_parity(y, ref, f"q {qt} kv {kt} out {ot} D={D} {kn}")
+    for W in (7, 500):
+        y, _ = gpu_run(d, variant=variant, out_dtype=TORCH_DT[ot], window=W)
+        assert_parity(y, oracle_run(inp, window=W), f"q {qt} kv {kt} out {ot} D={D} W={W}")
+
+
+def test_fp32_cache_on_mfma_is_enotsup():
+    w = custom(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=128, page_size=16, ctx=(5,))
+    d = to_device(make_inputs(w, seed=1, dtype="f32"))
+    q, k, v = d.call(0)
+    with pytest.raises(pa.PaError):
+        pa.decode(q, k, v, d.block_tables, d.context_lens, variant="mfma")
+
+
+@pytest.mark.parametrize("kt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (16, 4), (16, 2)])
+def test_head_dim_512(kt, Hq, Hkv):
+    """head_dim 512 on the vector-ALU kernel (two query heads per workgroup
+    at most): split and unsplit, with and without a window."""
+    w = custom(batch=4, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=512, page_size=16,
+               ctx=(1, 33, 700, 1500))
+    inp = make_inputs(w, seed=Hq * Hkv, poison_unused=True, dtype=kt)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for T in (0, 64, 4096):
+        y, s = gpu_run(d, variant="valu", partition_tokens=T)
+        assert_parity(y, ref, f"D=512 kv {kt} Hq={Hq} Hkv={Hkv} T={T}")
+    y, _ = gpu_run(d, variant="valu", window=100)
+    assert_parity(y, oracle_run(inp, window=100), f"D=512 kv {kt} W=100")
+    # the automatic choice takes the vector-ALU kernel at head_dim 512
+    pa.pa_reset_stats()
+    q, k, v = d.call(0)
+    pa.decode(q, k, v, d.block_tables, d.context_lens)
+    torch.cuda.synchronize()
+    assert pa.pa_get_stats()["valu_launches"] == 1
+
+
+@pytest.mark.parametrize("kt", ["f16", "f32"])
+def test_append_typed_caches_bitwise(kt):
+    w = custom(batch=4, num_q_heads=8, num_kv_heads=4, head_dim=128, page_size=16, ctx=(1, 16, 17, 90))
+    inp = make_inputs(w, seed=9, dtype=kt)
+    rng = np.random.default_rng(9)
+    dt = workloads.STORAGE[kt]
+    k_new = rng.standard_normal((4, 4, 128)).astype(dt)
+    v_new = rng.standard_normal((4, 4, 128)).astype(dt)
+    k_ref, v_ref = oracle.cache_append(inp.k[0], inp.v[0], inp.block_tables, inp.context_lens, k_new, v_new)
+    d = to_device(inp)
+    k, v = d.k[0].clone(), d.v[0].clone()
+    pa.cache_append(torch.from_numpy(k_new).cuda(), torch.from_numpy(v_new).cuda(), k, v,
+                    d.block_tables, d.context_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(k.cpu().numpy().view(np.uint8), k_ref.view(np.uint8))
+    assert np.array_equal(v.cpu().numpy().view(np.uint8), v_ref.view(np.uint8))

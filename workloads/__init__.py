@@ -21,6 +21,8 @@ kernel", numerics table):
 ``hd256_gqa4``     32 seqs, ctx U[512, 4096], Hq 8, Hkv 2, d 256, page 32,
                    K rows x4 on 1% of tokens
 ``long_ctx_gqa8``  64 seqs, ctx U[8192, 32768], Hq 64, Hkv 8, d 128, page 16
+``hd512_gqa4``     16 seqs, ctx U[1024, 4096], Hq 8, Hkv 2, d 512, page 16
+                   (head_dim 512; an extra line, not one of the five)
 =================  ===================================================
 
 Recipe (NumPy PCG64 ``default_rng(seed)``, draws in this order):
@@ -100,6 +102,9 @@ WORKLOADS = {
                            desc="32 seqs ctx U[512,4096], Hq8/Hkv2, d256, page 32, 1% K x4"),
     "long_ctx_gqa8": Workload("long_ctx_gqa8", 64, 64, 8, 128, 16, ctx_range=(8192, 32768),
                               desc="64 seqs ctx U[8192,32768], Hq64/Hkv8, d128, page 16"),
+    # head_dim 512 (the pages' EPL=16 case): not one of the five configurations
+    "hd512_gqa4": Workload("hd512_gqa4", 16, 8, 2, 512, 16, ctx_range=(1024, 4096),
+                           desc="16 seqs ctx U[1024,4096], Hq8/Hkv2, d512, page 16"),
 }
 ORDER = ["tiny", "single_seq", "batch16", "hd256_gqa4", "long_ctx_gqa8"]
 
@@ -267,9 +272,13 @@ def make_inputs(w: Workload | str, seed: int = 0, poison_unused: bool = False,
     return Inputs(w, q, k, v, lay)
 
 
-def kv_bytes(w: Workload, context_lens) -> int:
-    """Algorithmic KV bytes of one call: sum_b L_b * Hkv * D * 2 (K and V) * 2 B."""
-    return int(np.asarray(context_lens, dtype=np.int64).sum()) * w.num_kv_heads * w.head_dim * 4
+def kv_bytes(w: Workload, context_lens, window: int = 0, elem_bytes: int = 2) -> int:
+    """Algorithmic KV bytes of one call: sum_b min(L_b, window) * Hkv * D * 2
+    (K and V) * element size (window 0 = the whole sequence)."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    if window:
+        lens = np.minimum(lens, window)
+    return int(lens.sum()) * w.num_kv_heads * w.head_dim * 2 * elem_bytes
 
 
 # ----------------------------------------------------------------------------
@@ -302,13 +311,15 @@ def to_device(inp: Inputs, device="cuda") -> DeviceInputs:
                         torch.from_numpy(inp.context_lens).to(device), inp.layout)
 
 
-def device_inputs(w: Workload | str, seed: int = 0, device="cuda") -> DeviceInputs:
+def device_inputs(w: Workload | str, seed: int = 0, device="cuda", dtype: str = "bf16") -> DeviceInputs:
     """Same layout recipe (steps 1, 2, 4); Q/K/V drawn on the device with
     ``torch.Generator(device).manual_seed(seed)`` as N(0, 1) fp32 rounded to
-    bf16 (torch rounds to nearest even).  Unused pool pages hold zeros."""
+    the storage type (bf16 by default; torch rounds to nearest even).  Unused
+    pool pages hold zeros."""
     import torch
     if isinstance(w, str):
         w = WORKLOADS[w]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     rng = np.random.default_rng(seed)
     lay = make_layout(w, rng)
     spikes = _spikes(w, lay, rng)
@@ -316,11 +327,11 @@ def device_inputs(w: Workload | str, seed: int = 0, device="cuda") -> DeviceInpu
     B, Hq, Hkv, D, P = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    q = torch.randn((w.calls, B, Hq, D), generator=gen, device=device).to(torch.bfloat16)
+    q = torch.randn((w.calls, B, Hq, D), generator=gen, device=device).to(tdt)
     used = torch.from_numpy(lay.used_pages).to(device)
     full = lay.used_pages.size == lay.num_pages and np.array_equal(
         np.sort(lay.used_pages), np.arange(lay.num_pages))
-    k = torch.zeros((w.layers, lay.num_pages, P, Hkv, D), dtype=torch.bfloat16, device=device)
+    k = torch.zeros((w.layers, lay.num_pages, P, Hkv, D), dtype=tdt, device=device)
     v = torch.zeros_like(k)
     chunk = 4096
     for layer in range(w.layers):
@@ -328,7 +339,7 @@ def device_inputs(w: Workload | str, seed: int = 0, device="cuda") -> DeviceInpu
             for s in range(0, used.numel(), chunk):
                 ids = used[s:s + chunk]
                 vals = torch.randn((ids.numel(), P, Hkv, D), generator=gen,
-                                   device=device).to(torch.bfloat16)
+                                   device=device).to(tdt)
                 if full:
                     dst[layer].index_copy_(0, ids, vals)
                 else:
@@ -344,7 +355,11 @@ def device_inputs(w: Workload | str, seed: int = 0, device="cuda") -> DeviceInpu
 
 
 def host_copy(d: DeviceInputs) -> Inputs:
-    """Bit-exact host copy of device inputs (for the oracle)."""
+    """Bit-exact host copy of device inputs (for the oracle): bf16 as uint16
+    bit patterns, fp16 / fp32 as numpy float16 / float32."""
+    import torch
     def bits(t):
-        return t.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
     return Inputs(d.w, bits(d.q), bits(d.k), bits(d.v), d.layout)
