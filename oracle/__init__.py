@@ -73,6 +73,8 @@ def _load():
     lib.pa_oracle_f64_pairs_window.restype = i32
     lib.pa_oracle_f64_typed.argtypes = common + [i32, i32, i64, p, i32, i32]
     lib.pa_oracle_f64_typed.restype = i32
+    lib.pa_oracle_f64_queries.argtypes = common + [p, i64, i32, i32, i64, p, i32, i32]
+    lib.pa_oracle_f64_queries.restype = i32
     lib.pa_oracle_decode.argtypes = [p, i32, i64, p]
     lib.pa_oracle_decode.restype = i32
     lib.pa_oracle_num_mutants.argtypes = []
@@ -172,6 +174,38 @@ def attention_pairs(q, k_cache, v_cache, block_tables, context_lens, scale,
         _ptr(q), qst[0], qst[1], _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], NP,
         _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale),
         int(window), _ptr(pairs), pairs.shape[0], _ptr(out), n)
+    if rc != 0:
+        raise OracleError(f"oracle returned {rc}")
+    return out
+
+
+def attention_queries(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                      num_kv_heads, threads: int | None = None, mutant: int = 0, window: int = 0):
+    """Several queries per sequence (chunked prefill): q [n_rows, Hq, D] holds
+    sequence b's queries at rows [query_start[b], query_start[b+1]), which are
+    its last tokens; query i attends causally to positions up to its own.
+    Returns fp64 [n_rows, Hq, D]."""
+    lib = _load()
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    ctx_arr = np.asarray(context_lens)
+    B = len(ctx_arr)
+    if qs.shape != (B + 1,):
+        raise OracleError("query_start must have B + 1 entries")
+    q = np.asarray(q)
+    # the shape checks of _prep, on a [B, Hq, D] view of the first rows
+    # (only the pools, tables and head geometry are taken from it)
+    probe = np.broadcast_to(q[:1], (B,) + q.shape[1:]) if q.shape[0] else np.zeros((B,) + q.shape[1:], q.dtype)
+    _, bt, ctx, (_, Hq, D, NP, P, Hkv), st, _ = _prep(
+        np.ascontiguousarray(probe), k_cache, v_cache, block_tables, context_lens, num_kv_heads)
+    if q.ndim != 3 or q.strides[2] != q.itemsize:
+        raise OracleError("q must be [n_rows, Hq, D] with contiguous D")
+    qst = [s // q.itemsize for s in q.strides[:2]]
+    out = np.zeros((q.shape[0], Hq, D), dtype=np.float64)
+    n = threads or default_threads()
+    rc = lib.pa_oracle_f64_queries(
+        _ptr(q), qst[0], qst[1], _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], NP,
+        _ptr(bt), bt.shape[1], _ptr(ctx), B, Hq, Hkv, D, P, ctypes.c_float(scale),
+        _ptr(qs), q.shape[0], dtype_code(q), dtype_code(k_cache), int(window), _ptr(out), n, mutant)
     if rc != 0:
         raise OracleError(f"oracle returned {rc}")
     return out

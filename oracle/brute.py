@@ -108,3 +108,37 @@ def exact(q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads,
                     num = ctx.add(num, ctx.multiply(wt, D_(float(vf[pg, sl, g, i]))))
                 out[b, h, i] = float(ctx.divide(num, Z))
     return out
+
+
+def dense_queries(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                  num_kv_heads, window=0):
+    """[n_rows, Hq, D] fp64 for several queries per sequence: dense K/V per
+    sequence, a logits matrix [n, L] with a causal (and window) mask of
+    -inf, and a library softmax over each row."""
+    qf = widen(q)
+    kf = widen(k_cache)
+    vf = widen(v_cache)
+    n_rows, Hq, D = qf.shape
+    P = kf.shape[1]
+    qg = Hq // num_kv_heads
+    s = float(np.float32(scale))
+    out = np.zeros((n_rows, Hq, D))
+    for b in range(len(context_lens)):
+        L = int(context_lens[b])
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        n = r1 - r0
+        if n == 0 or L <= 0:
+            continue
+        Kb = _dense_kv(kf, block_tables[b], L, P)              # [L, Hkv, D]
+        Vb = _dense_kv(vf, block_tables[b], L, P)
+        pos = np.arange(L - n, L)[:, None]                     # [n, 1]
+        t = np.arange(L)[None, :]                              # [1, L]
+        allowed = t <= pos
+        if window > 0:
+            allowed &= t > pos - window
+        for h in range(Hq):
+            g = h // qg
+            logits = (qf[r0:r1, h] @ Kb[:, g, :].T) * s       # [n, L]
+            logits = np.where(allowed, logits, -np.inf)
+            out[r0:r1, h] = softmax(logits, axis=1) @ Vb[:, g, :]
+    return out

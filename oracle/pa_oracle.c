@@ -30,6 +30,13 @@
  * reading: the decode query sits at position L - 1 and sees itself and the
  * W - 1 tokens before it.
  *
+ * Several queries per sequence (chunked prefill; page 1, "Where to look",
+ * names vLLM's chunked-prefill paged-decode path; the pages owe d=128
+ * prefill -- page 2, "Not claimed"): sequence b's n_b query rows are its
+ * last n_b tokens, so query i sits at position pos = L - n_b + i and
+ * attends causally to t in [0, pos] (with a window W: [max(0, pos-W+1),
+ * pos]).  One query per sequence is the decode case above.
+ *
  * Readings where the pages are silent: L == 0 gives an all-zero row; the
  * scale is the fp32 value the caller passes, widened exactly; there is no
  * mask other than the window, no soft-cap and no positional term.  Sums run
@@ -74,6 +81,9 @@ typedef struct {
     double scale;
     int64_t window;                     /* 0 = none, else the last W tokens  */
     int mutant;
+    /* several queries per sequence: rows [qstart[b], qstart[b+1]) of q */
+    const int32_t* qstart;              /* NULL = one query per sequence     */
+    int64_t n_rows;
     /* work list */
     const int32_t* pairs;               /* (b, h) pairs, or NULL = all       */
     int64_t n_items;
@@ -114,11 +124,12 @@ static double elem(const void* base, int64_t idx, int dtype)
     return bf16_bits_to_f64(((const uint16_t*)base)[idx]);
 }
 
-/* One output row o[b][h][0..D) following the definition above. */
-static int attend_row(const orc_args* a, int b, int h, double* o)
+/* One output row o[0..D) following the definition above: query row qoff of
+ * q, head h, attending to tokens [.., L) of sequence b (L = the position of
+ * the query plus one). */
+static int attend(const orc_args* a, int b, int64_t qoff, int64_t L, int h, double* o)
 {
     const int D = a->D;
-    int64_t L = a->ctx[b];
     for (int i = 0; i < D; ++i) o[i] = 0.0;
     if (L <= 0) return ORC_OK;
     if (L > a->max_blk * a->P) return ORC_EINVAL;
@@ -127,11 +138,11 @@ static int attend_row(const orc_args* a, int b, int h, double* o)
     int g = h / qg;
     if (a->mutant == 1) g = h % a->Hkv;            /* wrong head map          */
 
+    if (a->mutant == 10 && a->qstart && L < a->max_blk * a->P) L += 1;   /* sees one token ahead */
     /* first attended token: the window keeps t >= L - W */
     int64_t t0 = (a->window > 0 && L > a->window) ? L - a->window : 0;
     if (a->mutant == 9 && a->window > 0 && L > a->window) t0 += 1;   /* window one short */
 
-    const int64_t qoff = (int64_t)b * a->q_sb + (int64_t)h * a->q_sh;
     double* x = (double*)malloc((size_t)L * sizeof(double));
     int64_t* voff = (int64_t*)malloc((size_t)L * sizeof(int64_t));
     const void** vbase = (const void**)malloc((size_t)L * sizeof(void*));
@@ -160,8 +171,8 @@ static int attend_row(const orc_args* a, int b, int h, double* o)
         if (a->mutant == 4) x[t] = -a->scale * dot;       /* wrong sign      */
     }
 
-    double m = x[t0];
-    for (int64_t t = t0 + 1; t < L; ++t) if (x[t] > m) m = x[t];
+    double m = -INFINITY;
+    for (int64_t t = t0; t < L; ++t) if (x[t] > m) m = x[t];
     double Z = 0.0;
     for (int64_t t = t0; t < L; ++t) {
         x[t] = exp(x[t] - m);                             /* x now holds w_t */
@@ -179,17 +190,41 @@ static int attend_row(const orc_args* a, int b, int h, double* o)
     return ORC_OK;
 }
 
+/* Decode: sequence b's one query q[b][h] over all L_b tokens. */
+static int attend_row(const orc_args* a, int b, int h, double* o)
+{
+    return attend(a, b, (int64_t)b * a->q_sb + (int64_t)h * a->q_sh, a->ctx[b], h, o);
+}
+
+/* Several queries: query row r (of sequence b, found from qstart) over
+ * [.., pos + 1). */
+static int attend_query(const orc_args* a, int64_t r, int h, double* o)
+{
+    int b = 0;
+    while (b < a->B && a->qstart[b + 1] <= r) ++b;
+    if (b >= a->B || r < a->qstart[b]) return ORC_EINVAL;
+    const int64_t n = a->qstart[b + 1] - a->qstart[b];
+    const int64_t pos = (int64_t)a->ctx[b] - n + (r - a->qstart[b]);
+    if (pos < 0) return ORC_EINVAL;                  /* more queries than tokens */
+    return attend(a, b, r * a->q_sb + (int64_t)h * a->q_sh, pos + 1, h, o);
+}
+
 static void* run_slice(void* p)
 {
     orc_slice* s = (orc_slice*)p;
     const orc_args* a = s->a;
     s->status = ORC_OK;
     for (int64_t it = s->begin; it < s->end; ++it) {
-        int b, h;
-        if (a->pairs) { b = a->pairs[2 * it]; h = a->pairs[2 * it + 1]; }
-        else { b = (int)(it / a->Hq); h = (int)(it % a->Hq); }
-        if (b < 0 || b >= a->B || h < 0 || h >= a->Hq) { s->status = ORC_EINVAL; return NULL; }
-        int rc = attend_row(a, b, h, a->out + it * a->D);
+        int rc;
+        if (a->qstart) {
+            rc = attend_query(a, it / a->Hq, (int)(it % a->Hq), a->out + it * a->D);
+        } else {
+            int b, h;
+            if (a->pairs) { b = a->pairs[2 * it]; h = a->pairs[2 * it + 1]; }
+            else { b = (int)(it / a->Hq); h = (int)(it % a->Hq); }
+            if (b < 0 || b >= a->B || h < 0 || h >= a->Hq) { s->status = ORC_EINVAL; return NULL; }
+            rc = attend_row(a, b, h, a->out + it * a->D);
+        }
         if (rc != ORC_OK) { s->status = rc; return NULL; }
     }
     return NULL;
@@ -331,6 +366,36 @@ int pa_oracle_f64_typed(const void* q, int64_t q_sb, int64_t q_sh,
     return run(&a, n_threads);
 }
 
+/* Several queries per sequence: q is [n_rows][Hq][D] with sequence b's
+ * queries at rows [qstart[b], qstart[b+1]) (its last tokens); out is
+ * [n_rows][Hq][D].  Element types, window and mutant as above. */
+int pa_oracle_f64_queries(const void* q, int64_t q_sb, int64_t q_sh,
+                          const void* k, const void* v,
+                          int64_t s_page, int64_t s_slot, int64_t s_head, int64_t num_pages,
+                          const int32_t* bt, int64_t max_blk, const int32_t* ctx,
+                          int B, int Hq, int Hkv, int D, int P, float scale,
+                          const int32_t* qstart, int64_t n_rows,
+                          int q_dtype, int kv_dtype, int64_t window, double* out, int n_threads,
+                          int mutant)
+{
+    orc_args a;
+    if (window < 0 || !qstart || n_rows < 0) return ORC_EINVAL;
+    if (qstart[0] != 0 || qstart[B] != n_rows) return ORC_EINVAL;
+    for (int b = 0; b < B; ++b)
+        if (qstart[b + 1] < qstart[b]) return ORC_EINVAL;
+    fill(&a, q, q_sb, q_sh, k, v, s_page, s_slot, s_head, num_pages, bt, max_blk, ctx,
+         B, Hq, Hkv, D, P, scale);
+    a.q_dtype = q_dtype;
+    a.kv_dtype = kv_dtype;
+    a.qstart = qstart;
+    a.n_rows = n_rows;
+    a.out = out;
+    a.n_items = n_rows * Hq;
+    a.window = window;
+    a.mutant = mutant;
+    return run(&a, n_threads);
+}
+
 /* Decodes of one element type over n bit patterns (tests of the decoder). */
 int pa_oracle_decode(const void* bits, int dtype, int64_t n, double* out)
 {
@@ -376,4 +441,4 @@ int pa_oracle_f64_mutant(const uint16_t* q, int64_t q_sb, int64_t q_sh,
     return run(&a, n_threads);
 }
 
-int pa_oracle_num_mutants(void) { return 9; }
+int pa_oracle_num_mutants(void) { return 10; }

@@ -24,6 +24,10 @@ Each pin follows something the source pages or plain mathematics fix:
   numpy's on all 65536 bit patterns, bf16 equals the bit-shift widening,
   fp16 / fp32 / mixed inputs match the dense brute force, and the same values
   stored as bf16, fp16 or fp32 give bit-identical results;
+* several queries per sequence (chunked prefill, causal): the dense brute
+  force with a causal mask matrix; one query per sequence is the decode
+  result bit for bit, and so is the last query of every chunk; reordering
+  the sequences reorders the rows and nothing else;
 * KV-cache append writes exactly the newest token's K/V rows: every other
   byte is unchanged, the rows read back through the block table, and
   appending into a fresh one-token sequence makes attention return v_new;
@@ -388,6 +392,79 @@ def test_same_values_in_every_storage_type_give_identical_bits():
 
 
 # --------------------------------------------------------------------------
+# several queries per sequence (chunked prefill)
+# --------------------------------------------------------------------------
+def query_case(rng, lens, chunks, Hq=8, Hkv=2, D=32, P=4, dtype=np.uint16):
+    c = random_case(rng, len(lens), Hq, Hkv, D, P, lens)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = bf16(rng, (int(qs[-1]), Hq, D))
+    return dict(c, q=q), qs
+
+
+def run_queries(c, qs, **kw):
+    return oracle.attention_queries(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                                    c["context_lens"], qs, c["scale"], c["num_kv_heads"], **kw)
+
+
+@pytest.mark.parametrize("W", [0, 3, 40])
+def test_queries_match_dense_causal_bruteforce(W):
+    rng = np.random.default_rng(110 + W)
+    c, qs = query_case(rng, [1, 9, 40, 33, 17], [1, 9, 5, 33, 0])
+    ref = brute.dense_queries(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                              c["context_lens"], qs, c["scale"], c["num_kv_heads"], window=W)
+    assert rel_err(run_queries(c, qs, window=W), ref) <= 1e-12
+
+
+def test_one_query_per_sequence_is_decode():
+    rng = np.random.default_rng(111)
+    c, qs = query_case(rng, [1, 9, 40], [1, 1, 1])
+    assert np.array_equal(run_queries(c, qs), run_oracle(c))
+    assert np.array_equal(run_queries(c, qs, window=5), run_oracle(c, window=5))
+
+
+def test_last_query_of_each_chunk_is_decode():
+    rng = np.random.default_rng(112)
+    lens, chunks = [12, 40, 7], [12, 6, 3]
+    c, qs = query_case(rng, lens, chunks)
+    out = run_queries(c, qs)
+    last = c["q"][qs[1:] - 1]                       # [B, Hq, D]
+    dec = run_oracle(dict(c, q=np.ascontiguousarray(last)))
+    assert np.array_equal(out[qs[1:] - 1], dec)
+
+
+def test_reordering_sequences_reorders_rows():
+    rng = np.random.default_rng(113)
+    lens, chunks = [12, 40, 7, 20], [4, 6, 3, 1]
+    c, qs = query_case(rng, lens, chunks)
+    out = run_queries(c, qs)
+    perm = [2, 0, 3, 1]
+    rows = np.concatenate([np.arange(qs[b], qs[b + 1]) for b in perm])
+    qs2 = np.concatenate([[0], np.cumsum([chunks[b] for b in perm])]).astype(np.int32)
+    c2 = dict(c, q=np.ascontiguousarray(c["q"][rows]), block_tables=c["block_tables"][perm],
+              context_lens=np.asarray(lens, dtype=np.int32)[perm])
+    assert np.array_equal(run_queries(c2, qs2), out[rows])
+
+
+def test_more_queries_than_tokens_is_an_error():
+    rng = np.random.default_rng(114)
+    c, qs = query_case(rng, [3, 5], [4, 1])
+    with pytest.raises(oracle.OracleError):
+        run_queries(c, qs)
+
+
+def test_causal_mistake_is_caught():
+    rng = np.random.default_rng(115)
+    c, qs = query_case(rng, [20, 33], [8, 5])
+    ref = brute.dense_queries(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                              c["context_lens"], qs, c["scale"], c["num_kv_heads"])
+    try:
+        out = run_queries(c, qs, mutant=10)
+    except oracle.OracleError:
+        return
+    assert rel_err(out, ref) > 1e-6
+
+
+# --------------------------------------------------------------------------
 # KV-cache append
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("P", [1, 7, 16])
@@ -450,6 +527,8 @@ def test_every_planted_mistake_is_caught(window):
     for m in range(1, oracle.num_mutants() + 1):
         if m == 9 and not window:
             continue                        # the window mistake needs a window
+        if m == 10:
+            continue                        # the causal mistake needs several queries (own test)
         try:
             out = run_oracle(c, mutant=m, window=window)
         except oracle.OracleError:
