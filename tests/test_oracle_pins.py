@@ -555,6 +555,22 @@ def test_comparator_selftest_matches_pages():
     assert not gross.ok()
 
 
+def test_comparator_quantization_bound_elements():
+    """|r| >= 4: the correctly rounded bf16 value may be more than 1e-2 away
+    (r = -4.11025..., nearest bf16 -4.125); within one ULP it passes, two
+    ULPs off it fails.  Below 4 the 1e-2 bar stays."""
+    from oracle.compare import compare, f64_to_bf16_bits, bump_ulp
+    r = np.array([-4.110250183701639, 0.5, -1.25, 3.0])
+    y = f64_to_bf16_bits(r)
+    rep = compare(y, r)
+    assert rep.n_big == 1 and rep.max_abs > 1e-2 and rep.big_ulps <= 1.0 and rep.ok()
+    y2 = bump_ulp(y, [0], 2)
+    assert not compare(y2, r).ok()
+    y3 = y.copy()
+    y3[1] = f64_to_bf16_bits(np.array([0.5 + 0.02]))[0]      # 0.02 off where |r| < 4
+    assert not compare(y3, r).ok()
+
+
 def test_comparator_on_fp16_and_fp32_outputs():
     """The pages' self-test shape on binary16 and binary32 outputs: exact
     copies are 100% bitwise, three 1-ULP changes in 2048 give 99.8535%."""
