@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "paged-attn decode µs/call + achieved KV-read GB/s (% of MI355X HBM peak)"
 
@@ -253,6 +254,36 @@ def append_line(pa, torch, workloads_mod, name="long_ctx_gqa8"):
     return entry
 
 
+def prefill_line(pa, torch, workloads_mod, B=8, ctx=4096, chunk=512, Hq=32, Hkv=8, D=128, P=16):
+    """Several queries per sequence: B sequences of ctx tokens whose last
+    chunk tokens are queried (chunked prefill).  Graph-timed microseconds
+    per call, attention FLOPs (4 D Hq per query per attended token) as
+    TFLOP/s against the dense bf16 MFMA peak."""
+    import numpy as np
+    w = workloads_mod.custom("prefill_chunks", batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                             page_size=P, ctx=(ctx,) * B)
+    inp = workloads_mod.make_inputs(w, seed=0)
+    d = workloads_mod.to_device(inp)
+    rows = B * chunk
+    q = torch.randn((rows, Hq, D), device="cuda").to(torch.bfloat16)
+    qs = torch.arange(0, rows + 1, chunk, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    k, v = d.k[0], d.v[0]
+    calls = [lambda: pa.prefill(q, k, v, d.block_tables, d.context_lens, qs, w.scale, out=out)] * 16
+    us = graph_time_us(calls, 20, torch)
+    attended = B * (chunk * (ctx - chunk) + chunk * (chunk + 1) // 2)
+    flops = 4 * D * Hq * attended
+    tflops = flops / (us * 1e-6) / 1e12
+    entry = {"workload": f"{B} seqs x ctx {ctx}, last {chunk} tokens queried, Hq{Hq}/Hkv{Hkv}, d{D}, page {P}",
+             "us_per_call": round(us, 2), "flops_per_call": flops, "TFLOPs": round(tflops, 1),
+             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "kernel": "pa_prefill_mfma_kernel",
+             "partitions": int(pa.pa_get_stats()["last_num_partitions"])}
+    log(f"[prefill] {entry}")
+    del d
+    torch.cuda.empty_cache()
+    return entry
+
+
 def cpu_baseline(d, w, target_s, workloads_mod):
     """The oracle as it stands, on the host cores, over whole sequences of the
     same workload (all query heads) until about target_s seconds."""
@@ -398,6 +429,7 @@ def main():
     if not args.profile and not args.no_per_config:
         result["per_config"] = per_config(pa, knobs, torch, wl)
         result["append"] = append_line(pa, torch, wl)
+        result["prefill"] = prefill_line(pa, torch, wl)
     if not args.profile and not args.no_cpu_baseline:
         t = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds, wl)

@@ -245,6 +245,56 @@ int pa_check_args(const pa_tensor* q,
                   const pa_tensor* out,
                   const pa_opts* opts);
 
+/*
+ * pa_prefill -- several queries per sequence: chunked prefill, or a batch
+ * that mixes prefill chunks with decode steps.  (The pages name vLLM's
+ * chunked-prefill paged-decode path -- page 1, issue "ROCm gfx1200:
+ * PagedAttnOnline is 8.1x slower per call", section "Where to look" -- and
+ * owe d=128 prefill -- page 2, PR "head_dim=128 decode arm", "Not
+ * claimed".)
+ *
+ *  q             [R, Hq, D]       the query rows of all sequences, bf16, fp16
+ *                                 or fp32; sequence b's rows are
+ *                                 [query_start[b], query_start[b+1]).
+ *  query_start   [B + 1] int32    0 = query_start[0] <= ... <= query_start[B] = R.
+ *  k_cache, v_cache, block_tables [B, MaxBlk], context_lens [B]: as in
+ *                pa_decode; context_lens already count the queried tokens.
+ *  out           [R, Hq, D]       bf16, fp16 or fp32.
+ *  opts          may be NULL; window and partition_tokens apply; the variant
+ *                must be automatic or MFMA and the schedule not balanced.
+ *
+ * Sequence b's n_b = query_start[b+1] - query_start[b] queries are its last
+ * n_b tokens: query i sits at position pos = L_b - n_b + i and attends to the
+ * tokens [0, pos] (with a window W: [max(0, pos - W + 1), pos]).  n_b = 1 is
+ * the decode of pa_decode.  Runs on the matrix cores only: head_dim 128 or
+ * 256 and a bf16 or fp16 cache (else PA_ENOTSUP), at most 4096 sequences.
+ * Device-side preconditions, not checked on the host: query_start as above
+ * and n_b <= L_b (a query at a negative position gives zeros).  Workspace
+ * rules as in pa_decode_ex (workspace NULL = the library's own).
+ */
+int pa_prefill(const pa_tensor* q,
+               const pa_tensor* k_cache,
+               const pa_tensor* v_cache,
+               const pa_tensor* block_tables,
+               const pa_tensor* context_lens,
+               const pa_tensor* query_start,
+               float scale,
+               int num_q_heads,
+               int num_kv_heads,
+               int head_dim,
+               int page_size,
+               const pa_tensor* out,
+               void* stream,
+               const pa_opts* opts,
+               void* workspace,
+               size_t workspace_bytes);
+
+/* Bytes of workspace pa_prefill needs for num_rows query rows over num_seqs
+ * sequences (0 when the call does not split; 0 on bad arguments). */
+size_t pa_prefill_workspace_bytes(int64_t num_rows, int64_t num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int64_t max_blocks_per_seq,
+                                  int page_size, const pa_opts* opts);
+
 /* ----------------------------------------------------- introspection */
 /* Launch counters since load or the last pa_reset_stats (process-wide). */
 typedef struct pa_stats {
@@ -261,6 +311,7 @@ typedef struct pa_stats {
     uint64_t balanced_calls;        /* calls run on the balanced schedule      */
     uint64_t last_schedule;         /* PA_SCHEDULE_* of the last call          */
     uint64_t append_launches;       /* pa_cache_append kernel launches         */
+    uint64_t prefill_launches;      /* pa_prefill kernel launches              */
 } pa_stats;
 
 int  pa_get_stats(pa_stats* stats);   /* PA_EINVAL if stats is NULL            */

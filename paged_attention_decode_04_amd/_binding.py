@@ -39,7 +39,7 @@ class PaStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
         "last_partition_tokens", "last_num_partitions", "last_variant", "balanced_calls",
-        "last_schedule", "append_launches")]
+        "last_schedule", "append_launches", "prefill_launches")]
 
 
 class PaError(RuntimeError):
@@ -84,6 +84,14 @@ def _load() -> ctypes.CDLL:
     lib.pa_cache_append.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p]
     lib.pa_cache_append.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [T, T, T, T, T, T, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, T, ctypes.c_void_p, ctypes.POINTER(PaOpts), ctypes.c_void_p,
+                               ctypes.c_size_t]
+    lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_prefill_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.POINTER(PaOpts)]
+    lib.pa_prefill_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -198,6 +206,54 @@ def cache_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, str
     """KV-cache append on torch tensors; sizes come from the shapes."""
     NP, P, Hkv, D = k_cache.shape
     pa_cache_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, Hkv, D, P, stream)
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, num_q_heads,
+               num_kv_heads, head_dim, page_size, out, stream=None, opts: PaOpts | None = None,
+               workspace=None):
+    """C ``pa_prefill``; ``workspace`` is a torch uint8 tensor or None."""
+    import torch
+    _require_device(q, k_cache, v_cache, block_tables, context_lens, query_start, out)
+    with torch.cuda.device(q.device):
+        rc = LIB.pa_prefill(tensor_desc(q), tensor_desc(k_cache), tensor_desc(v_cache),
+                            tensor_desc(block_tables), tensor_desc(context_lens),
+                            tensor_desc(query_start), float(scale), num_q_heads, num_kv_heads,
+                            head_dim, page_size, tensor_desc(out), _stream_handle(stream, q.device),
+                            ctypes.byref(opts) if opts else None,
+                            workspace.data_ptr() if workspace is not None else None,
+                            workspace.numel() if workspace is not None else 0)
+    _check(rc, "pa_prefill")
+    return out
+
+
+def pa_prefill_workspace_bytes(num_rows, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               max_blocks_per_seq, page_size, opts: PaOpts | None = None) -> int:
+    return int(LIB.pa_prefill_workspace_bytes(num_rows, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              max_blocks_per_seq, page_size,
+                                              ctypes.byref(opts) if opts else None))
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale=None, out=None, *,
+            window: int = 0, partition_tokens: int = 0, workspace=None, stream=None, out_dtype=None):
+    """Several queries per sequence on torch tensors: q [R, Hq, D] holds
+    sequence b's queries at rows [query_start[b], query_start[b+1]) (its last
+    tokens, attending causally).  Returns out [R, Hq, D]."""
+    import torch
+    R, Hq, D = q.shape
+    NP, P, Hkv, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    opts = make_opts("auto", partition_tokens, "auto", 0, window)
+    if workspace is None:
+        n = pa_prefill_workspace_bytes(R, block_tables.shape[0], Hq, Hkv, D, block_tables.shape[1], P, opts)
+        if n:
+            workspace = torch.zeros(n + 256, dtype=torch.uint8, device=q.device)
+            off = (-workspace.data_ptr()) % 256
+            workspace = workspace[off:off + n]
+    return pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, Hq, Hkv, D, P,
+                      out, stream, opts, workspace)
 
 
 def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

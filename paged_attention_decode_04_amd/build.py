@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpa_decode.so")
-SOURCES = ["pa_api.hip", "pa_valu.hip", "pa_mfma.hip", "pa_append.hip"]
+SOURCES = ["pa_api.hip", "pa_valu.hip", "pa_mfma.hip", "pa_append.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -35,7 +35,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 struct Counters {
-    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0}, lean{0}, append{0};
+    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0}, lean{0}, append{0}, prefill{0};
     std::atomic<uint64_t> last_t{0}, last_np{0}, last_variant{0}, last_schedule{0};
 } g_stats;
 
@@ -493,9 +493,223 @@ int validate_append(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* k
     return PA_OK;
 }
 
+// ---------------------------------------------------------------- several queries
+struct PrefillPlan {
+    int n_slots;        // query-block slots (an upper bound on the blocks)
+    int part_tokens;
+    int n_part;
+    bool split;
+    size_t ws_bytes, o_offset, lse_offset;
+};
+
+int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* bt,
+                     const pa_tensor* ctx, const pa_tensor* qs, float scale, int num_q_heads,
+                     int num_kv_heads, int head_dim, int page_size, const pa_tensor* out,
+                     const pa_opts* opts, Geometry& geo, int64_t& rows) {
+    int rc;
+    if ((rc = check_tensor(q, "q", kAnyFloat, 3))) return rc;
+    if ((rc = check_tensor(k, "k_cache", kAnyFloat, 4))) return rc;
+    if ((rc = check_tensor(v, "v_cache", kAnyFloat, 4))) return rc;
+    if ((rc = check_tensor(bt, "block_tables", PA_DTYPE_INT32, 2))) return rc;
+    if ((rc = check_tensor(ctx, "context_lens", PA_DTYPE_INT32, 1))) return rc;
+    if ((rc = check_tensor(qs, "query_start", PA_DTYPE_INT32, 1))) return rc;
+    if ((rc = check_tensor(out, "out", kAnyFloat, 3))) return rc;
+    if (k->dtype != v->dtype) return fail(PA_EINVAL, "k_cache and v_cache element types differ");
+    if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+    if (page_size < 1) return fail(PA_EINVAL, "page_size %d < 1", page_size);
+    if (num_q_heads < 1 || num_kv_heads < 1) return fail(PA_EINVAL, "head counts must be >= 1");
+    if (num_q_heads % num_kv_heads)
+        return fail(PA_EINVAL, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
+    rows = q->shape[0];
+    const int64_t B = bt->shape[0];
+    if (q->shape[1] != num_q_heads || q->shape[2] != head_dim)
+        return fail(PA_EINVAL, "q shape does not match Hq=%d, D=%d", num_q_heads, head_dim);
+    for (int i = 0; i < 4; ++i)
+        if (k->shape[i] != v->shape[i]) return fail(PA_EINVAL, "k_cache and v_cache shapes differ");
+    if (k->shape[1] != page_size || k->shape[2] != num_kv_heads || k->shape[3] != head_dim)
+        return fail(PA_EINVAL, "k_cache shape does not match P=%d, Hkv=%d, D=%d", page_size, num_kv_heads,
+                    head_dim);
+    if (ctx->shape[0] != B) return fail(PA_EINVAL, "context_lens has %lld entries, block_tables %lld rows",
+                                        (long long)ctx->shape[0], (long long)B);
+    if (qs->shape[0] != B + 1) return fail(PA_EINVAL, "query_start has %lld entries, %lld expected",
+                                           (long long)qs->shape[0], (long long)(B + 1));
+    if (out->shape[0] != rows || out->shape[1] != num_q_heads || out->shape[2] != head_dim)
+        return fail(PA_EINVAL, "out shape does not match q");
+    if (opts) {
+        for (int i = 0; i < 3; ++i)
+            if (opts->reserved[i]) return fail(PA_EINVAL, "pa_opts.reserved must be zero");
+        if (opts->variant != PA_VARIANT_AUTO && opts->variant != PA_VARIANT_MFMA)
+            return fail(PA_ENOTSUP, "several-query attention runs on the MFMA kernel only");
+        if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
+        if (opts->schedule == PA_SCHEDULE_BALANCED)
+            return fail(PA_ENOTSUP, "several-query attention uses the partition schedule");
+        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_BALANCED)
+            return fail(PA_EINVAL, "unknown schedule %d", opts->schedule);
+        if (opts->shares != 0) return fail(PA_EINVAL, "shares apply to the balanced schedule only");
+        if (opts->window < 0) return fail(PA_EINVAL, "window %d < 0", opts->window);
+    }
+    const int qg = num_q_heads / num_kv_heads;
+    if (qg != 1 && qg != 2 && qg != 4 && qg != 8 && qg != 16)
+        return fail(PA_ENOTSUP, "Hq/Hkv = %d (supported: 1, 2, 4, 8, 16)", qg);
+    if (!pa::mfma_supported(head_dim, 16, k->dtype))
+        return fail(PA_ENOTSUP, "several-query attention needs head_dim 128/256 and a bf16 or fp16 cache");
+    if (B > kLeanMaxBatch) return fail(PA_ENOTSUP, "batch %lld > %d", (long long)B, kLeanMaxBatch);
+    if (rows > INT32_MAX / 4) return fail(PA_ENOTSUP, "too many query rows");
+    if (bt->shape[1] > (int64_t)1 << 24 || (int64_t)bt->shape[1] * page_size > INT32_MAX / 2)
+        return fail(PA_ENOTSUP, "block table too wide");
+    if (k->shape[0] > INT32_MAX) return fail(PA_ENOTSUP, "pool too large");
+    if ((rc = check_rows16(q, "q", 2))) return rc;
+    if ((rc = check_rows16(k, "k_cache", 3))) return rc;
+    if ((rc = check_rows16(v, "v_cache", 3))) return rc;
+    if ((rc = check_rows16(out, "out", 2))) return rc;
+    if ((reinterpret_cast<uintptr_t>(bt->data) & 3u) || (reinterpret_cast<uintptr_t>(ctx->data) & 3u) ||
+        (reinterpret_cast<uintptr_t>(qs->data) & 3u))
+        return fail(PA_EALIGN, "block_tables / context_lens / query_start not 4-byte aligned");
+    if (B > 0 && bt->shape[1] > 1 && bt->stride[1] != 1)
+        return fail(PA_EINVAL, "block_tables: innermost stride must be 1");
+    geo = Geometry{B, num_q_heads, num_kv_heads, head_dim, page_size, k->shape[0], bt->shape[1], qg,
+                   q->dtype, k->dtype, out->dtype};
+    return PA_OK;
+}
+
+PrefillPlan plan_prefill(const Geometry& g, int64_t rows, const pa_opts* opts) {
+    PrefillPlan pl{};
+    const int qt = 16 / g.qg;
+    pl.n_slots = (int)((rows + qt - 1) / qt + g.B);
+    // Span of one block's work: the whole table, or with a window W the
+    // block's W + qt - 1 attended tokens from a 16-token tile boundary.
+    int64_t span = std::max<int64_t>(g.max_blk * g.P, 1);
+    if (opts && opts->window > 0) span = std::min<int64_t>(span, (int64_t)opts->window + qt + 15);
+    const int64_t blocks = (int64_t)pl.n_slots * g.Hkv;
+    int64_t T;
+    if (opts && opts->partition_tokens > 0) {
+        T = (opts->partition_tokens + 63) / 64 * 64;
+    } else if (blocks >= 256) {
+        T = span;                               // enough query blocks to fill the chip: no split
+    } else {
+        T = (span * blocks + 255) / 256;
+        T = std::max<int64_t>(256, std::min<int64_t>(T, 4096));
+        T = (T + 63) / 64 * 64;
+    }
+    if (T >= span) T = span;
+    pl.part_tokens = (int)T;
+    pl.n_part = (int)((span + T - 1) / T);
+    pl.split = pl.n_part > 1;
+    if (pl.split) {
+        const size_t n = (size_t)rows * g.Hq * pl.n_part;
+        pl.o_offset = pa::kLeanCounterBytes;
+        pl.lse_offset = pl.o_offset + align_up(n * g.D * sizeof(float), kAlign);
+        pl.ws_bytes = pl.lse_offset + align_up(n * sizeof(float), kAlign);
+    }
+    return pl;
+}
+
+int prefill_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* bt,
+                 const pa_tensor* ctx, const pa_tensor* qs, float scale, int num_q_heads, int num_kv_heads,
+                 int head_dim, int page_size, const pa_tensor* out, void* stream, const pa_opts* opts,
+                 void* workspace, size_t workspace_bytes) {
+    t_err.clear();
+    Geometry g;
+    int64_t rows = 0;
+    int rc = validate_prefill(q, k, v, bt, ctx, qs, scale, num_q_heads, num_kv_heads, head_dim, page_size, out,
+                              opts, g, rows);
+    if (rc) return rc;
+    const PrefillPlan pl = plan_prefill(g, rows, opts);
+    if ((int64_t)pl.n_slots * g.Hkv * pl.n_part > INT32_MAX) return fail(PA_ENOTSUP, "grid too large");
+    if (rows == 0 || g.B == 0) return PA_OK;
+    int ndev = 0, dev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(PA_ENODEV, "no HIP device");
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ENODEV, "hipGetDevice: %s", hipGetErrorString(e));
+    void* ws = nullptr;
+    if (pl.split) {
+        if (workspace) {
+            if (workspace_bytes < pl.ws_bytes)
+                return fail(PA_ENOMEM, "workspace of %zu bytes, %zu needed", workspace_bytes, pl.ws_bytes);
+            if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+                return fail(PA_EALIGN, "workspace not %zu-byte aligned", kAlign);
+            ws = workspace;
+        } else {
+            rc = library_workspace(dev, pl.ws_bytes, &ws);
+            if (rc) return rc;
+        }
+    }
+    pa::DecodeParams p{};
+    p.q = q->data;
+    p.q_dtype = g.q_dtype;
+    p.out_dtype = g.out_dtype;
+    p.q_sb = q->stride[0];
+    p.q_sh = q->stride[1];
+    p.k = k->data;
+    p.k_sp = k->stride[0];
+    p.k_ss = k->stride[1];
+    p.k_sh = k->stride[2];
+    p.v = v->data;
+    p.v_sp = v->stride[0];
+    p.v_ss = v->stride[1];
+    p.v_sh = v->stride[2];
+    p.bt = static_cast<const int32_t*>(bt->data);
+    p.bt_sb = bt->stride[0];
+    p.ctx = static_cast<const int32_t*>(ctx->data);
+    p.qstart = static_cast<const int32_t*>(qs->data);
+    p.q_rows = (int)rows;
+    p.n_slots = pl.n_slots;
+    p.out = out->data;
+    p.o_sb = out->stride[0];
+    p.o_sh = out->stride[1];
+    p.part_o = pl.split ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.o_offset) : nullptr;
+    p.part_lse = pl.split ? reinterpret_cast<float*>(static_cast<char*>(ws) + pl.lse_offset) : nullptr;
+    p.B = (int)g.B;
+    p.Hq = (int)g.Hq;
+    p.Hkv = (int)g.Hkv;
+    p.P = (int)g.P;
+    p.p_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((int64_t)1 << sh == g.P) p.p_shift = sh;
+    p.max_blk = (int)g.max_blk;
+    p.num_pages = (int)std::max<int64_t>(g.NP, 1);
+    p.part_tokens = pl.part_tokens;
+    p.n_part = pl.n_part;
+    p.qw = 16;
+    p.lean_page_slots = pa::lean_page_slots(p.P);
+    p.window = opts ? opts->window : 0;
+    p.scale_log2 = scale * pa::kLog2e;
+    e = pa::launch_prefill(p, (int)g.D, g.kv_dtype, pl.split, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_EHIP, "several-query launch: %s", hipGetErrorString(e));
+    g_stats.prefill++;
+    if (pl.split) g_stats.merge++;
+    g_stats.last_t = (uint64_t)pl.part_tokens;
+    g_stats.last_np = (uint64_t)pl.n_part;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int pa_prefill(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+               const pa_tensor* block_tables, const pa_tensor* context_lens, const pa_tensor* query_start,
+               float scale, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+               const pa_tensor* out, void* stream, const pa_opts* opts, void* workspace,
+               size_t workspace_bytes) {
+    return prefill_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, num_q_heads,
+                        num_kv_heads, head_dim, page_size, out, stream, opts, workspace, workspace_bytes);
+}
+
+size_t pa_prefill_workspace_bytes(int64_t num_rows, int64_t num_seqs, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int64_t max_blocks_per_seq, int page_size,
+                                  const pa_opts* opts) {
+    if (num_rows < 0 || num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads ||
+        head_dim < 1 || max_blocks_per_seq < 0 || page_size < 1)
+        return 0;
+    const int qg = num_q_heads / num_kv_heads;
+    if (16 % qg) return 0;
+    if (opts && (opts->partition_tokens < 0 || opts->window < 0)) return 0;
+    Geometry g{num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, 1, max_blocks_per_seq, qg,
+               PA_DTYPE_BF16, PA_DTYPE_BF16, PA_DTYPE_BF16};
+    return plan_prefill(g, num_rows, opts).ws_bytes;
+}
+
 
 int pa_cache_append(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* k_cache,
                     const pa_tensor* v_cache, const pa_tensor* block_tables,
@@ -604,6 +818,7 @@ int pa_get_stats(pa_stats* s) {
     s->last_variant = g_stats.last_variant;
     s->balanced_calls = g_stats.lean;
     s->append_launches = g_stats.append;
+    s->prefill_launches = g_stats.prefill;
     s->last_schedule = g_stats.last_schedule;
     return PA_OK;
 }
@@ -616,6 +831,7 @@ void pa_reset_stats(void) {
     g_stats.merge = 0;
     g_stats.lean = 0;
     g_stats.append = 0;
+    g_stats.prefill = 0;
     g_stats.last_schedule = 0;
     g_stats.last_t = 0;
     g_stats.last_np = 0;

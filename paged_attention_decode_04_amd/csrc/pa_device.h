@@ -31,6 +31,9 @@ struct DecodeParams {
     int*  lean_ctr;                                         // balanced schedule: next unit, finished WGs
     int   lean_page_slots;                                  // balanced schedule: page-id LDS entries
     int   window;                                           // 0 = none, else the last `window` tokens
+    const int32_t* qstart;                                  // several queries: rows of sequence b [B + 1]
+    int   q_rows;                                           // several queries: rows of q and out
+    int   n_slots;                                          // several queries: query-block slots in the grid
     float scale_log2;                                       // scale * log2(e)
 };
 

@@ -42,6 +42,10 @@ constexpr int kLeanDynMinPerWg = 256;
 // Workspace: two int counters at its start, zero between calls.
 constexpr int kLeanCounterBytes = 256;
 
+// Several queries per sequence (MFMA, 16-column query blocks), followed by
+// the per-row merge when split.
+hipError_t launch_prefill(const DecodeParams& p, int head_dim, int kv_dtype, bool split, hipStream_t s);
+
 // KV-cache append (one workgroup per sequence).
 hipError_t launch_append(const AppendParams& a, hipStream_t s);
 

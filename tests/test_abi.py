@@ -247,7 +247,7 @@ def test_stats_roundtrip():
     assert s["calls"] == 0 and s["valu_launches"] == 0
     assert set(s) == {"calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
                       "last_partition_tokens", "last_num_partitions", "last_variant",
-                      "balanced_calls", "last_schedule", "append_launches"}
+                      "balanced_calls", "last_schedule", "append_launches", "prefill_launches"}
 
 
 # ------------------------------------------------------------------ KV-cache append
@@ -307,3 +307,52 @@ def test_missing_library_fails_loudly_at_first_use(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding._Library, "_lib", None)
     with pytest.raises(ImportError):
         pa.version()
+
+
+# ------------------------------------------------------------------ several queries per sequence
+def prefill_args(R=6, B=2, Hq=16, Hkv=8, D=128, P=16, NP=8, maxblk=4, kv=torch.bfloat16):
+    q = torch.zeros(R, Hq, D, dtype=torch.bfloat16)
+    k = torch.zeros(NP, P, Hkv, D, dtype=kv)
+    v = torch.zeros(NP, P, Hkv, D, dtype=kv)
+    bt = torch.zeros(B, maxblk, dtype=torch.int32)
+    ctx = torch.full((B,), 10, dtype=torch.int32)
+    qs = torch.tensor([0, 4, R][:B + 1] if B == 2 else list(range(B)) + [R], dtype=torch.int32)
+    out = torch.zeros(R, Hq, D, dtype=torch.bfloat16)
+    return [q, k, v, bt, ctx, qs], out, (Hq, Hkv, D, P)
+
+
+def call_prefill(ts, out, dims, opts=None, scale=0.1):
+    T = _binding.tensor_desc
+    return _binding.LIB.pa_prefill(*[T(t) if t is not None else None for t in ts], scale, *dims, T(out),
+                                   None, opts, None, 0)
+
+
+def test_prefill_validation():
+    ts, out, dims = prefill_args()
+    if not torch.cuda.is_available():
+        assert call_prefill(ts, out, dims) == pa.PA_ENODEV        # valid, no device here
+    bad = list(ts); bad[5] = torch.tensor([0, 6], dtype=torch.int32)   # needs B + 1 entries
+    assert call_prefill(bad, out, dims) == pa.PA_EINVAL
+    assert call_prefill(ts, torch.zeros(5, 16, 128, dtype=torch.bfloat16), dims) == pa.PA_EINVAL
+    ts2, out2, dims2 = prefill_args(kv=torch.float32)
+    assert call_prefill(ts2, out2, dims2) == pa.PA_ENOTSUP      # fp32 cache: no MFMA path
+    ts3, out3, dims3 = prefill_args(Hq=16, Hkv=16, D=512)
+    assert call_prefill(ts3, out3, dims3) == pa.PA_ENOTSUP
+    assert call_prefill(ts, out, dims, pa.make_opts("valu")) == pa.PA_ENOTSUP
+    assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, "balanced")) == pa.PA_ENOTSUP
+    assert call_prefill(ts, out, dims, pa.make_opts(window=-2)) == pa.PA_EINVAL
+    ts4, out4, dims4 = prefill_args(R=0, B=2)
+    ts4[5] = torch.zeros(3, dtype=torch.int32)
+    assert call_prefill(ts4, out4, dims4) == pa.PA_OK           # no rows: nothing to do
+
+
+def test_prefill_workspace_bytes():
+    rnd = lambda x: (x + 255) // 256 * 256
+    # 4 sequences x 1 query (decode-like): 4 + 4 slots x 8 KV heads = 64 blocks
+    # -> split: T = clamp(1024 * 64 / 256 = 256) = 256 -> 4 partitions
+    n = pa.pa_prefill_workspace_bytes(4, 4, 16, 8, 128, 64, 16, None)
+    parts = 4
+    assert n == 256 + rnd(4 * 16 * parts * 128 * 4) + rnd(4 * 16 * parts * 4)
+    # many query rows: enough blocks, no split
+    assert pa.pa_prefill_workspace_bytes(4096, 4, 16, 8, 128, 64, 16, None) == 0
+    assert pa.pa_prefill_workspace_bytes(4, 4, 12, 8, 128, 64, 16, None) == 0   # Hq % Hkv

@@ -199,7 +199,7 @@ def test_analysis_catches_cross_lane_op_in_region():
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("src", ["pa_mfma.hip", "pa_valu.hip"])
+@pytest.mark.parametrize("src", ["pa_mfma.hip", "pa_valu.hip", "pa_prefill.hip", "pa_append.hip"])
 def test_no_cross_lane_ops_under_divergent_exec(src, tmp_path):
     from paged_attention_decode_04_amd import build
     out = tmp_path / "k.s"

@@ -602,3 +602,89 @@ def test_append_typed_caches_bitwise(kt):
     torch.cuda.synchronize()
     assert np.array_equal(k.cpu().numpy().view(np.uint8), k_ref.view(np.uint8))
     assert np.array_equal(v.cpu().numpy().view(np.uint8), v_ref.view(np.uint8))
+
+
+# ------------------------------------------------------------------ several queries per sequence
+def queries_case(lens, chunks, Hq, Hkv, D, P, dtype="bf16", q_dtype=None, seed=0):
+    w = custom(batch=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P, ctx=lens)
+    inp = make_inputs(w, seed=seed, poison_unused=True, dtype=dtype)
+    rng = np.random.default_rng(seed + 1)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = workloads.encode(rng.standard_normal((int(qs[-1]), Hq, D)).astype(np.float32), q_dtype or dtype)
+    return inp, q, qs
+
+
+def to_torch(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def prefill_run(d, q, qs, out_dtype=None, **kw):
+    qd = to_torch(q)
+    out = torch.full(qd.shape, float("nan"), dtype=out_dtype or qd.dtype, device="cuda")
+    pa.pa_reset_stats()
+    pa.prefill(qd, d.k[0], d.v[0], d.block_tables, d.context_lens, torch.from_numpy(qs).cuda(),
+               d.w.scale, out=out, **kw)
+    torch.cuda.synchronize()
+    s = pa.pa_get_stats()
+    assert s["prefill_launches"] == 1, s
+    return host_out(out), s
+
+
+def oracle_queries(inp, q, qs, window=0):
+    return oracle.attention_queries(q, inp.k[0], inp.v[0], inp.block_tables, inp.context_lens, qs,
+                                    inp.w.scale, inp.w.num_kv_heads, window=window)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 16), (128, 32, 2, 16), (256, 8, 2, 32),
+                                        (128, 16, 16, 16), (128, 16, 1, 7)])
+def test_prefill_parity(D, Hq, Hkv, P):
+    """A batch mixing whole-prompt prefill, chunked prefill and decode steps:
+    every query row against the causal oracle, split and unsplit, with and
+    without a window; unused pool slots are NaN."""
+    lens = (1, 17, 40, 300, 1000, 2500)
+    chunks = (1, 17, 1, 100, 64, 33)
+    inp, q, qs = queries_case(lens, chunks, Hq, Hkv, D, P, seed=D + Hq + P)
+    d = to_device(inp)
+    for W in (0, 7, 200):
+        ref = oracle_queries(inp, q, qs, window=W)
+        for T in (0, 64, 1 << 20):
+            y, s = prefill_run(d, q, qs, window=W, partition_tokens=T)
+            assert_parity(y, ref, f"prefill D={D} Hq={Hq} Hkv={Hkv} P={P} W={W} T={T} "
+                                  f"(x{s['last_num_partitions']})")
+
+
+@pytest.mark.parametrize("kt,qt,ot", [("f16", "f16", "f16"), ("bf16", "f32", "f32"), ("f16", "bf16", "f32")])
+def test_prefill_element_types(kt, qt, ot):
+    inp, q, qs = queries_case((64, 900, 33), (64, 40, 1), 16, 4, 128, 16, dtype=kt, q_dtype=qt, seed=5)
+    d = to_device(inp)
+    y, _ = prefill_run(d, q, qs, out_dtype=TORCH_DT[ot])
+    assert_parity(y, oracle_queries(inp, q, qs), f"prefill q {qt} kv {kt} out {ot}")
+
+
+def test_prefill_one_query_per_sequence_matches_decode():
+    """n_b = 1 everywhere is decode: the several-query kernel and the decode
+    kernels agree with the oracle and with each other."""
+    inp = make_inputs("batch16", seed=3)
+    q = inp.q[0]
+    qs = np.arange(inp.w.batch + 1, dtype=np.int32)
+    d = to_device(inp)
+    y, _ = prefill_run(d, q, qs)
+    ref = oracle_run(inp)
+    assert_parity(y, ref, "prefill as decode")
+    yd, _ = gpu_run(d, variant="mfma")
+    r = compare(y, yd)
+    assert r.nmse < 1e-4, r
+
+
+def test_prefill_long_chunk_spare_slots_and_empty_sequences():
+    """A long chunk (many query blocks), empty sequences (no rows), and a
+    sequence with no tokens at all."""
+    lens = (0, 700, 5, 2048)
+    chunks = (0, 700, 0, 512)
+    inp, q, qs = queries_case(lens, chunks, 8, 2, 128, 16, seed=11)
+    d = to_device(inp)
+    y, _ = prefill_run(d, q, qs)
+    assert_parity(y, oracle_queries(inp, q, qs), "long chunks")
