@@ -271,13 +271,26 @@ def prefill_line(pa, torch, workloads_mod, B=8, ctx=4096, chunk=512, Hq=32, Hkv=
     k, v = d.k[0], d.v[0]
     calls = [lambda: pa.prefill(q, k, v, d.block_tables, d.context_lens, qs, w.scale, out=out)] * 16
     us = graph_time_us(calls, 20, torch)
+    st = pa.pa_get_stats()
+    staged = st["last_schedule"] == pa.PA_SCHEDULE_STAGED
+    ws = torch.zeros(pa.pa_prefill_workspace_bytes(rows, B, Hq, Hkv, D, d.block_tables.shape[1], P,
+                                                   pa.make_opts(schedule="partitions")) + 256,
+                     dtype=torch.uint8, device="cuda")
+    calls = [lambda: pa.prefill(q, k, v, d.block_tables, d.context_lens, qs, w.scale, out=out,
+                                schedule="partitions", workspace=ws[:ws.numel() - 256])] * 16
+    us_blocks = graph_time_us(calls, 20, torch)
+    st_blocks = pa.pa_get_stats()
     attended = B * (chunk * (ctx - chunk) + chunk * (chunk + 1) // 2)
     flops = 4 * D * Hq * attended
     tflops = flops / (us * 1e-6) / 1e12
     entry = {"workload": f"{B} seqs x ctx {ctx}, last {chunk} tokens queried, Hq{Hq}/Hkv{Hkv}, d{D}, page {P}",
              "us_per_call": round(us, 2), "flops_per_call": flops, "TFLOPs": round(tflops, 1),
-             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "kernel": "pa_prefill_mfma_kernel",
-             "partitions": int(pa.pa_get_stats()["last_num_partitions"])}
+             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+             "kernel": "pa_prefill_staged_kernel" if staged else "pa_prefill_mfma_kernel",
+             "schedule": "staged" if staged else "partitions",
+             "per_block_kernel": {"kernel": "pa_prefill_mfma_kernel", "us_per_call": round(us_blocks, 2),
+                                  "TFLOPs": round(flops / (us_blocks * 1e-6) / 1e12, 1),
+                                  "partitions": int(st_blocks["last_num_partitions"])}}
     log(f"[prefill] {entry}")
     del d
     torch.cuda.empty_cache()

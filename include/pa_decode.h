@@ -169,6 +169,9 @@ int pa_cache_append(const pa_tensor* k_new,
                                       into one equal static share per
                                       workgroup plus small units taken from a
                                       counter as workgroups finish           */
+#define PA_SCHEDULE_STAGED      3  /* pa_prefill only: a workgroup takes four
+                                      query blocks of one sequence, which share
+                                      every K/V stage through LDS; no split   */
 
 typedef struct pa_opts {
     int32_t variant;            /* PA_VARIANT_*                                */
@@ -261,7 +264,16 @@ int pa_check_args(const pa_tensor* q,
  *                pa_decode; context_lens already count the queried tokens.
  *  out           [R, Hq, D]       bf16, fp16 or fp32.
  *  opts          may be NULL; window and partition_tokens apply; the variant
- *                must be automatic or MFMA and the schedule not balanced.
+ *                must be automatic or MFMA.  Schedules: PARTITIONS = one
+ *                workgroup per query block (16 / qg query tokens times the
+ *                qg heads of a KV head), long contexts split into partitions
+ *                merged by log-sum-exp; STAGED = four consecutive query
+ *                blocks per workgroup share each K/V stage (no split, no
+ *                workspace; partition_tokens must be 0); AUTO takes STAGED
+ *                when partition_tokens is 0, the call has at least two query
+ *                blocks per sequence on average and the staged grid has at
+ *                least 256 workgroups, else PARTITIONS.  BALANCED is
+ *                PA_ENOTSUP.
  *
  * Sequence b's n_b = query_start[b+1] - query_start[b] queries are its last
  * n_b tokens: query i sits at position pos = L_b - n_b + i and attends to the

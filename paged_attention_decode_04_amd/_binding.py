@@ -19,9 +19,9 @@ PA_OK, PA_EINVAL, PA_ENOTSUP, PA_EALIGN, PA_ENODEV, PA_ENOMEM, PA_EHIP = range(7
 PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32, PA_DTYPE_F16 = 1, 2, 3, 4
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 VARIANTS = {"auto": PA_VARIANT_AUTO, "valu": PA_VARIANT_VALU, "mfma": PA_VARIANT_MFMA}
-PA_SCHEDULE_AUTO, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED = 0, 1, 2
+PA_SCHEDULE_AUTO, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED, PA_SCHEDULE_STAGED = 0, 1, 2, 3
 SCHEDULES = {"auto": PA_SCHEDULE_AUTO, "partitions": PA_SCHEDULE_PARTITIONS,
-             "balanced": PA_SCHEDULE_BALANCED}
+             "balanced": PA_SCHEDULE_BALANCED, "staged": PA_SCHEDULE_STAGED}
 
 
 class PaTensor(ctypes.Structure):
@@ -234,10 +234,12 @@ def pa_prefill_workspace_bytes(num_rows, num_seqs, num_q_heads, num_kv_heads, he
 
 
 def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale=None, out=None, *,
-            window: int = 0, partition_tokens: int = 0, workspace=None, stream=None, out_dtype=None):
+            window: int = 0, partition_tokens: int = 0, schedule="auto", workspace=None, stream=None,
+            out_dtype=None):
     """Several queries per sequence on torch tensors: q [R, Hq, D] holds
     sequence b's queries at rows [query_start[b], query_start[b+1]) (its last
-    tokens, attending causally).  Returns out [R, Hq, D]."""
+    tokens, attending causally).  schedule: "auto", "partitions" or "staged".
+    Returns out [R, Hq, D]."""
     import torch
     R, Hq, D = q.shape
     NP, P, Hkv, _ = k_cache.shape
@@ -245,7 +247,7 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale=
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
-    opts = make_opts("auto", partition_tokens, "auto", 0, window)
+    opts = make_opts("auto", partition_tokens, schedule, 0, window)
     if workspace is None:
         n = pa_prefill_workspace_bytes(R, block_tables.shape[0], Hq, Hkv, D, block_tables.shape[1], P, opts)
         if n:

@@ -153,6 +153,8 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
         if (opts->variant < PA_VARIANT_AUTO || opts->variant > PA_VARIANT_MFMA)
             return fail(PA_EINVAL, "unknown variant %d", opts->variant);
         if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
+        if (opts->schedule == PA_SCHEDULE_STAGED)
+            return fail(PA_ENOTSUP, "the staged schedule is for several queries per sequence (pa_prefill)");
         if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_BALANCED)
             return fail(PA_EINVAL, "unknown schedule %d", opts->schedule);
         if (opts->shares < 0 || opts->shares > kLeanMaxShares)
@@ -495,7 +497,8 @@ int validate_append(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* k
 
 // ---------------------------------------------------------------- several queries
 struct PrefillPlan {
-    int n_slots;        // query-block slots (an upper bound on the blocks)
+    bool staged;        // four query blocks per workgroup (no split)
+    int n_slots;        // query-block slots (an upper bound on the blocks); staged: workgroup slots
     int part_tokens;
     int n_part;
     bool split;
@@ -543,8 +546,10 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
         if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
         if (opts->schedule == PA_SCHEDULE_BALANCED)
             return fail(PA_ENOTSUP, "several-query attention uses the partition schedule");
-        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_BALANCED)
+        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_STAGED)
             return fail(PA_EINVAL, "unknown schedule %d", opts->schedule);
+        if (opts->schedule == PA_SCHEDULE_STAGED && opts->partition_tokens > 0)
+            return fail(PA_EINVAL, "the staged schedule has no partitions (partition_tokens must be 0)");
         if (opts->shares != 0) return fail(PA_EINVAL, "shares apply to the balanced schedule only");
         if (opts->window < 0) return fail(PA_EINVAL, "window %d < 0", opts->window);
     }
@@ -572,9 +577,29 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
     return PA_OK;
 }
 
-PrefillPlan plan_prefill(const Geometry& g, int64_t rows, const pa_opts* opts) {
+// The staged kernel addresses the pool with a 32-bit page stride and a
+// 24-bit slot stride (P slots of at most 2^31 elements).
+bool staged_strides_ok(int64_t sp, int64_t ss, int64_t P) {
+    return sp >= 0 && sp < ((int64_t)1 << 32) && ss >= 0 && ss < ((int64_t)1 << 23) && P * ss < ((int64_t)1 << 31);
+}
+
+PrefillPlan plan_prefill(const Geometry& g, int64_t rows, const pa_opts* opts, bool staged_ok = true) {
     PrefillPlan pl{};
     const int qt = 16 / g.qg;
+    const int sched = opts ? opts->schedule : PA_SCHEDULE_AUTO;
+    // Staged: slots of kStagedWaves query blocks, an upper bound over any
+    // split of the rows into B sequences (each sequence rounds up once).
+    const int64_t gq = (int64_t)pa::kStagedWaves * qt;
+    const int64_t staged_slots = (rows + gq - 1) / gq + g.B;
+    if ((sched == PA_SCHEDULE_STAGED && staged_ok) ||
+        (sched == PA_SCHEDULE_AUTO && staged_ok && !(opts && opts->partition_tokens > 0) && rows >= 2 * qt * g.B &&
+         staged_slots * g.Hkv >= 256)) {
+        pl.staged = true;
+        pl.n_slots = (int)std::min<int64_t>(staged_slots, INT32_MAX);
+        pl.part_tokens = 0;
+        pl.n_part = 1;
+        return pl;
+    }
     pl.n_slots = (int)((rows + qt - 1) / qt + g.B);
     // Span of one block's work: the whole table, or with a window W the
     // block's W + qt - 1 attended tokens from a 16-token tile boundary.
@@ -614,7 +639,11 @@ int prefill_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, con
     int rc = validate_prefill(q, k, v, bt, ctx, qs, scale, num_q_heads, num_kv_heads, head_dim, page_size, out,
                               opts, g, rows);
     if (rc) return rc;
-    const PrefillPlan pl = plan_prefill(g, rows, opts);
+    const bool staged_ok = staged_strides_ok(k->stride[0], k->stride[1], g.P) &&
+                           staged_strides_ok(v->stride[0], v->stride[1], g.P);
+    if (opts && opts->schedule == PA_SCHEDULE_STAGED && !staged_ok)
+        return fail(PA_ENOTSUP, "staged schedule: page stride >= 2^32 or slot stride >= 2^23 elements");
+    const PrefillPlan pl = plan_prefill(g, rows, opts, staged_ok);
     if ((int64_t)pl.n_slots * g.Hkv * pl.n_part > INT32_MAX) return fail(PA_ENOTSUP, "grid too large");
     if (rows == 0 || g.B == 0) return PA_OK;
     int ndev = 0, dev = 0;
@@ -674,9 +703,11 @@ int prefill_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, con
     p.lean_page_slots = pa::lean_page_slots(p.P);
     p.window = opts ? opts->window : 0;
     p.scale_log2 = scale * pa::kLog2e;
-    e = pa::launch_prefill(p, (int)g.D, g.kv_dtype, pl.split, static_cast<hipStream_t>(stream));
+    e = pl.staged ? pa::launch_prefill_staged(p, (int)g.D, g.kv_dtype, static_cast<hipStream_t>(stream))
+                  : pa::launch_prefill(p, (int)g.D, g.kv_dtype, pl.split, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_EHIP, "several-query launch: %s", hipGetErrorString(e));
     g_stats.prefill++;
+    g_stats.last_schedule = pl.staged ? PA_SCHEDULE_STAGED : PA_SCHEDULE_PARTITIONS;
     if (pl.split) g_stats.merge++;
     g_stats.last_t = (uint64_t)pl.part_tokens;
     g_stats.last_np = (uint64_t)pl.n_part;
@@ -707,7 +738,11 @@ size_t pa_prefill_workspace_bytes(int64_t num_rows, int64_t num_seqs, int num_q_
     if (opts && (opts->partition_tokens < 0 || opts->window < 0)) return 0;
     Geometry g{num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, 1, max_blocks_per_seq, qg,
                PA_DTYPE_BF16, PA_DTYPE_BF16, PA_DTYPE_BF16};
-    return plan_prefill(g, num_rows, opts).ws_bytes;
+    // An upper bound over the pool's strides: with strides the staged kernel
+    // cannot take, the automatic schedule runs on partitions (and the staged
+    // one fails).
+    if (opts && opts->schedule == PA_SCHEDULE_STAGED) return plan_prefill(g, num_rows, opts, true).ws_bytes;
+    return std::max(plan_prefill(g, num_rows, opts, true).ws_bytes, plan_prefill(g, num_rows, opts, false).ws_bytes);
 }
 
 

@@ -45,6 +45,17 @@ constexpr int kLeanCounterBytes = 256;
 // Several queries per sequence (MFMA, 16-column query blocks), followed by
 // the per-row merge when split.
 hipError_t launch_prefill(const DecodeParams& p, int head_dim, int kv_dtype, bool split, hipStream_t s);
+// The same with kStagedWaves query blocks per workgroup sharing K/V stages in
+// LDS (no split); p.n_slots counts workgroup slots.
+#ifndef PA_STAGED_WAVES
+#define PA_STAGED_WAVES 8
+#endif
+#ifndef PA_STAGED_BUFFERS
+#define PA_STAGED_BUFFERS 4
+#endif
+constexpr int kStagedWaves = PA_STAGED_WAVES;
+constexpr int kStagedBuffers = PA_STAGED_BUFFERS;
+hipError_t launch_prefill_staged(const DecodeParams& p, int head_dim, int kv_dtype, hipStream_t s);
 
 // KV-cache append (one workgroup per sequence).
 hipError_t launch_append(const AppendParams& a, hipStream_t s);

@@ -299,11 +299,12 @@ __device__ __forceinline__ void run_tiles(const DecodeParams& p, const int* s_pa
 
 // Page ids of logical pages [lp0, lp1] of sequence b into s_pages (whole
 // workgroup; the caller synchronises before use).
+template <int NT = kMBlock>
 __device__ __forceinline__ void fetch_pages(const DecodeParams& p, int b, int lp0, int lp1, int* s_pages,
                                             int tid) {
     lp1 = min(lp1, p.max_blk - 1);
     const int32_t* btrow = p.bt + (int64_t)b * p.bt_sb;
-    for (int i = tid; i <= lp1 - lp0; i += kMBlock) s_pages[i] = clampi(btrow[lp0 + i], 0, p.num_pages - 1);
+    for (int i = tid; i <= lp1 - lp0; i += NT) s_pages[i] = clampi(btrow[lp0 + i], 0, p.num_pages - 1);
 }
 
 template <int D>
@@ -367,12 +368,12 @@ __device__ __forceinline__ void store_f32x8(float* dst, const float (&v)[8]) {
 }
 
 // Exclusive prefix sums s_pref[b] = sum_{b' < b} value(b') for b in [0, n]
-// into LDS, by the whole workgroup (every thread calls it), 256 entries per
-// pass: a shuffle scan inside each wave, then across the waves.
-template <typename F>
+// into LDS, by the whole workgroup of NT threads (every thread calls it), NT
+// entries per pass: a shuffle scan inside each wave, then across the waves.
+template <int NT = kMBlock, typename F>
 __device__ __forceinline__ void block_prefix(int n, int* s_pref, F value) {
     __shared__ int s_carry;
-    __shared__ int s_wsum[kMWaves];
+    __shared__ int s_wsum[NT / 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid == 0) {
@@ -380,7 +381,7 @@ __device__ __forceinline__ void block_prefix(int n, int* s_pref, F value) {
         s_pref[0] = 0;
     }
     __syncthreads();
-    for (int c = 0; c < n; c += kMBlock) {
+    for (int c = 0; c < n; c += NT) {
         const int bb = c + tid;
         int v = bb < n ? value(bb) : 0;
         for (int off = 1; off < 64; off <<= 1) {
@@ -393,7 +394,7 @@ __device__ __forceinline__ void block_prefix(int n, int* s_pref, F value) {
         for (int i = 0; i < wave; ++i) before += s_wsum[i];
         if (bb < n) s_pref[bb + 1] = before + v;
         __syncthreads();
-        if (tid == 0) s_carry = s_pref[min(c + kMBlock, n)];
+        if (tid == 0) s_carry = s_pref[min(c + NT, n)];
         __syncthreads();
     }
 }

@@ -164,6 +164,306 @@ __global__ __launch_bounds__(64) void pa_prefill_merge_kernel(DecodeParams p) {
                       (int64_t)r * p.o_sb + (int64_t)h * p.o_sh);
 }
 
+// ---------------------------------------------------------------------------
+// Staged layout, for calls with many query blocks: a workgroup of NW waves
+// takes NW consecutive query blocks of one sequence (one per wave) and one
+// KV head.  K and V stream through LDS in stages of ST tokens, read from
+// memory once per workgroup and consumed by every wave; each wave keeps its
+// own columns' online-softmax state over the whole range, so there is
+// neither a split nor a wave merge.
+//
+// The stages arrive by direct global-to-LDS loads (no registers on the way),
+// NB - 1 stages ahead of the one being consumed, into NB rotating buffers.
+// LDS rows are D elements with no padding; the 16-byte chunk c of row r sits
+// at chunk position c ^ (r & 15), so the K reads (16 rows, one chunk each)
+// and the V reads (16 chunks of one row) both spread over all banks.
+template <int D, int NW, int NB>
+struct Staged {
+    static constexpr int NT = NW * 64;
+    static constexpr int ST = D == 128 ? 64 : 32;    // tokens per stage (whole 32-token pairs)
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int BLK = ST * CPR / 64;        // 1 KiB blocks per tensor and stage
+    static constexpr int LPW = BLK / NW;             // blocks per wave per tensor and stage
+    static constexpr int STAGE = ST * D;             // elements per tensor and stage
+    static constexpr int kFillTokens = 2048;         // tokens per page-id fill
+    static_assert(BLK % NW == 0 && ST % 32 == 0, "stage must split evenly over the waves");
+    static_assert(2 * LPW * (NB - 2) <= 63, "outstanding loads must fit the vector-memory counter");
+};
+
+__device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Element offset, inside its row, of chunk `chunk` of row `row`.
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 15)) << 3; }
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and its LDS operations are done, then meet the workgroup.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// 32 tokens tb .. tb + 31 from one stage buffer (rows 0 .. 31 of kl / vl):
+// logits of the two 16-token halves on MFMA, one online-softmax update, and
+// P.V as one 16x16x32 MFMA per 16 dims whose contraction runs over both
+// halves (lane q's eight k-slots: tokens 4q .. 4q+3 of each half).  P enters
+// P.V as the sum of two KV-type values, hi = round(p) and lo = round(p - hi):
+// the weights are then exact to about 2^-17 relative and the normaliser
+// sums p itself.
+template <int D, typename KV>
+__device__ __forceinline__ void stage_pair(const DecodeParams& p, const uint16_t* kl, const uint16_t* vl,
+                                           const u32x4 (&qop)[D / 32], int tb, bool mask, int mask_lo, int mask_hi,
+                                           int n, int q, bool col_live, f32x4 (&o)[D / 16], float& m_run,
+                                           float& l_run) {
+    constexpr int KK = D / 32;
+    constexpr int VH = D / 128;
+    constexpr int NO = D / 16;
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        sa = KV::mma_qk(lds16(kl + n * D + swz(n, 4 * kk + q)), qop[kk], sa);
+        sb = KV::mma_qk(lds16(kl + (16 + n) * D + swz(16 + n, 4 * kk + q)), qop[kk], sb);
+    }
+    float sv[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = tb + 4 * q + r;
+        sv[r] = sa[r] * p.scale_log2;
+        sv[4 + r] = sb[r] * p.scale_log2;
+        if (mask) {                             // (wave-uniform) else every token is in every column's range
+            sv[r] = (col_live && t < mask_hi && t >= mask_lo) ? sv[r] : -INFINITY;
+            sv[4 + r] = (col_live && t + 16 < mask_hi && t + 16 >= mask_lo) ? sv[4 + r] : -INFINITY;
+        }
+        mt = fmaxf(mt, fmaxf(sv[r], sv[4 + r]));
+    }
+    mt = xmax32(xmax16(mt));
+    if (__any(mt > m_run + kRescaleSlack)) {    // as in tile_step
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - mn);
+        m_run = mn;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NO; ++i) o[i] *= alpha;
+    }
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(sv[i] - m_run);
+    u32x4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ph[i] = KV::pack2(pr[2 * i], pr[2 * i + 1]);
+        pl[i] = KV::pack2(pr[2 * i] - KV::lo(ph[i]), pr[2 * i + 1] - KV::hi(ph[i]));
+    }
+    l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+
+#pragma unroll
+    for (int hh = 0; hh < VH; ++hh) {
+        u32x4 va[4], vb[4];                     // rows 4q + jj of each half, dims 8n .. 8n + 7 (+128 hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            va[jj] = lds16(vl + (4 * q + jj) * D + swz(4 * q + jj, n + 16 * hh));
+            vb[jj] = lds16(vl + (16 + 4 * q + jj) * D + swz(16 + 4 * q + jj, n + 16 * hh));
+        }
+        u32x4 vt[8];                            // V^T operand of dim 8n + mm
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+            const int x = mm >> 1;
+            const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+            vt[mm] = u32x4{__builtin_amdgcn_perm(va[1][x], va[0][x], sel), __builtin_amdgcn_perm(va[3][x], va[2][x], sel),
+                           __builtin_amdgcn_perm(vb[1][x], vb[0][x], sel), __builtin_amdgcn_perm(vb[3][x], vb[2][x], sel)};
+        }
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) o[hh * 8 + mm] = KV::mma_qk(vt[mm], ph, o[hh * 8 + mm]);
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) o[hh * 8 + mm] = KV::mma_qk(vt[mm], pl, o[hh * 8 + mm]);
+    }
+}
+
+template <int D, int NW, int NB, typename KV>
+__global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams p) {
+    using C = Staged<D, NW, NB>;
+    constexpr int KK = D / 32;
+    constexpr int VH = D / 128;
+    constexpr int NO = D / 16;
+    constexpr int NT = C::NT, ST = C::ST, CPR = C::CPR, LPW = C::LPW;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, q = lane >> 4;
+    const int qg = p.Hq / p.Hkv;
+    const int qt = 16 / qg;                     // query tokens per block
+    const int gq = NW * qt;                     // query tokens per workgroup
+    // Workgroups go round-robin over the 8 dies (XCDs), each with its own L2:
+    // renumber so that each die runs a contiguous range of (KV head, slot),
+    // whose neighbours read the same sequence's K/V.
+    const int nwg = gridDim.x, xcd = blockIdx.x & 7, per = nwg >> 3, rem = nwg & 7;
+    const int lid = xcd * per + min(xcd, rem) + (blockIdx.x >> 3);
+    const int slot = lid % p.n_slots;
+    const int g = lid / p.n_slots;
+
+    extern __shared__ int s_dyn[];
+    int* s_pages = s_dyn;                       // kFillTokens / P + 2 entries
+    int* s_pref = s_dyn + p.lean_page_slots;    // B + 1 prefix sums of workgroup slots
+    block_prefix<NT>(p.B, s_pref, [&](int bb) {
+        const int nq = max(p.qstart[bb + 1] - p.qstart[bb], 0);
+        return (nq + gq - 1) / gq;
+    });
+    auto sp = [&](int i) { return __builtin_amdgcn_readfirstlane(s_pref[i]); };
+    if (slot >= sp(p.B)) return;
+    int lo_b = 0, hi_b = p.B - 1;
+    while (lo_b < hi_b) {
+        const int mid = (lo_b + hi_b + 1) >> 1;
+        if (sp(mid) <= slot) lo_b = mid; else hi_b = mid - 1;
+    }
+    const int b = lo_b;
+    const int r0 = p.qstart[b];
+    const int nq = p.qstart[b + 1] - r0;
+    const int gtok0 = (slot - sp(b)) * gq;      // the workgroup's first query token
+    if (r0 < 0 || r0 + gtok0 >= p.q_rows) return;
+    const int gntok = min(min(gq, nq - gtok0), p.q_rows - (r0 + gtok0));
+    const int Lb = clampi(p.ctx[b], 0, p.max_blk * p.P);
+
+    // This wave's block: query tokens tok0 .. tok0 + ntok - 1 of the sequence.
+    const int tok0 = gtok0 + wave * qt;
+    const int ntok = clampi(gntok - wave * qt, 0, qt);
+    const bool col_live = n < ntok * qg;
+    const int pos_n = Lb - nq + tok0 + (col_live ? n / qg : 0);
+    const int mask_hi = col_live ? pos_n + 1 : 0;
+    const int mask_lo = p.window > 0 ? max(0, pos_n - p.window + 1) : 0;
+    // Tokens [free_lo, free_hi) lie in every column's range (none if a
+    // column is empty): pairs inside it skip the masking.
+    const bool full = ntok == qt;
+    const int free_hi = full ? Lb - nq + tok0 + 1 : INT32_MIN;
+    const int free_lo = p.window > 0 ? max(0, Lb - nq + tok0 + qt - p.window) : 0;
+    // The workgroup's tokens: from its first query's window start (a tile
+    // boundary below it) to its last query.
+    const int pos_first = Lb - nq + gtok0;
+    const int te = pos_first + gntok;
+    const int lo_min = p.window > 0 ? max(0, pos_first - p.window + 1) : 0;
+    const int ts = lo_min & ~(kTile - 1);
+
+    u32x4 qop[KK];
+    {
+        const int r = r0 + tok0 + (col_live ? n / qg : 0);
+        const int h = g * qg + n % qg;
+        const int64_t qr = (int64_t)r * p.q_sb + (int64_t)h * p.q_sh;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int64_t off = qr + 32 * kk + 8 * q;
+            u32x4 w = u32x4{0u, 0u, 0u, 0u};
+            if (col_live) {
+                if (p.q_dtype == KV::code) {
+                    w = load16(static_cast<const uint16_t*>(p.q) + off);
+                } else {
+                    float f[8];
+                    load8f(p.q, p.q_dtype, off, f);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = KV::pack2(f[2 * i], f[2 * i + 1]);
+                }
+            }
+            qop[kk] = w;
+        }
+    }
+
+    f32x4 o[NO];
+#pragma unroll
+    for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kEmptyMax, l_run = 0.f;
+    __shared__ __attribute__((aligned(16))) uint16_t s_kv[NB][2][C::STAGE];
+    const uint16_t* kb = static_cast<const uint16_t*>(p.k) + (int64_t)g * p.k_sh;
+    const uint16_t* vb = static_cast<const uint16_t*>(p.v) + (int64_t)g * p.v_sh;
+
+    for (int c0 = ts; c0 < te; c0 += C::kFillTokens) {
+        const int c1 = min(te, c0 + C::kFillTokens);
+        int pg0, lp1, unused;
+        page_slot(p, c0, pg0, unused);
+        page_slot(p, c1 - 1, lp1, unused);
+        fetch_pages<NT>(p, b, pg0, lp1, s_pages, tid);
+        __syncthreads();                        // page ids ready; every wave is done with the last chunk
+        const int n_st = (c1 - c0 + ST - 1) / ST;
+        // This wave's share of stage s: blocks j * NW + wave of K and of V.
+        // Rows are clamped into [lo_min, te), which lies in this chunk's pages.
+        auto issue = [&](int s) {
+            uint16_t* kd = &s_kv[s % NB][0][0];
+            uint16_t* vd = &s_kv[s % NB][1][0];
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) {
+                const int cb = j * NW + wave;
+                const int lin = cb * 64 + lane;
+                const int row = lin / CPR;
+                const int chunk = (lin % CPR) ^ (row & 15);
+                const int t = clampi(c0 + s * ST + row, lo_min, te - 1);
+                int lp, sl;
+                page_slot(p, t, lp, sl);
+                // 32-bit page stride, 24-bit slot stride (the host checks both)
+                const uint32_t page = (uint32_t)s_pages[lp - pg0];
+                const uint64_t ko = (uint64_t)page * (uint32_t)p.k_sp + (uint32_t)(__mul24(sl, (int)p.k_ss) + chunk * 8);
+                const uint64_t vo = (uint64_t)page * (uint32_t)p.v_sp + (uint32_t)(__mul24(sl, (int)p.v_ss) + chunk * 8);
+                __builtin_amdgcn_global_load_lds(kb + ko, kd + cb * 512, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vb + vo, vd + cb * 512, 16, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < NB - 1; ++s)
+            if (s < n_st) issue(s);
+        for (int st = 0; st < n_st; ++st) {
+            // Stage st has landed once at most `ahead` later stages are in flight.
+            const int ahead = min(NB - 2, n_st - 1 - st);
+            if (NB >= 4 && ahead >= 2) vm_wait_barrier<4 * LPW>();
+            else if (NB >= 3 && ahead == 1) vm_wait_barrier<2 * LPW>();
+            else vm_wait_barrier<0>();
+            // The buffer of stage st - 1 is free: every wave has passed the barrier.
+            if (st + NB - 1 < n_st) issue(st + NB - 1);
+            const uint16_t* kl = &s_kv[st % NB][0][0];
+            const uint16_t* vl = &s_kv[st % NB][1][0];
+#pragma unroll
+            for (int i = 0; i < ST / 32; ++i) {
+                const int tb = c0 + st * ST + 32 * i;
+                const bool mask = !(tb >= free_lo && tb + 32 <= free_hi);   // wave-uniform
+                stage_pair<D, KV>(p, kl + 32 * i * D, vl + 32 * i * D, qop, tb, mask, mask_lo, mask_hi, n, q,
+                                  col_live, o, m_run, l_run);
+            }
+        }
+        __syncthreads();                        // every wave is done reading the stage buffers and page ids
+    }
+
+    // Each wave holds all tokens of its columns: normalise and store.
+    l_run = xsum32(xsum16(l_run));
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (col_live) {
+        const int64_t r = r0 + tok0 + n / qg;
+        const int h = g * qg + n % qg;
+        const int64_t base = r * p.o_sb + (int64_t)h * p.o_sh;
+#pragma unroll
+        for (int hh = 0; hh < VH; ++hh)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                float vals[8];
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm) vals[mm] = o[hh * 8 + mm][rr] * inv;
+                store8(p.out, p.out_dtype, base + 128 * hh + 32 * q + 8 * rr, vals);
+            }
+    }
+}
+
+template <int D, int NW, int NB, typename KV>
+static hipError_t launch_staged_d(DecodeParams p, hipStream_t s) {
+    using C = Staged<D, NW, NB>;
+    p.lean_page_slots = C::kFillTokens / p.P + 2;
+    const size_t lds = sizeof(int) * (size_t)(p.lean_page_slots + p.B + 1);
+    dim3 grid((uint32_t)((int64_t)p.n_slots * p.Hkv));
+    hipLaunchKernelGGL((pa_prefill_staged_kernel<D, NW, NB, KV>), grid, dim3(C::NT), lds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_staged(const DecodeParams& p, int head_dim, int kv_dtype, hipStream_t s) {
+    if (!mfma_supported(head_dim, 16, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
+    constexpr int NW = kStagedWaves, NB = kStagedBuffers;
+    if (kv_dtype == kDtF16)
+        return head_dim == 128 ? launch_staged_d<128, NW, NB, KvF16>(p, s) : launch_staged_d<256, NW, NB, KvF16>(p, s);
+    return head_dim == 128 ? launch_staged_d<128, NW, NB, KvBF16>(p, s) : launch_staged_d<256, NW, NB, KvBF16>(p, s);
+}
+
 template <int D, bool SPLIT, bool PAGE16, typename KV>
 static hipError_t launch_prefill_t(const DecodeParams& p, hipStream_t s) {
     constexpr int NBUF = D == 128 ? 3 : 2;

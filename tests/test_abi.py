@@ -147,8 +147,10 @@ def test_opts_are_validated():
     assert check(args(), o) == pa.PA_EINVAL
     o = pa.make_opts("valu", -5)
     assert check(args(), o) == pa.PA_EINVAL
-    o = pa.make_opts("mfma", 0, 3)
+    o = pa.make_opts("mfma", 0, 4)
     assert check(args(), o) == pa.PA_EINVAL
+    o = pa.make_opts("mfma", 0, "staged")                 # several queries only
+    assert check(args(), o) == pa.PA_ENOTSUP
     assert check(args(), pa.make_opts(window=-1)) == pa.PA_EINVAL
     assert check(args(), pa.make_opts(window=7)) == pa.PA_OK
     for sched in ("auto", "partitions", "balanced"):
@@ -341,6 +343,8 @@ def test_prefill_validation():
     assert call_prefill(ts, out, dims, pa.make_opts("valu")) == pa.PA_ENOTSUP
     assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, "balanced")) == pa.PA_ENOTSUP
     assert call_prefill(ts, out, dims, pa.make_opts(window=-2)) == pa.PA_EINVAL
+    assert call_prefill(ts, out, dims, pa.make_opts("auto", 64, "staged")) == pa.PA_EINVAL   # no partitions
+    assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, 4)) == pa.PA_EINVAL
     ts4, out4, dims4 = prefill_args(R=0, B=2)
     ts4[5] = torch.zeros(3, dtype=torch.int32)
     assert call_prefill(ts4, out4, dims4) == pa.PA_OK           # no rows: nothing to do
@@ -356,3 +360,12 @@ def test_prefill_workspace_bytes():
     # many query rows: enough blocks, no split
     assert pa.pa_prefill_workspace_bytes(4096, 4, 16, 8, 128, 64, 16, None) == 0
     assert pa.pa_prefill_workspace_bytes(4, 4, 12, 8, 128, 64, 16, None) == 0   # Hq % Hkv
+    # the staged schedule never splits; the same call on partitions does
+    staged = pa.make_opts("auto", 0, "staged")
+    parts = pa.make_opts("auto", 0, "partitions")
+    assert pa.pa_prefill_workspace_bytes(64, 4, 16, 8, 128, 64, 16, staged) == 0
+    assert pa.pa_prefill_workspace_bytes(64, 4, 16, 8, 128, 64, 16, parts) > 0
+    # automatic: 64 rows over 4 sequences (qt = 8: two blocks each) but only
+    # (64 / 32 + 4) x 8 = 48 staged workgroups -> partitions
+    assert pa.pa_prefill_workspace_bytes(64, 4, 16, 8, 128, 64, 16, None) == \
+        pa.pa_prefill_workspace_bytes(64, 4, 16, 8, 128, 64, 16, parts)

@@ -630,7 +630,16 @@ def prefill_run(d, q, qs, out_dtype=None, **kw):
     torch.cuda.synchronize()
     s = pa.pa_get_stats()
     assert s["prefill_launches"] == 1, s
+    if kw.get("schedule") == "staged":
+        assert s["last_schedule"] == pa.PA_SCHEDULE_STAGED and s["merge_launches"] == 0, s
+    elif kw.get("schedule") == "partitions":
+        assert s["last_schedule"] == pa.PA_SCHEDULE_PARTITIONS, s
     return host_out(out), s
+
+
+# (schedule, partition_tokens): the per-block kernel unsplit / split / one
+# partition, and four query blocks per workgroup sharing K/V stages in LDS
+PREFILL_SCHEDULES = [("partitions", 0), ("partitions", 64), ("partitions", 1 << 20), ("staged", 0)]
 
 
 def oracle_queries(inp, q, qs, window=0):
@@ -650,9 +659,9 @@ def test_prefill_parity(D, Hq, Hkv, P):
     d = to_device(inp)
     for W in (0, 7, 200):
         ref = oracle_queries(inp, q, qs, window=W)
-        for T in (0, 64, 1 << 20):
-            y, s = prefill_run(d, q, qs, window=W, partition_tokens=T)
-            assert_parity(y, ref, f"prefill D={D} Hq={Hq} Hkv={Hkv} P={P} W={W} T={T} "
+        for sched, T in PREFILL_SCHEDULES:
+            y, s = prefill_run(d, q, qs, window=W, partition_tokens=T, schedule=sched)
+            assert_parity(y, ref, f"prefill D={D} Hq={Hq} Hkv={Hkv} P={P} W={W} {sched} T={T} "
                                   f"(x{s['last_num_partitions']})")
 
 
@@ -660,8 +669,10 @@ def test_prefill_parity(D, Hq, Hkv, P):
 def test_prefill_element_types(kt, qt, ot):
     inp, q, qs = queries_case((64, 900, 33), (64, 40, 1), 16, 4, 128, 16, dtype=kt, q_dtype=qt, seed=5)
     d = to_device(inp)
-    y, _ = prefill_run(d, q, qs, out_dtype=TORCH_DT[ot])
-    assert_parity(y, oracle_queries(inp, q, qs), f"prefill q {qt} kv {kt} out {ot}")
+    ref = oracle_queries(inp, q, qs)
+    for sched in ("partitions", "staged"):
+        y, _ = prefill_run(d, q, qs, out_dtype=TORCH_DT[ot], schedule=sched)
+        assert_parity(y, ref, f"prefill {sched} q {qt} kv {kt} out {ot}")
 
 
 def test_prefill_one_query_per_sequence_matches_decode():
@@ -686,5 +697,34 @@ def test_prefill_long_chunk_spare_slots_and_empty_sequences():
     chunks = (0, 700, 0, 512)
     inp, q, qs = queries_case(lens, chunks, 8, 2, 128, 16, seed=11)
     d = to_device(inp)
-    y, _ = prefill_run(d, q, qs)
-    assert_parity(y, oracle_queries(inp, q, qs), "long chunks")
+    ref = oracle_queries(inp, q, qs)
+    for sched in ("auto", "partitions", "staged"):
+        y, _ = prefill_run(d, q, qs, schedule=sched)
+        assert_parity(y, ref, f"long chunks {sched}")
+
+
+def test_prefill_full_size_sampled_rows():
+    """The chunked-prefill workload the benchmark times (8 sequences of 4096
+    tokens whose last 512 are queried, Hq 32 / Hkv 8, d 128, page 16) in its
+    launch configuration (automatic: staged).  Sampled rows against the
+    oracle through an identity of the definition -- the query at position pos
+    attends exactly as a decode query over a context of pos + 1 tokens --
+    and the whole output against the per-block kernel."""
+    B, ctx, chunk, Hq, Hkv, D, P = 8, 4096, 512, 32, 8, 128, 16
+    w = custom(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P, ctx=(ctx,) * B)
+    inp = make_inputs(w, seed=0)
+    rng = np.random.default_rng(7)
+    qs = np.arange(0, B * chunk + 1, chunk, dtype=np.int32)
+    q = workloads.encode(rng.standard_normal((B * chunk, Hq, D)).astype(np.float32), "bf16")
+    d = to_device(inp)
+    y, s = prefill_run(d, q, qs)
+    assert s["last_schedule"] == pa.PA_SCHEDULE_STAGED, s
+    rows = np.unique(np.concatenate([rng.choice(B * chunk, 45, replace=False), [0, chunk - 1, B * chunk - 1]]))
+    pos = ctx - chunk + rows % chunk
+    ref = oracle.attention(np.ascontiguousarray(q[rows]), inp.k[0], inp.v[0],
+                           np.ascontiguousarray(inp.block_tables[rows // chunk]), (pos + 1).astype(np.int32),
+                           w.scale, Hkv)
+    assert_parity(y[rows], ref, f"full-size prefill, {len(rows)} sampled rows")
+    y2, _ = prefill_run(d, q, qs, schedule="partitions")
+    r = compare(y, y2)
+    assert r.nmse < 1e-4, r
