@@ -76,12 +76,13 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     page_slot(p, ts, pg0, unused);
     page_slot(p, ts + p.part_tokens - 1, lp_hi, unused);
     fetch_pages(p, b, pg0, lp_hi, s_pages, tid);
+    // Q does not depend on the length either: its load goes out with the
+    // others (a partition past the end drops it).
+    u32x4 qop[KK];
+    load_q<D, HALF, KV>(p, b, h0, qw, n, q, qop);
     if (p.window <= 0) L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     if (ts >= L && part > 0) return;
     const int te = min(L, ts + p.part_tokens);
-
-    u32x4 qop[KK];
-    load_q<D, HALF, KV>(p, b, h0, qw, n, q, qop);
     const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
     __syncthreads();
 

@@ -361,7 +361,8 @@ def test_balanced_share_sweep(D, Hq, Hkv):
 
 
 def test_balanced_workspace_reuse_and_counters():
-    """One caller workspace serves many calls of both schedules: the work
+    """One caller workspace serves many calls of every schedule and variant
+    (partition counts varying between calls): the balanced schedule's work
     counters are zero after every call and balanced reruns are bitwise
     identical (units have fixed bounds, whichever workgroup takes them)."""
     inp = make_inputs("hd256_gqa4", seed=3)
@@ -369,23 +370,26 @@ def test_balanced_workspace_reuse_and_counters():
     q, k, v = d.call(0)
     B, Hq, D = q.shape
     NP, P, Hkv, _ = k.shape
-    n = max(pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P,
-                                         pa.make_opts("mfma", 0, sch)) for sch in ("partitions", "balanced"))
+    n = max(pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, pa.make_opts(var, T, sch))
+            for var, sch, T in (("mfma", "partitions", 0), ("mfma", "balanced", 0), ("mfma", "partitions", 256),
+                                ("valu", "partitions", 256)))
     raw = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
     off = (-raw.data_ptr()) % 256
     ws = raw[off:off + n]
     ref = oracle_run(inp)
     first = None
-    for i, (sch, shares) in enumerate([("balanced", 0), ("partitions", 0), ("balanced", 256),
-                                       ("balanced", 7), ("balanced", 256), ("partitions", 0),
-                                       ("balanced", 1024), ("balanced", 256)]):
+    for i, (var, sch, shares, T) in enumerate([
+            ("mfma", "balanced", 0, 0), ("mfma", "partitions", 0, 0), ("mfma", "balanced", 256, 0),
+            ("mfma", "partitions", 0, 256), ("mfma", "balanced", 7, 0), ("valu", "partitions", 0, 256),
+            ("mfma", "balanced", 256, 0), ("mfma", "partitions", 0, 0), ("mfma", "partitions", 0, 1024),
+            ("mfma", "balanced", 1024, 0), ("mfma", "partitions", 0, 256), ("mfma", "balanced", 256, 0)]):
         out = torch.full_like(q, float("nan"))
-        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, variant="mfma",
-                  schedule=sch, shares=shares, workspace=ws)
+        pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, variant=var,
+                  schedule=sch, shares=shares, partition_tokens=T, workspace=ws)
         torch.cuda.synchronize()
         assert torch.all(ws[:256] == 0), f"call {i}: counters not reset"
         y = bits(out)
-        assert_parity(y, ref, f"reuse call {i} {sch} {shares}")
+        assert_parity(y, ref, f"reuse call {i} {var} {sch} {shares} T={T}")
         if sch == "balanced" and shares == 256:
             if first is None:
                 first = y
