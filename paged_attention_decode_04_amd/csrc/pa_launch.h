@@ -46,15 +46,13 @@ constexpr int kLeanCounterBytes = 256;
 // the per-row merge when split.
 hipError_t launch_prefill(const DecodeParams& p, int head_dim, int kv_dtype, bool split, hipStream_t s);
 // The same with kStagedWaves query blocks per workgroup sharing K/V stages in
-// LDS (no split); p.n_slots counts workgroup slots.
-#ifndef PA_STAGED_WAVES
-#define PA_STAGED_WAVES 8
-#endif
-#ifndef PA_STAGED_BUFFERS
-#define PA_STAGED_BUFFERS 4
-#endif
-constexpr int kStagedWaves = PA_STAGED_WAVES;
-constexpr int kStagedBuffers = PA_STAGED_BUFFERS;
+// LDS (no split); p.n_slots counts workgroup slots.  Stage buffers: two at
+// head_dim 128 (64 KiB, so two workgroups share a CU), four at 256 (the
+// register file allows one workgroup per CU there; measured on the
+// chunked-prefill workload).
+constexpr int kStagedWaves = 8;
+constexpr int kStagedBuffers128 = 2;
+constexpr int kStagedBuffers256 = 4;
 hipError_t launch_prefill_staged(const DecodeParams& p, int head_dim, int kv_dtype, hipStream_t s);
 
 // KV-cache append (one workgroup per sequence).

@@ -191,6 +191,12 @@ struct Staged {
 };
 
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) void*)(p)));
+}
 // Element offset, inside its row, of chunk `chunk` of row `row`.
 __device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 15)) << 3; }
 
@@ -202,27 +208,32 @@ __device__ __forceinline__ void vm_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// 32 tokens tb .. tb + 31 from one stage buffer (rows 0 .. 31 of kl / vl):
-// logits of the two 16-token halves on MFMA, one online-softmax update, and
-// P.V as one 16x16x32 MFMA per 16 dims whose contraction runs over both
-// halves (lane q's eight k-slots: tokens 4q .. 4q+3 of each half).  P enters
-// P.V as the sum of two KV-type values, hi = round(p) and lo = round(p - hi):
-// the weights are then exact to about 2^-17 relative and the normaliser
-// sums p itself.
+// 32 tokens tb .. tb + 31 from one stage buffer (rows 0 .. 31 of kl / vl),
+// in two steps so that a stage can issue the logits of all its pairs before
+// the first softmax (the matrix cores then overlap the vector work):
+// pair_logits: the logits of the two 16-token halves on MFMA;
+// pair_update: one online-softmax update, and P.V as one 16x16x32 MFMA per
+// 16 dims whose contraction runs over both halves (lane q's eight k-slots:
+// tokens 4q .. 4q+3 of each half).  P enters P.V as the sum of two KV-type
+// values, hi = round(p) and lo = round(p - hi): the weights are then exact to
+// about 2^-17 relative and the normaliser sums p itself.
 template <int D, typename KV>
-__device__ __forceinline__ void stage_pair(const DecodeParams& p, const uint16_t* kl, const uint16_t* vl,
-                                           const u32x4 (&qop)[D / 32], int tb, bool mask, int mask_lo, int mask_hi,
-                                           int n, int q, bool col_live, f32x4 (&o)[D / 16], float& m_run,
-                                           float& l_run) {
-    constexpr int KK = D / 32;
-    constexpr int VH = D / 128;
-    constexpr int NO = D / 16;
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void pair_logits(const uint16_t* kl, const u32x4 (&qop)[D / 32], int n, int q,
+                                            f32x4& sa, f32x4& sb) {
+    sa = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < D / 32; ++kk) {
         sa = KV::mma_qk(lds16(kl + n * D + swz(n, 4 * kk + q)), qop[kk], sa);
         sb = KV::mma_qk(lds16(kl + (16 + n) * D + swz(16 + n, 4 * kk + q)), qop[kk], sb);
     }
+}
+
+template <int D, typename KV>
+__device__ __forceinline__ void pair_update(const DecodeParams& p, const uint16_t* vl, const f32x4& sa,
+                                            const f32x4& sb, int tb, bool mask, int mask_lo, int mask_hi, int n,
+                                            int q, bool col_live, f32x4 (&o)[D / 16], float& m_run, float& l_run) {
+    constexpr int NO = D / 16;
     float sv[8];
     float mt = -INFINITY;
 #pragma unroll
@@ -256,26 +267,22 @@ __device__ __forceinline__ void stage_pair(const DecodeParams& p, const uint16_t
     }
     l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
 
+    // V^T operands by transposing LDS reads (ds_read_b64_tr_b16): inside each
+    // 16-lane group, lane j gets slot k from element j % 4 of the 8 bytes at
+    // the address of lane 4k + j / 4.  Lane 4k + m of group q points at V row
+    // 4q + k, dims 16t + 4m .. +3, so lane (j, q) receives tokens 4q .. 4q+3
+    // of dim 16t + j: the A operand of output tile t (rows = dims 16t ..
+    // 16t + 15), one read per half.  Rows are swizzled like the K reads.
+    const int vx = 4 * q + (n >> 2);            // row inside the half (= row & 15)
+    const int vy = ((n >> 1) & 1) ^ vx;
+    const int vrow = vx * D + 4 * (n & 1);
 #pragma unroll
-    for (int hh = 0; hh < VH; ++hh) {
-        u32x4 va[4], vb[4];                     // rows 4q + jj of each half, dims 8n .. 8n + 7 (+128 hh)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            va[jj] = lds16(vl + (4 * q + jj) * D + swz(4 * q + jj, n + 16 * hh));
-            vb[jj] = lds16(vl + (16 + 4 * q + jj) * D + swz(16 + 4 * q + jj, n + 16 * hh));
-        }
-        u32x4 vt[8];                            // V^T operand of dim 8n + mm
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-            const int x = mm >> 1;
-            const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
-            vt[mm] = u32x4{__builtin_amdgcn_perm(va[1][x], va[0][x], sel), __builtin_amdgcn_perm(va[3][x], va[2][x], sel),
-                           __builtin_amdgcn_perm(vb[1][x], vb[0][x], sel), __builtin_amdgcn_perm(vb[3][x], vb[2][x], sel)};
-        }
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) o[hh * 8 + mm] = KV::mma_qk(vt[mm], ph, o[hh * 8 + mm]);
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) o[hh * 8 + mm] = KV::mma_qk(vt[mm], pl, o[hh * 8 + mm]);
+    for (int t = 0; t < NO; ++t) {
+        const int off = vrow + (((2 * t) ^ vy) << 3);
+        const u32x2 a = lds_tr(vl + off), b = lds_tr(vl + 16 * D + off);
+        const u32x4 vt = {a[0], a[1], b[0], b[1]};
+        o[t] = KV::mma_qk(vt, ph, o[t]);
+        o[t] = KV::mma_qk(vt, pl, o[t]);
     }
 }
 
@@ -283,7 +290,6 @@ template <int D, int NW, int NB, typename KV>
 __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams p) {
     using C = Staged<D, NW, NB>;
     constexpr int KK = D / 32;
-    constexpr int VH = D / 128;
     constexpr int NO = D / 16;
     constexpr int NT = C::NT, ST = C::ST, CPR = C::CPR, LPW = C::LPW;
     const int tid = threadIdx.x;
@@ -416,12 +422,16 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
             if (st + NB - 1 < n_st) issue(st + NB - 1);
             const uint16_t* kl = &s_kv[st % NB][0][0];
             const uint16_t* vl = &s_kv[st % NB][1][0];
+            constexpr int NPAIR = ST / 32;
+            f32x4 sa[NPAIR], sb[NPAIR];
 #pragma unroll
-            for (int i = 0; i < ST / 32; ++i) {
+            for (int i = 0; i < NPAIR; ++i) pair_logits<D, KV>(kl + 32 * i * D, qop, n, q, sa[i], sb[i]);
+#pragma unroll
+            for (int i = 0; i < NPAIR; ++i) {
                 const int tb = c0 + st * ST + 32 * i;
                 const bool mask = !(tb >= free_lo && tb + 32 <= free_hi);   // wave-uniform
-                stage_pair<D, KV>(p, kl + 32 * i * D, vl + 32 * i * D, qop, tb, mask, mask_lo, mask_hi, n, q,
-                                  col_live, o, m_run, l_run);
+                pair_update<D, KV>(p, vl + 32 * i * D, sa[i], sb[i], tb, mask, mask_lo, mask_hi, n, q, col_live, o,
+                                   m_run, l_run);
             }
         }
         __syncthreads();                        // every wave is done reading the stage buffers and page ids
@@ -430,19 +440,15 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
     // Each wave holds all tokens of its columns: normalise and store.
     l_run = xsum32(xsum16(l_run));
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    if (col_live) {
+    if (col_live) {                             // o[t][r]: dim 16t + 4q + r
         const int64_t r = r0 + tok0 + n / qg;
         const int h = g * qg + n % qg;
-        const int64_t base = r * p.o_sb + (int64_t)h * p.o_sh;
+        const int64_t base = r * p.o_sb + (int64_t)h * p.o_sh + 4 * q;
 #pragma unroll
-        for (int hh = 0; hh < VH; ++hh)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                float vals[8];
-#pragma unroll
-                for (int mm = 0; mm < 8; ++mm) vals[mm] = o[hh * 8 + mm][rr] * inv;
-                store8(p.out, p.out_dtype, base + 128 * hh + 32 * q + 8 * rr, vals);
-            }
+        for (int t = 0; t < NO; ++t) {
+            store2(p.out, p.out_dtype, base + 16 * t, o[t][0] * inv, o[t][1] * inv);
+            store2(p.out, p.out_dtype, base + 16 * t + 2, o[t][2] * inv, o[t][3] * inv);
+        }
     }
 }
 
@@ -458,10 +464,10 @@ static hipError_t launch_staged_d(DecodeParams p, hipStream_t s) {
 
 hipError_t launch_prefill_staged(const DecodeParams& p, int head_dim, int kv_dtype, hipStream_t s) {
     if (!mfma_supported(head_dim, 16, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
-    constexpr int NW = kStagedWaves, NB = kStagedBuffers;
+    constexpr int NW = kStagedWaves, NB1 = kStagedBuffers128, NB2 = kStagedBuffers256;
     if (kv_dtype == kDtF16)
-        return head_dim == 128 ? launch_staged_d<128, NW, NB, KvF16>(p, s) : launch_staged_d<256, NW, NB, KvF16>(p, s);
-    return head_dim == 128 ? launch_staged_d<128, NW, NB, KvBF16>(p, s) : launch_staged_d<256, NW, NB, KvBF16>(p, s);
+        return head_dim == 128 ? launch_staged_d<128, NW, NB1, KvF16>(p, s) : launch_staged_d<256, NW, NB2, KvF16>(p, s);
+    return head_dim == 128 ? launch_staged_d<128, NW, NB1, KvBF16>(p, s) : launch_staged_d<256, NW, NB2, KvBF16>(p, s);
 }
 
 template <int D, bool SPLIT, bool PAGE16, typename KV>

@@ -1,7 +1,9 @@
 """Code-generation guard for the gfx950 kernels (CPU only: hipcc cross-compiles).
 
-Cross-lane moves (permlane swaps, DPP) read other lanes' registers; under a
-partial exec mask they read inactive lanes and return stale data.  The MFMA
+Cross-lane moves (permlane swaps, DPP) read other lanes' registers, and the
+transposing LDS reads (ds_read_b64_tr_b16) gather through other lanes'
+addresses; under a partial exec mask they read inactive lanes and return
+stale data.  The MFMA
 kernels therefore evaluate every cross-lane move unconditionally.  This test
 compiles the kernels to gfx950 assembly and checks, by a data-flow pass over
 each kernel's control-flow graph, that no permlane or DPP instruction can run
@@ -115,7 +117,7 @@ def cross_lane_under_divergence(body):
         states = set(entry[i])
         for t in ins:
             if any(nar for st in states for _, nar in st) and (
-                    "permlane" in t or "_dpp" in t or " row_" in t):
+                    "permlane" in t or "_dpp" in t or " row_" in t or "_tr_b" in t):
                 bad.add(t)
             states = {_step(st, t) for st in states}
         for s in succ:
@@ -160,6 +162,8 @@ def test_analysis_catches_cross_lane_op_in_region():
     s_endpgm
 """
     assert cross_lane_under_divergence(body) == ["v_permlane32_swap_b32_e32 v1, v2"]
+    assert cross_lane_under_divergence(body.replace("v_permlane32_swap_b32_e32 v1, v2",
+                                                    "ds_read_b64_tr_b16 v[1:2], v3")) == ["ds_read_b64_tr_b16 v[1:2], v3"]
     # the same through an else arm, and inside a divergent loop
     body_else = """
     s_and_saveexec_b64 s[4:5], vcc
