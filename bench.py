@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="timed steps only (no per-config sweep, no CPU baseline): for rocprofv3 runs")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="only the several-query (chunked-prefill) line, printed as the JSON line: "
+                         "for rocprofv3 runs over its kernel")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a plain device copy of this many MiB (HBM reference and the "
                          "calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -361,6 +364,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.profile_prefill:
+        print(json.dumps(prefill_line(pa, torch, wl)), flush=True)
+        return
     w = wl.WORKLOADS[args.workload]
     t_gen = time.perf_counter()
     if w.name == "long_ctx_gqa8":
