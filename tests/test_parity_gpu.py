@@ -13,7 +13,7 @@ import torch
 import oracle
 import paged_attention_decode_04_amd as pa
 import workloads
-from oracle.compare import compare
+from oracle.compare import bf16_bits_to_f64, compare
 from workloads import WORKLOADS, custom, make_inputs, to_device
 
 pytestmark = pytest.mark.gpu
@@ -732,3 +732,60 @@ def test_prefill_full_size_sampled_rows():
     y2, _ = prefill_run(d, q, qs, schedule="partitions")
     r = compare(y, y2)
     assert r.nmse < 1e-4, r
+
+
+@pytest.mark.parametrize("schedule", ["partitions", "staged"])
+def test_prefill_more_queries_than_tokens(schedule):
+    """A broken precondition (n_b > L_b) is handled safely: rows at negative
+    positions give zeros, the others attend to their [0, pos] as a decode
+    query over pos + 1 tokens would (the oracle refuses such inputs, so
+    those rows are checked through that identity)."""
+    lens, chunks = (40, 3), (4, 8)
+    inp, q, qs = queries_case(lens, chunks, 16, 4, 128, 16, seed=23)
+    d = to_device(inp)
+    y, _ = prefill_run(d, q, qs, schedule=schedule)
+    yf = bf16_bits_to_f64(y) if y.dtype == np.uint16 else y.astype(np.float64)
+    assert np.all(yf[4:9] == 0), "rows at negative positions must be zero"
+    rows = np.array([0, 1, 2, 3, 9, 10, 11])
+    b_of = np.array([0, 0, 0, 0, 1, 1, 1])
+    pos = np.array([36, 37, 38, 39, 0, 1, 2])
+    ref = oracle.attention(np.ascontiguousarray(q[rows]), inp.k[0], inp.v[0],
+                           np.ascontiguousarray(inp.block_tables[b_of]), (pos + 1).astype(np.int32),
+                           inp.w.scale, inp.w.num_kv_heads)
+    assert_parity(y[rows], ref, f"n_b > L_b, {schedule}")
+
+
+@pytest.mark.parametrize("schedule", ["partitions", "staged"])
+def test_prefill_graph_replays_match_eager(schedule):
+    """Several-query calls captured in a HIP graph: every replay, with eager
+    work and synchronisations in between, equals the eager result bit for
+    bit (split partitions included: the workspace holds partials only)."""
+    inp, q, qs = queries_case((300, 1000, 2500), (100, 64, 33), 16, 4, 128, 16, seed=21)
+    d = to_device(inp)
+    qd, qsd = to_torch(q), torch.from_numpy(qs).cuda()
+    kw = dict(schedule=schedule, partition_tokens=64 if schedule == "partitions" else 0)
+    eager = pa.prefill(qd, d.k[0], d.v[0], d.block_tables, d.context_lens, qsd, d.w.scale, **kw)
+    torch.cuda.synchronize()
+    R, Hq, D = qd.shape
+    n = pa.pa_prefill_workspace_bytes(R, 3, Hq, 4, D, d.block_tables.shape[1], 16, pa.make_opts(**kw))
+    ws = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
+    ws = ws[(-ws.data_ptr()) % 256:][:max(n, 1)]
+    out = torch.empty_like(qd)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pa.prefill(qd, d.k[0], d.v[0], d.block_tables, d.context_lens, qsd, d.w.scale, out=out, workspace=ws, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.prefill(qd, d.k[0], d.v[0], d.block_tables, d.context_lens, qsd, d.w.scale, out=out, workspace=ws, **kw)
+    for i in range(4):
+        out.zero_()
+        junk = pa.prefill(qd, d.k[0], d.v[0], d.block_tables, d.context_lens, qsd, d.w.scale * 0.5, **kw)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del junk
+    assert_parity(host_out(out), oracle_queries(inp, q, qs), f"graph {schedule}")
