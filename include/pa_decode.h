@@ -160,7 +160,9 @@ int pa_cache_append(const pa_tensor* k_new,
 /* ---------------------------------------------------------------- options */
 #define PA_VARIANT_AUTO  0   /* the library picks                              */
 #define PA_VARIANT_VALU  1   /* vector-ALU kernel (any supported qg)            */
-#define PA_VARIANT_MFMA  2   /* matrix-core kernel (bf16 MFMA for Q.K and P.V)  */
+#define PA_VARIANT_MFMA  2   /* matrix-core kernel (bf16 or fp16 MFMA for Q.K
+                                and P.V; 16-bit caches, head_dim 128/256/512;
+                                the balanced schedule at 128/256 only)        */
 
 #define PA_SCHEDULE_AUTO        0  /* the library picks                         */
 #define PA_SCHEDULE_PARTITIONS  1  /* one workgroup per fixed-size partition of

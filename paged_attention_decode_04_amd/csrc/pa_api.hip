@@ -203,8 +203,8 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     // tile) work, whatever the mix of sequence lengths.
     const int64_t ub_tiles = groups * ((max_ctx + 15) / 16);
     const int sched = opts ? opts->schedule : PA_SCHEDULE_AUTO;
-    const bool lean_ok = pl.variant == PA_VARIANT_MFMA && g.B <= kLeanMaxBatch &&
-                         ub_tiles < ((int64_t)1 << 30);
+    const bool lean_ok = pl.variant == PA_VARIANT_MFMA && pa::mfma_lean_supported((int)g.D, pl.qw, g.kv_dtype) &&
+                         g.B <= kLeanMaxBatch && ub_tiles < ((int64_t)1 << 30);
     if (sched == PA_SCHEDULE_BALANCED)
         pl.lean = lean_ok;
     else if (sched == PA_SCHEDULE_AUTO)
@@ -242,7 +242,10 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         T = std::max<int64_t>(64, std::min<int64_t>(T, 1024));
     }
     T = (T + 63) / 64 * 64;
-    T = std::min<int64_t>(T, 8192 * g.P);   // page-id LDS stays <= ~32 KB
+    // Page-id LDS stays <= ~32 KB (16 KB beside the d512 MFMA merge buffer,
+    // 130 KB, inside the CU's 160 KB).
+    const bool big_merge = pl.variant == PA_VARIANT_MFMA && g.D == 512;
+    T = std::min<int64_t>(T, (big_merge ? 4096 : 8192) * g.P);
     if (T >= max_ctx) T = max_ctx;
     pl.part_tokens = (int)T;
     pl.n_part = (int)((max_ctx + T - 1) / T);
@@ -311,12 +314,12 @@ int cu_count(int dev) {
 
 int check_plan(const Geometry& g, const Plan& pl, const pa_opts* opts) {
     if (pl.variant == PA_VARIANT_MFMA && !pa::mfma_supported((int)g.D, pl.qw, g.kv_dtype))
-        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d, K/V dtype %d (D 128/256, "
+        return fail(PA_ENOTSUP, "MFMA variant does not support D=%lld, qg=%d, K/V dtype %d (D 128/256/512, "
                     "bf16 or fp16 K/V)", (long long)g.D, g.qg, g.kv_dtype);
     if (pl.variant == PA_VARIANT_VALU && !pa::valu_supported((int)g.D, pl.qw, g.kv_dtype))
         return fail(PA_ENOTSUP, "vector-ALU variant does not support D=%lld, qg=%d", (long long)g.D, g.qg);
     if (opts && opts->schedule == PA_SCHEDULE_BALANCED && !pl.lean)
-        return fail(PA_ENOTSUP, "balanced schedule needs the MFMA variant and at most %d sequences",
+        return fail(PA_ENOTSUP, "balanced schedule needs the MFMA variant, head_dim 128/256 and at most %d sequences",
                     kLeanMaxBatch);
     return PA_OK;
 }
@@ -556,7 +559,7 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
     const int qg = num_q_heads / num_kv_heads;
     if (qg != 1 && qg != 2 && qg != 4 && qg != 8 && qg != 16)
         return fail(PA_ENOTSUP, "Hq/Hkv = %d (supported: 1, 2, 4, 8, 16)", qg);
-    if (!pa::mfma_supported(head_dim, 16, k->dtype))
+    if (!pa::prefill_supported(head_dim, k->dtype))
         return fail(PA_ENOTSUP, "several-query attention needs head_dim 128/256 and a bf16 or fp16 cache");
     if (B > kLeanMaxBatch) return fail(PA_ENOTSUP, "batch %lld > %d", (long long)B, kLeanMaxBatch);
     if (rows > INT32_MAX / 4) return fail(PA_ENOTSUP, "too many query rows");

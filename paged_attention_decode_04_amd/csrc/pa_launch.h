@@ -18,9 +18,13 @@ inline size_t pages_lds_bytes(const DecodeParams& p) {
 hipError_t launch_valu(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s);
 bool valu_supported(int head_dim, int qw, int kv_dtype);
 
-// Matrix-core decode kernel (16 query rows per MFMA tile); bf16 or fp16 K/V.
+// Matrix-core decode kernel (16 query rows per MFMA tile); bf16 or fp16 K/V;
+// head_dim 128, 256 or 512 (the balanced schedule: 128 or 256).
 hipError_t launch_mfma(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s);
 bool mfma_supported(int head_dim, int qw, int kv_dtype);
+bool mfma_lean_supported(int head_dim, int qw, int kv_dtype);
+// Several queries per sequence: head_dim 128 or 256, bf16 or fp16 K/V.
+bool prefill_supported(int head_dim, int kv_dtype);
 
 // Matrix-core decode over a balanced schedule (the sequence-major list of
 // (sequence, query block, 16-token tile) cut into one static unit per

@@ -335,13 +335,22 @@ __global__ __launch_bounds__(64) void pa_lean_merge_kernel(DecodeParams p) {
 }
 
 bool mfma_supported(int head_dim, int qw, int kv_dtype) {
-    return (head_dim == 128 || head_dim == 256) && qw >= 1 && qw <= 16 &&
+    return (head_dim == 128 || head_dim == 256 || head_dim == 512) && qw >= 1 && qw <= 16 &&
            (kv_dtype == kDtBF16 || kv_dtype == kDtF16);
+}
+
+// The balanced schedule keeps the 4-wave merge buffer and the page ids of a
+// whole fill in LDS: head_dim 128 and 256 only.
+bool mfma_lean_supported(int head_dim, int qw, int kv_dtype) {
+    return head_dim <= 256 && mfma_supported(head_dim, qw, kv_dtype);
 }
 
 template <int D, bool SPLIT, bool PAGE16, typename KV>
 static hipError_t launch_mfma_t(const DecodeParams& p, int qw, hipStream_t s) {
     dim3 grid((uint32_t)((int64_t)p.n_part * (p.Hq / qw) * p.B));
+    // Tiles in flight per wave: three 8 KB tiles at d128, two at d256 and
+    // d512 (a d512 tile is 32 KB and 128 registers; the accumulators go to
+    // AGPRs, one wave per SIMD).
     constexpr int NBUF = D == 128 ? 3 : 2;
     if (qw <= 8)
         hipLaunchKernelGGL((pa_decode_mfma_kernel<D, SPLIT, PAGE16, true, NBUF, KV>), grid, dim3(kMBlock),
@@ -387,7 +396,7 @@ static hipError_t launch_lean_d(const DecodeParams& p, int n_wg, hipStream_t s) 
 }
 
 hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int kv_dtype, int n_wg, hipStream_t s) {
-    if (!mfma_supported(head_dim, p.qw, kv_dtype) || p.Hq % p.qw) return hipErrorInvalidValue;
+    if (!mfma_lean_supported(head_dim, p.qw, kv_dtype) || p.Hq % p.qw) return hipErrorInvalidValue;
     if (kv_dtype == kDtF16)
         return head_dim == 128 ? launch_lean_d<128, KvF16>(p, n_wg, s) : launch_lean_d<256, KvF16>(p, n_wg, s);
     return head_dim == 128 ? launch_lean_d<128, KvBF16>(p, n_wg, s) : launch_lean_d<256, KvBF16>(p, n_wg, s);
@@ -395,6 +404,8 @@ hipError_t launch_mfma_lean(const DecodeParams& p, int head_dim, int kv_dtype, i
 
 hipError_t launch_mfma(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s) {
     if (!mfma_supported(head_dim, qw, kv_dtype) || p.Hq % qw) return hipErrorInvalidValue;
+    if (head_dim == 512)
+        return kv_dtype == kDtF16 ? launch_mfma_d<512, KvF16>(p, qw, split, s) : launch_mfma_d<512, KvBF16>(p, qw, split, s);
     if (kv_dtype == kDtF16)
         return head_dim == 128 ? launch_mfma_d<128, KvF16>(p, qw, split, s)
                                : launch_mfma_d<256, KvF16>(p, qw, split, s);

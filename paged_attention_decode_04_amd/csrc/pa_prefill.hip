@@ -20,6 +20,10 @@
 
 namespace pa {
 
+bool prefill_supported(int head_dim, int kv_dtype) {
+    return (head_dim == 128 || head_dim == 256) && (kv_dtype == kDtBF16 || kv_dtype == kDtF16);
+}
+
 template <int D, bool SPLIT, bool PAGE16, int NBUF, typename KV>
 __global__ __launch_bounds__(kMBlock) void pa_prefill_mfma_kernel(DecodeParams p) {
     constexpr int KK = TileFrag<D>::KK;
@@ -463,7 +467,7 @@ static hipError_t launch_staged_d(DecodeParams p, hipStream_t s) {
 }
 
 hipError_t launch_prefill_staged(const DecodeParams& p, int head_dim, int kv_dtype, hipStream_t s) {
-    if (!mfma_supported(head_dim, 16, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
+    if (!prefill_supported(head_dim, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
     constexpr int NW = kStagedWaves, NB1 = kStagedBuffers128, NB2 = kStagedBuffers256;
     if (kv_dtype == kDtF16)
         return head_dim == 128 ? launch_staged_d<128, NW, NB1, KvF16>(p, s) : launch_staged_d<256, NW, NB2, KvF16>(p, s);
@@ -490,7 +494,7 @@ static hipError_t launch_prefill_d(const DecodeParams& p, bool split, hipStream_
 }
 
 hipError_t launch_prefill(const DecodeParams& p, int head_dim, int kv_dtype, bool split, hipStream_t s) {
-    if (!mfma_supported(head_dim, 16, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
+    if (!prefill_supported(head_dim, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
     if (kv_dtype == kDtF16)
         return head_dim == 128 ? launch_prefill_d<128, KvF16>(p, split, s) : launch_prefill_d<256, KvF16>(p, split, s);
     return head_dim == 128 ? launch_prefill_d<128, KvBF16>(p, split, s) : launch_prefill_d<256, KvBF16>(p, split, s);

@@ -92,9 +92,9 @@ def test_bad_arguments_are_rejected(mutate, code):
 
 
 def test_element_types_and_head_sizes():
-    """bf16 / fp16 / fp32 for Q, K/V and out; head_dim 512 and fp32 K/V run
-    on the vector-ALU kernel, so asking for the MFMA variant there is
-    ENOTSUP."""
+    """bf16 / fp16 / fp32 for Q, K/V and out.  fp32 K/V runs on the
+    vector-ALU kernel only (the MFMA variant is ENOTSUP there); head_dim 512
+    runs on both, but not on the balanced schedule."""
     for qt in (torch.bfloat16, torch.float16, torch.float32):
         for kt in (torch.bfloat16, torch.float16, torch.float32):
             a = args()
@@ -106,7 +106,8 @@ def test_element_types_and_head_sizes():
     assert check(a, pa.make_opts("mfma")) == pa.PA_ENOTSUP
     assert check(a, pa.make_opts("valu")) == pa.PA_OK
     assert check(args(D=512, Hq=16, Hkv=8)) == pa.PA_OK
-    assert check(args(D=512, Hq=16, Hkv=8), pa.make_opts("mfma")) == pa.PA_ENOTSUP
+    assert check(args(D=512, Hq=16, Hkv=8), pa.make_opts("mfma")) == pa.PA_OK
+    assert check(args(D=512, Hq=16, Hkv=8), pa.make_opts("mfma", 0, "balanced")) == pa.PA_ENOTSUP
     a = args()
     big = torch.zeros(8, 16, 8, 130, dtype=torch.float32)[..., :128]   # fp32 rows 520 B apart
     a.update(k_cache=big, v_cache=torch.zeros(8, 16, 8, 128))

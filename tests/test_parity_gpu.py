@@ -570,24 +570,29 @@ def test_fp32_cache_on_mfma_is_enotsup():
 @pytest.mark.parametrize("kt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (16, 4), (16, 2)])
 def test_head_dim_512(kt, Hq, Hkv):
-    """head_dim 512 on the vector-ALU kernel (two query heads per workgroup
-    at most): split and unsplit, with and without a window."""
+    """head_dim 512: the vector-ALU kernel (two query heads per workgroup at
+    most) and, for 16-bit caches, the MFMA kernel (all query heads of a KV
+    head; 32 KB tiles): split and unsplit, with and without a window."""
     w = custom(batch=4, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=512, page_size=16,
                ctx=(1, 33, 700, 1500))
     inp = make_inputs(w, seed=Hq * Hkv, poison_unused=True, dtype=kt)
     d = to_device(inp)
     ref = oracle_run(inp)
-    for T in (0, 64, 4096):
-        y, s = gpu_run(d, variant="valu", partition_tokens=T)
-        assert_parity(y, ref, f"D=512 kv {kt} Hq={Hq} Hkv={Hkv} T={T}")
-    y, _ = gpu_run(d, variant="valu", window=100)
-    assert_parity(y, oracle_run(inp, window=100), f"D=512 kv {kt} W=100")
-    # the automatic choice takes the vector-ALU kernel at head_dim 512
+    ref_w = oracle_run(inp, window=100)
+    variants = ["valu"] + (["mfma"] if kt != "f32" else [])
+    for var in variants:
+        for T in (0, 64, 4096):
+            y, s = gpu_run(d, variant=var, partition_tokens=T)
+            assert_parity(y, ref, f"D=512 {var} kv {kt} Hq={Hq} Hkv={Hkv} T={T}")
+        y, _ = gpu_run(d, variant=var, window=100)
+        assert_parity(y, ref_w, f"D=512 {var} kv {kt} W=100")
+    # the automatic choice: MFMA for 16-bit caches, vector ALU for fp32
     pa.pa_reset_stats()
     q, k, v = d.call(0)
     pa.decode(q, k, v, d.block_tables, d.context_lens)
     torch.cuda.synchronize()
-    assert pa.pa_get_stats()["valu_launches"] == 1
+    st = pa.pa_get_stats()
+    assert st["valu_launches" if kt == "f32" else "mfma_launches"] == 1, st
 
 
 @pytest.mark.parametrize("kt", ["f16", "f32"])
