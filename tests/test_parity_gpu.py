@@ -95,6 +95,16 @@ def test_config_parity(name, variant):
     assert_parity(y, oracle_run(inp), f"{name}/{variant} T={s['last_partition_tokens']}")
 
 
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_hd512_full_size(variant):
+    """The head_dim-512 workload timed by the benchmark (16 seqs, ctx
+    U[1024,4096], Hq8/Hkv2), all rows against the oracle, on both kernels
+    (the automatic choice is the MFMA one)."""
+    inp = make_inputs("hd512_gqa4", seed=0)
+    y, s = gpu_run(to_device(inp), variant=variant)
+    assert_parity(y, oracle_run(inp), f"hd512_gqa4/{variant} T={s['last_partition_tokens']}")
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_single_seq_layers_and_tokens(variant):
     """The 28-layer x 32-token workload: several calls spread over layers."""
