@@ -220,7 +220,7 @@ __device__ __forceinline__ void vm_wait_barrier() {
 // 16 dims whose contraction runs over both halves (lane q's eight k-slots:
 // tokens 4q .. 4q+3 of each half).  P enters P.V as the sum of two KV-type
 // values, hi = round(p) and lo = round(p - hi): the weights are then exact to
-// about 2^-17 relative and the normaliser sums p itself.
+// about 2^-17 relative, and the normaliser sums those same weights.
 template <int D, typename KV>
 __device__ __forceinline__ void pair_logits(const uint16_t* kl, const u32x4 (&qop)[D / 32], int n, int q,
                                             f32x4& sa, f32x4& sb) {
@@ -236,40 +236,66 @@ __device__ __forceinline__ void pair_logits(const uint16_t* kl, const u32x4 (&qo
 template <int D, typename KV>
 __device__ __forceinline__ void pair_update(const DecodeParams& p, const uint16_t* vl, const f32x4& sa,
                                             const f32x4& sb, int tb, bool mask, int mask_lo, int mask_hi, int n,
-                                            int q, bool col_live, f32x4 (&o)[D / 16], float& m_run, float& l_run) {
+                                            int q, bool col_live, f32x4 (&o)[D / 16], float& m_run, f32x4& l_acc) {
     constexpr int NO = D / 16;
-    float sv[8];
-    float mt = -INFINITY;
+    const float sc = p.scale_log2;
+    auto live = [&](int t) { return col_live && t < mask_hi && t >= mask_lo; };
+    // Exponents relative to the reference max, one fma each; the column max
+    // is only formed when some logit passes the reference by more than
+    // kRescaleSlack (then, as in tile_step, the reference moves and the
+    // accumulators rescale).
+    float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int t = tb + 4 * q + r;
-        sv[r] = sa[r] * p.scale_log2;
-        sv[4 + r] = sb[r] * p.scale_log2;
+        x[r] = fmaf(sa[r], sc, -m_run);
+        x[4 + r] = fmaf(sb[r], sc, -m_run);
         if (mask) {                             // (wave-uniform) else every token is in every column's range
-            sv[r] = (col_live && t < mask_hi && t >= mask_lo) ? sv[r] : -INFINITY;
-            sv[4 + r] = (col_live && t + 16 < mask_hi && t + 16 >= mask_lo) ? sv[4 + r] : -INFINITY;
+            x[r] = live(t) ? x[r] : -INFINITY;
+            x[4 + r] = live(t + 16) ? x[4 + r] : -INFINITY;
         }
-        mt = fmaxf(mt, fmaxf(sv[r], sv[4 + r]));
     }
-    mt = xmax32(xmax16(mt));
-    if (__any(mt > m_run + kRescaleSlack)) {    // as in tile_step
+    const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    if (__any(xm > kRescaleSlack)) {
+        float sv[8];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tb + 4 * q + r;
+            sv[r] = sa[r] * sc;
+            sv[4 + r] = sb[r] * sc;
+            if (mask) {
+                sv[r] = live(t) ? sv[r] : -INFINITY;
+                sv[4 + r] = live(t + 16) ? sv[4 + r] : -INFINITY;
+            }
+            mt = fmaxf(mt, fmaxf(sv[r], sv[4 + r]));
+        }
+        mt = xmax32(xmax16(mt));
         const float mn = fmaxf(m_run, mt);
         const float alpha = fast_exp2(m_run - mn);
         m_run = mn;
-        l_run *= alpha;
+        l_acc *= alpha;
 #pragma unroll
         for (int i = 0; i < NO; ++i) o[i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = sv[i] - mn;
     }
     float pr[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(sv[i] - m_run);
+    for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(x[i]);
     u32x4 ph, pl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         ph[i] = KV::pack2(pr[2 * i], pr[2 * i + 1]);
         pl[i] = KV::pack2(pr[2 * i] - KV::lo(ph[i]), pr[2 * i + 1] - KV::hi(ph[i]));
     }
-    l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+    // The normaliser on the matrix cores: an all-ones operand times P^T sums
+    // each column's weights (hi + lo, exactly the ones P.V uses) over all 32
+    // tokens, in every row of the tile.
+    const uint32_t one2 = KV::pack2(1.f, 1.f);
+    const u32x4 ones = {one2, one2, one2, one2};
+    l_acc = KV::mma_qk(ones, ph, l_acc);
+    l_acc = KV::mma_qk(ones, pl, l_acc);
 
     // V^T operands by transposing LDS reads (ds_read_b64_tr_b16): inside each
     // 16-lane group, lane j gets slot k from element j % 4 of the 8 bytes at
@@ -378,7 +404,8 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
     f32x4 o[NO];
 #pragma unroll
     for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = kEmptyMax, l_run = 0.f;
+    float m_run = kEmptyMax;
+    f32x4 l_acc = {0.f, 0.f, 0.f, 0.f};         // every element: the lane's column sum of weights
     __shared__ __attribute__((aligned(16))) uint16_t s_kv[NB][2][C::STAGE];
     const uint16_t* kb = static_cast<const uint16_t*>(p.k) + (int64_t)g * p.k_sh;
     const uint16_t* vb = static_cast<const uint16_t*>(p.v) + (int64_t)g * p.v_sh;
@@ -435,15 +462,14 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
                 const int tb = c0 + st * ST + 32 * i;
                 const bool mask = !(tb >= free_lo && tb + 32 <= free_hi);   // wave-uniform
                 pair_update<D, KV>(p, vl + 32 * i * D, sa[i], sb[i], tb, mask, mask_lo, mask_hi, n, q, col_live, o,
-                                   m_run, l_run);
+                                   m_run, l_acc);
             }
         }
         __syncthreads();                        // every wave is done reading the stage buffers and page ids
     }
 
     // Each wave holds all tokens of its columns: normalise and store.
-    l_run = xsum32(xsum16(l_run));
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv = l_acc[0] > 0.f ? 1.f / l_acc[0] : 0.f;
     if (col_live) {                             // o[t][r]: dim 16t + 4q + r
         const int64_t r = r0 + tok0 + n / qg;
         const int h = g * qg + n % qg;
