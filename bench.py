@@ -286,8 +286,10 @@ def prefill_line(pa, torch, workloads_mod, B=8, ctx=4096, chunk=512, Hq=32, Hkv=
     attended = B * (chunk * (ctx - chunk) + chunk * (chunk + 1) // 2)
     flops = 4 * D * Hq * attended
     tflops = flops / (us * 1e-6) / 1e12
+    kvb = B * ctx * Hkv * D * 4
     entry = {"workload": f"{B} seqs x ctx {ctx}, last {chunk} tokens queried, Hq{Hq}/Hkv{Hkv}, d{D}, page {P}",
              "us_per_call": round(us, 2), "flops_per_call": flops, "TFLOPs": round(tflops, 1),
+             "kv_bytes_per_call": kvb, "kv_GBps": round(kvb / (us * 1e-6) / 1e9, 1),
              "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
              "kernel": "pa_prefill_staged_kernel" if staged else "pa_prefill_mfma_kernel",
              "schedule": "staged" if staged else "partitions",
@@ -449,6 +451,8 @@ def main():
         result["per_config"] = per_config(pa, knobs, torch, wl)
         result["append"] = append_line(pa, torch, wl)
         result["prefill"] = prefill_line(pa, torch, wl)
+        # several queries per sequence in a decode step (speculative decoding)
+        result["prefill_spec4"] = prefill_line(pa, torch, wl, B=64, ctx=8192, chunk=4, Hq=64, Hkv=8)
     if not args.profile and not args.no_cpu_baseline:
         t = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(d, w, args.cpu_seconds, wl)

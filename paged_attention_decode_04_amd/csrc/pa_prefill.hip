@@ -453,13 +453,17 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
             if (st + NB - 1 < n_st) issue(st + NB - 1);
             const uint16_t* kl = &s_kv[st % NB][0][0];
             const uint16_t* vl = &s_kv[st % NB][1][0];
+            // A wave with no query (the last workgroup of a sequence, or few
+            // queries per sequence) only loads its share of every stage.
+            if (ntok == 0) continue;                                        // wave-uniform
+            const int sb0 = c0 + st * ST;
             constexpr int NPAIR = ST / 32;
             f32x4 sa[NPAIR], sb[NPAIR];
 #pragma unroll
             for (int i = 0; i < NPAIR; ++i) pair_logits<D, KV>(kl + 32 * i * D, qop, n, q, sa[i], sb[i]);
 #pragma unroll
             for (int i = 0; i < NPAIR; ++i) {
-                const int tb = c0 + st * ST + 32 * i;
+                const int tb = sb0 + 32 * i;
                 const bool mask = !(tb >= free_lo && tb + 32 <= free_hi);   // wave-uniform
                 pair_update<D, KV>(p, vl + 32 * i * D, sa[i], sb[i], tb, mask, mask_lo, mask_hi, n, q, col_live, o,
                                    m_run, l_acc);
