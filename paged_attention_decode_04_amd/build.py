@@ -30,11 +30,20 @@ CFLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source additions.  The several-query kernels assume no NaN in their
+# arithmetic (no input NaN reaches it: rows outside a sequence are never
+# loaded), so fmax needs no operand canonicalisation (one v_max per element
+# instead of two in the VALU-bound softmax).  Infinities keep their meaning.
+SOURCE_FLAGS = {"pa_prefill.hip": ["-fno-honor-nans"]}
+
+
+def flags(src: str) -> list[str]:
+    return [*CFLAGS, *SOURCE_FLAGS.get(src, [])]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

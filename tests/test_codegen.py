@@ -207,7 +207,7 @@ def test_analysis_catches_cross_lane_op_in_region():
 def test_no_cross_lane_ops_under_divergent_exec(src, tmp_path):
     from paged_attention_decode_04_amd import build
     out = tmp_path / "k.s"
-    cmd = [HIPCC, *build.CFLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
+    cmd = [HIPCC, *build.flags(src), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     asm = out.read_text()
     kernels = re.findall(r"^(_ZN2pa\w+):", asm, flags=re.M)
