@@ -804,3 +804,33 @@ def test_prefill_graph_replays_match_eager(schedule):
         assert torch.equal(out, eager), f"replay {i}"
         del junk
     assert_parity(host_out(out), oracle_queries(inp, q, qs), f"graph {schedule}")
+
+
+def test_prefill_speculative_decode_full_size_sampled():
+    """The speculative-decode workload the benchmark times (64 sequences of
+    8192 cached tokens, the last 4 queried, Hq 64 / Hkv 8, d 128, page 16;
+    2.1 GB of K/V, so 64-bit offsets) in its launch configuration
+    (automatic: staged, 6 of 8 waves per workgroup without a query).
+    Sampled rows against the oracle through the decode identity (a query at
+    position pos attends as a decode query over pos + 1 tokens), and the
+    whole output against the per-block kernel."""
+    B, ctx, nq, Hq, Hkv, D, P = 64, 8192, 4, 64, 8, 128, 16
+    w = custom(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P, ctx=(ctx,) * B)
+    d = workloads.device_inputs(w, seed=2)
+    rng = np.random.default_rng(9)
+    qs = np.arange(0, B * nq + 1, nq, dtype=np.int32)
+    q = workloads.encode(rng.standard_normal((B * nq, Hq, D)).astype(np.float32), "bf16")
+    y, s = prefill_run(d, q, qs)
+    assert s["last_schedule"] == pa.PA_SCHEDULE_STAGED, s
+    host = workloads.host_copy(d)
+    rows = np.unique(np.concatenate([rng.choice(B * nq, 29, replace=False), [0, 3, B * nq - 1]]))
+    pos = ctx - nq + rows % nq
+    ref = oracle.attention(np.ascontiguousarray(q[rows]), host.k[0], host.v[0],
+                           np.ascontiguousarray(host.block_tables[rows // nq]), (pos + 1).astype(np.int32),
+                           w.scale, Hkv)
+    assert_parity(y[rows], ref, f"speculative decode, {len(rows)} sampled rows")
+    y2, _ = prefill_run(d, q, qs, schedule="partitions")
+    r = compare(y, y2)
+    assert r.nmse < 1e-4, r
+    del d, host
+    torch.cuda.empty_cache()
