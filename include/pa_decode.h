@@ -46,7 +46,8 @@ extern "C" {
 #define PA_OK       0  /* success                                                  */
 #define PA_EINVAL   1  /* null pointer, bad shape/dtype/stride, Hq % Hkv != 0,
                           non-finite scale, page_size < 1                          */
-#define PA_ENOTSUP  2  /* head_dim not 128/256, or Hq/Hkv not 1, 2, 4, 8 or 16      */
+#define PA_ENOTSUP  2  /* head_dim not 128/256/512, Hq/Hkv not 1, 2, 4, 8 or 16, or a
+                          kernel/schedule that does not take the call's shape      */
 #define PA_EALIGN   3  /* a base pointer or a row stride not 16-byte aligned       */
 #define PA_ENODEV   4  /* no HIP device available                                  */
 #define PA_ENOMEM   5  /* workspace could not be allocated, or is too small        */
