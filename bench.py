@@ -72,8 +72,8 @@ def parse():
     ap.add_argument("--workload", default="long_ctx_gqa8")
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--schedule", default="auto", choices=["auto", "partitions", "balanced"])
-    ap.add_argument("--shares", type=int, default=0, help="balanced schedule: shares (0 = automatic)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "partitions", "balanced", "fitted"])
+    ap.add_argument("--shares", type=int, default=0, help="balanced schedule: shares; fitted: workgroups to fill (0 = automatic)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
@@ -148,14 +148,17 @@ def graph_time_us(calls, reps, torch):
 def launch_info(st):
     """Kernel names and launch configuration of the last call, from the counters."""
     variant = {1: "valu", 2: "mfma"}.get(int(st["last_variant"]), "?")
-    balanced = int(st["last_schedule"]) == 2
+    schedule = {2: "balanced", 4: "fitted"}.get(int(st["last_schedule"]), "partitions")
+    balanced = schedule == "balanced"
     if variant == "valu":
         kernel, merge = "pa_decode_valu_kernel", "pa_lse_merge_kernel"
     elif balanced:
         kernel, merge = "pa_decode_mfma_lean_kernel", "pa_lean_merge_kernel"
     else:
         kernel, merge = "pa_decode_mfma_kernel", "pa_lse_merge_kernel"
-    launch = {"variant": variant, "schedule": "balanced" if balanced else "partitions",
+    # fitted: partition_tokens is the largest size the device may pick and
+    # partitions the partial slots per sequence (the smallest size)
+    launch = {"variant": variant, "schedule": schedule,
               "partition_tokens": int(st["last_partition_tokens"]),
               ("shares" if balanced else "partitions"): int(st["last_num_partitions"])}
     return kernel, (merge if st["merge_launches"] else None), launch

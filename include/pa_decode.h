@@ -175,6 +175,13 @@ int pa_cache_append(const pa_tensor* k_new,
 #define PA_SCHEDULE_STAGED      3  /* pa_prefill only: a workgroup takes four
                                       query blocks of one sequence, which share
                                       every K/V stage through LDS; no split   */
+#define PA_SCHEDULE_FITTED      4  /* MFMA only, no window, at most 256
+                                      sequences: split-KV partitions whose size
+                                      the kernel picks per call from the
+                                      context lengths, so that the partitions
+                                      fill `shares` workgroups (0 = one per
+                                      compute unit); partitions of no work are
+                                      never launched                          */
 
 typedef struct pa_opts {
     int32_t variant;            /* PA_VARIANT_*                                */

@@ -19,9 +19,10 @@ PA_OK, PA_EINVAL, PA_ENOTSUP, PA_EALIGN, PA_ENODEV, PA_ENOMEM, PA_EHIP = range(7
 PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32, PA_DTYPE_F16 = 1, 2, 3, 4
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 VARIANTS = {"auto": PA_VARIANT_AUTO, "valu": PA_VARIANT_VALU, "mfma": PA_VARIANT_MFMA}
-PA_SCHEDULE_AUTO, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED, PA_SCHEDULE_STAGED = 0, 1, 2, 3
+PA_SCHEDULE_AUTO, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED, PA_SCHEDULE_STAGED, PA_SCHEDULE_FITTED = \
+    0, 1, 2, 3, 4
 SCHEDULES = {"auto": PA_SCHEDULE_AUTO, "partitions": PA_SCHEDULE_PARTITIONS,
-             "balanced": PA_SCHEDULE_BALANCED, "staged": PA_SCHEDULE_STAGED}
+             "balanced": PA_SCHEDULE_BALANCED, "staged": PA_SCHEDULE_STAGED, "fitted": PA_SCHEDULE_FITTED}
 
 
 class PaTensor(ctypes.Structure):

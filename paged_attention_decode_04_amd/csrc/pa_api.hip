@@ -61,7 +61,19 @@ struct Plan {
     bool lean;          // balanced schedule (MFMA): shares instead of partitions
     bool n_part_fixed;  // balanced schedule: share count given by the caller
     size_t meta_offset; // balanced schedule: byte offset of the tile prefix sums
+    bool fit;           // fitted partitions: size chosen on the device in [fit_lo, part_tokens]
+    int fit_lo;         // fitted partitions: smallest size
+    int64_t fit_grid;   // fitted partitions: workgroups partitions of part_tokens may need
+    size_t fit_offset;  // fitted partitions: byte offset of the chosen size
 };
+
+// Fitted partitions: sizes from max(kFitMinTokens, T / kFitRange) up to the
+// size T the fixed schedule would take (its floor of 256 tokens holds here
+// too: shorter partitions cost more in per-workgroup overhead than they
+// gain in balance).
+constexpr int kFitMinTokens = 256;
+constexpr int kFitRange = 4;
+constexpr int kFitAutoMinParts = 4;
 
 // Balanced schedule: at most this many shares (workgroups) per call, so the
 // workspace size does not depend on the device it runs on.
@@ -155,7 +167,7 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
         if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
         if (opts->schedule == PA_SCHEDULE_STAGED)
             return fail(PA_ENOTSUP, "the staged schedule is for several queries per sequence (pa_prefill)");
-        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_BALANCED)
+        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_FITTED)
             return fail(PA_EINVAL, "unknown schedule %d", opts->schedule);
         if (opts->shares < 0 || opts->shares > kLeanMaxShares)
             return fail(PA_EINVAL, "shares %d outside 0..%d", opts->shares, kLeanMaxShares);
@@ -180,6 +192,18 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
                    q->dtype, k->dtype, out->dtype};
     return PA_OK;
 }
+
+// Whether a call may take fitted partitions: the MFMA kernel, no window,
+// lengths few enough for every workgroup to read, and no partition size
+// given by the caller.
+bool fit_allowed(const Geometry& g, const Plan& pl, const pa_opts* opts) {
+    return pl.variant == PA_VARIANT_MFMA && g.B <= pa::kFitMaxBatch && !(opts && opts->window > 0) &&
+           !(opts && opts->partition_tokens > 0);
+}
+
+// The automatic schedule takes fitted partitions where it would split them
+// and a smaller size than the fixed one is allowed.
+constexpr bool kFitAuto = true;
 
 Plan make_plan(const Geometry& g, const pa_opts* opts) {
     Plan pl{};
@@ -250,6 +274,26 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     pl.part_tokens = (int)T;
     pl.n_part = (int)((max_ctx + T - 1) / T);
     pl.split = pl.n_part > 1;
+    // Fitted partitions: the device picks the size in [fit_lo, T] from the
+    // actual lengths; the partial slots cover the smallest size.
+    pl.fit = pl.split && (sched == PA_SCHEDULE_FITTED || (sched == PA_SCHEDULE_AUTO && kFitAuto)) &&
+             fit_allowed(g, pl, opts);
+    if (pl.fit) {
+        pl.fit_lo = (int)std::min<int64_t>(T, (std::max<int64_t>(kFitMinTokens, T / kFitRange) + 63) / 64 * 64);
+        // The automatic choice keeps fixed partitions when there is no
+        // smaller size to pick, or when the block table holds fewer than
+        // kFitAutoMinParts fixed partitions: the fitted prologue (the
+        // lengths read first, the size search) costs about 1 us, which pays
+        // only where sequences much shorter than the table leave compute
+        // units idle (measured: 32 sequences of 512..4096 tokens in a
+        // 4096-token table, decode kernel 31.7 -> 29.0 us; 16 sequences of
+        // 1024..1152 tokens in a 1152-token table, 14.4 -> 15.4 us).
+        if (sched == PA_SCHEDULE_AUTO && (pl.fit_lo == T || pl.n_part < kFitAutoMinParts)) pl.fit = false;
+    }
+    if (pl.fit) {
+        pl.fit_grid = (int64_t)pl.n_part * groups;
+        pl.n_part = (int)((max_ctx + pl.fit_lo - 1) / pl.fit_lo);
+    }
     if (pl.split) {
         // The balanced schedule's counters keep their place at the start, so
         // one workspace can serve both schedules.
@@ -257,6 +301,10 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         pl.o_offset = pa::kLeanCounterBytes;
         pl.lse_offset = pl.o_offset + align_up(n * g.D * sizeof(float), kAlign);
         pl.ws_bytes = pl.lse_offset + align_up(n * sizeof(float), kAlign);
+        if (pl.fit) {
+            pl.fit_offset = pl.ws_bytes;
+            pl.ws_bytes += kAlign;
+        }
     }
     return pl;
 }
@@ -321,6 +369,9 @@ int check_plan(const Geometry& g, const Plan& pl, const pa_opts* opts) {
     if (opts && opts->schedule == PA_SCHEDULE_BALANCED && !pl.lean)
         return fail(PA_ENOTSUP, "balanced schedule needs the MFMA variant, head_dim 128/256 and at most %d sequences",
                     kLeanMaxBatch);
+    if (opts && opts->schedule == PA_SCHEDULE_FITTED && !fit_allowed(g, pl, opts))
+        return fail(PA_ENOTSUP, "fitted partitions need the MFMA variant, no window, no partition size and at most "
+                    "%d sequences", pa::kFitMaxBatch);
     return PA_OK;
 }
 
@@ -389,6 +440,12 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
         g_stats.last_schedule = PA_SCHEDULE_BALANCED;
         return PA_OK;
     }
+    if (pl.fit) {
+        p.fit_part = reinterpret_cast<int*>(static_cast<char*>(ws) + pl.fit_offset);
+        p.fit_lo = pl.fit_lo;
+        p.fit_target = opts && opts->shares > 0 ? opts->shares : cu_count(dev);
+        p.n_wg = (int)std::max<int64_t>(pl.fit_grid, p.fit_target);
+    }
     if (pl.variant == PA_VARIANT_MFMA) {
         e = pa::launch_mfma(p, (int)g.D, g.kv_dtype, pl.qw, pl.split, s);
         if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma) launch: %s", hipGetErrorString(e));
@@ -408,7 +465,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     g_stats.last_t = (uint64_t)pl.part_tokens;
     g_stats.last_np = (uint64_t)pl.n_part;
     g_stats.last_variant = (uint64_t)pl.variant;
-    g_stats.last_schedule = PA_SCHEDULE_PARTITIONS;
+    g_stats.last_schedule = pl.fit ? PA_SCHEDULE_FITTED : PA_SCHEDULE_PARTITIONS;
     return PA_OK;
 }
 
@@ -547,9 +604,9 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
         if (opts->variant != PA_VARIANT_AUTO && opts->variant != PA_VARIANT_MFMA)
             return fail(PA_ENOTSUP, "several-query attention runs on the MFMA kernel only");
         if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
-        if (opts->schedule == PA_SCHEDULE_BALANCED)
-            return fail(PA_ENOTSUP, "several-query attention uses the partition schedule");
-        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_STAGED)
+        if (opts->schedule == PA_SCHEDULE_BALANCED || opts->schedule == PA_SCHEDULE_FITTED)
+            return fail(PA_ENOTSUP, "several-query attention uses the partition or staged schedule");
+        if (opts->schedule < PA_SCHEDULE_AUTO || opts->schedule > PA_SCHEDULE_FITTED)
             return fail(PA_EINVAL, "unknown schedule %d", opts->schedule);
         if (opts->schedule == PA_SCHEDULE_STAGED && opts->partition_tokens > 0)
             return fail(PA_EINVAL, "the staged schedule has no partitions (partition_tokens must be 0)");

@@ -34,6 +34,11 @@ struct DecodeParams {
     const int32_t* qstart;                                  // several queries: rows of sequence b [B + 1]
     int   q_rows;                                           // several queries: rows of q and out
     int   n_slots;                                          // several queries: query-block slots in the grid
+    int*  fit_part;                                         // fitted partitions: the size chosen on the device
+                                                            // (written by workgroup 0, read by the merge); else null
+    int   fit_lo;                                           // fitted partitions: smallest size (multiple of 64)
+    int   fit_target;                                       // fitted partitions: workgroups live partitions may fill
+    int   n_wg;                                             // fitted partitions: workgroups in the grid
     float scale_log2;                                       // scale * log2(e)
 };
 
@@ -218,48 +223,78 @@ __device__ __forceinline__ void page_slot(const DecodeParams& p, int t, int& lp,
     }
 }
 
-// Log-sum-exp merge of n split partials (o_p fp32 rows of D, lse_p base 2)
-// at slots first, first + step, ... into the output row at element offset
-// out_off (in the output's type), by 64 threads
-// holding D / 64 elements each.  Partials are read four at a time with
-// their lse and o rows together, so a merge of up to four costs one round
-// trip to memory; the running maximum rescales between batches.  n == 0
-// writes zeros.
+// Running log-sum-exp merge of split partials (o_p fp32 rows of D, lse_p
+// base 2), by 64 threads holding D / 64 elements each.  Partials are added
+// four at a time, with their lse and o rows read together; the running
+// maximum rescales between batches.
 template <int D>
-__device__ __forceinline__ void merge_partials(const DecodeParams& p, int64_t first, int64_t step, int n,
-                                               int64_t out_off) {
-    constexpr int EPT = D / 64;
+struct LseMerge {
+    static constexpr int EPT = D / 64;
     typedef float vec_t __attribute__((ext_vector_type(EPT)));
-    const int t = threadIdx.x;
     float M = -INFINITY, wsum = 0.f;
     vec_t o = {};
-    for (int i0 = 0; i0 < n; i0 += 4) {
-        float l[4];
-        vec_t v[4];
+
+    // Read slots first + (i0 + j) * step, j < 4, clamped to slot n_read - 1
+    // (n_read >= 1 slots exist there).
+    __device__ __forceinline__ static void read(const DecodeParams& p, int64_t first, int64_t step, int i0,
+                                                int n_read, float (&l)[4], vec_t (&v)[4]) {
+        const int t = threadIdx.x;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int i = min(i0 + j, n - 1);           // in range; extra entries are ignored
-            const int64_t slot = first + (int64_t)i * step;
-            l[j] = i0 + j < n ? p.part_lse[slot] : -INFINITY;
+            const int64_t slot = first + (int64_t)min(i0 + j, n_read - 1) * step;
+            l[j] = p.part_lse[slot];
             v[j] = *reinterpret_cast<const vec_t*>(p.part_o + slot * D + t * EPT);
         }
-        const float mb = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
-        if (mb == -INFINITY) continue;
+    }
+    // Add the first `live` (0..4) of a batch; the others are ignored whatever
+    // they hold (selected away, never multiplied by a zero weight).
+    __device__ __forceinline__ void add(const float (&l)[4], const vec_t (&v)[4], int live) {
+        float lj[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lj[j] = j < live ? l[j] : -INFINITY;
+        const float mb = fmaxf(fmaxf(lj[0], lj[1]), fmaxf(lj[2], lj[3]));
+        if (mb == -INFINITY) return;
         const float mn = fmaxf(M, mb);
         const float a = fast_exp2(M - mn);
         wsum *= a;
         o *= a;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float w = fast_exp2(l[j] - mn);
-            wsum += w;
-            o += w * v[j];
+            if (j < live && lj[j] != -INFINITY) {
+                const float w = fast_exp2(lj[j] - mn);
+                wsum += w;
+                o += w * v[j];
+            }
         }
         M = mn;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    // Batches from partial i0 on, up to partial n.
+    __device__ __forceinline__ void add_range(const DecodeParams& p, int64_t first, int64_t step, int i0, int n) {
+        for (; i0 < n; i0 += 4) {
+            float l[4];
+            vec_t v[4];
+            read(p, first, step, i0, n, l, v);
+            add(l, v, n - i0);
+        }
+    }
+    // Normalised row into the output at element offset out_off (n == 0 writes zeros).
+    __device__ __forceinline__ void store(const DecodeParams& p, int64_t out_off) const {
+        const int t = threadIdx.x;
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-    for (int e = 0; e < EPT; e += 2) store2(p.out, p.out_dtype, out_off + t * EPT + e, o[e] * inv, o[e + 1] * inv);
+        for (int e = 0; e < EPT; e += 2)
+            store2(p.out, p.out_dtype, out_off + t * EPT + e, o[e] * inv, o[e + 1] * inv);
+    }
+};
+
+// Log-sum-exp merge of n split partials at slots first, first + step, ...
+// into the output row at element offset out_off (in the output's type).
+template <int D>
+__device__ __forceinline__ void merge_partials(const DecodeParams& p, int64_t first, int64_t step, int n,
+                                               int64_t out_off) {
+    LseMerge<D> m;
+    m.add_range(p, first, step, 0, n);
+    m.store(p, out_off);
 }
 
 }  // namespace pa

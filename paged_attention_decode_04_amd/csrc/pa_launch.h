@@ -62,6 +62,12 @@ hipError_t launch_prefill_staged(const DecodeParams& p, int head_dim, int kv_dty
 // KV-cache append (one workgroup per sequence).
 hipError_t launch_append(const AppendParams& a, hipStream_t s);
 
+// Fitted partitions (matrix-core decode): the partition size is chosen per
+// call on the device from the sequence lengths, so that the live partitions
+// fill a given number of workgroups; every workgroup reads all lengths, so
+// the batch is bounded.
+constexpr int kFitMaxBatch = 256;
+
 // Log-sum-exp merge of split partials into bf16 output.
 hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s);
 

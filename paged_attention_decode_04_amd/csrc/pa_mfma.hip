@@ -37,6 +37,138 @@
 namespace pa {
 
 // ---------------------------------------------------------------------------
+// Fitted partitions.  The partition size T is chosen per call from the
+// sequence lengths on the device: the smallest multiple of 64 in [fit_lo,
+// part_tokens] whose partitions, n_qb * sum_b ceil(L_b / T), fit in
+// fit_target workgroups (part_tokens when none does).  The live (partition,
+// sequence, query block) triples are then numbered partition-major, query
+// block fastest -- the order of the fixed-partition grid with the dead
+// triples left out -- and workgroup x takes triple x, so no workgroup of the
+// grid waits behind partitions that have nothing to do.  Every wave computes
+// the same result from the same lengths (lane i holds sequences i, i + 64,
+// ...; at most kFitMaxBatch).  Returns false for a workgroup past the last
+// triple.
+
+// Wave-wide integer sum / maximum, every lane gets it: DPP inside 16-lane
+// rows, then lane swaps across rows.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i(int v, Op op) {
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppQuadSwap1, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppQuadSwap2, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false));
+    v = op(v, __builtin_amdgcn_update_dpp(0, v, kDppRowMirror, 0xF, 0xF, false));
+    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = op((int)r[0], (int)r[1]);
+    r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return op((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+    return wave_reduce_i(v, [](int a, int c) { return a + c; });
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+    return wave_reduce_i(v, [](int a, int c) { return a > c ? a : c; });
+}
+
+constexpr int kFitChunks = kFitMaxBatch / 64;
+
+// Lane i's lengths: sequences i, i + 64, ... (0 past the batch).  Issued
+// before the prologue's other reads, so they are in flight together.
+__device__ __forceinline__ void fit_lengths(const DecodeParams& p, int (&len)[kFitChunks]) {
+    const int lane = threadIdx.x & 63;
+    const int nc = (p.B + 63) >> 6;
+#pragma unroll
+    for (int c = 0; c < kFitChunks; ++c) {
+        const int bb = c * 64 + lane;
+        len[c] = (c < nc && bb < p.B) ? p.ctx[bb] : 0;
+    }
+}
+
+__device__ __forceinline__ bool fit_locate(const DecodeParams& p, int x, int (&len)[kFitChunks], int& b, int& qb,
+                                           int& part, int& T, int& L) {
+    constexpr int NC = kFitChunks;
+    const int lane = threadIdx.x & 63;
+    const int n_qb = p.Hq / p.qw;
+    const int cap = p.max_blk * p.P;
+    const int nc = (p.B + 63) >> 6;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) len[c] = clampi(len[c], 0, cap);
+    // ceil(len / t) for 0 <= len < 2^24, 64 <= t: a float estimate off by at
+    // most one, made exact by two integer corrections
+    auto ceil_div = [](int len, int t, float rcp) {
+        int d = (int)((float)len * rcp);
+        d -= d * t > len ? 1 : 0;
+        d += (d + 1) * t <= len ? 1 : 0;        // d = floor(len / t)
+        return d + (d * t < len ? 1 : 0);
+    };
+    auto count = [&](int t) {
+        const float rcp = 1.f / (float)t;
+        int s = 0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (c < nc) s += ceil_div(len[c], t, rcp);
+        // uniform by construction; saying so keeps the search on scalar
+        // branches, so every reduction runs with the whole wave active
+        return __builtin_amdgcn_readfirstlane(wave_sum_i(s) * n_qb);
+    };
+    int lo = p.fit_lo >> 6, hi = p.part_tokens >> 6;   // sizes in units of 64 tokens
+    // The count only falls as the size grows: when one step below the
+    // largest size is already too many partitions, the largest is the answer
+    // (the common case for batches of even lengths: one probe, no search).
+    if (lo < hi && count((hi - 1) << 6) > p.fit_target) lo = hi;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (count(mid << 6) <= p.fit_target) hi = mid; else lo = mid + 1;
+    }
+    T = __builtin_amdgcn_readfirstlane(lo << 6);
+    if (x == 0 && threadIdx.x == 0) *p.fit_part = T;
+    // n_b partitions per sequence; before(j) = n_qb * sum_b min(n_b, j) live
+    // triples precede partition index j
+    int nb[NC];
+    int top = 0, tot = 0;
+    const float rcp = 1.f / (float)T;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        nb[c] = c < nc ? ceil_div(len[c], T, rcp) : 0;
+        top = max(top, nb[c]);
+        tot += nb[c];
+    }
+    if (x >= __builtin_amdgcn_readfirstlane(wave_sum_i(tot) * n_qb)) return false;   // past the last live triple
+    top = __builtin_amdgcn_readfirstlane(wave_max_i(top));
+    auto before = [&](int j) {
+        int s = 0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (c < nc) s += min(nb[c], j);
+        return __builtin_amdgcn_readfirstlane(wave_sum_i(s) * n_qb);
+    };
+    // partition index: the largest j < top with before(j) <= x
+    int a = 0, z = top - 1;
+    while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (before(mid) <= x) a = mid; else z = mid - 1;
+    }
+    part = a;
+    const int y = x - before(part);
+    qb = y % n_qb;
+    int k = y / n_qb;                           // the k-th sequence (from 0) with n_b > part
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (c >= nc) break;
+        const uint64_t m = __ballot(nb[c] > part);
+        const int cnt = __builtin_popcountll(m);
+        if (k < cnt) {
+            const bool hit = ((m >> lane) & 1u) && __builtin_popcountll(m & ((1ull << lane) - 1ull)) == k;
+            const int pos = __builtin_ctzll(__ballot(hit));
+            b = c * 64 + pos;
+            L = __builtin_amdgcn_readlane(len[c], pos);
+            return true;
+        }
+        k -= cnt;
+    }
+    return false;
+}
+
+// ---------------------------------------------------------------------------
 // Fixed partitions: one workgroup per (query block, sequence, partition of
 // part_tokens tokens).  Flat grid, query block fastest and partition slowest:
 // consecutive workgroups (dealt round-robin to the XCDs) cover different
@@ -47,18 +179,16 @@ template <int D, bool SPLIT, bool PAGE16, bool HALF, int NBUF, typename KV>
 __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p) {
     constexpr int KK = TileFrag<D>::KK;
     constexpr int NO = D / 16;                  // O^T accumulator tiles
-    const int n_qb = p.Hq / p.qw;
-    const int qb = blockIdx.x % n_qb;
-    const int rest = blockIdx.x / n_qb;
-    const int b = rest % p.B;
-    const int part = rest / p.B;
     const int qw = p.qw;                        // query heads of this workgroup (<= 16)
-    const int h0 = qb * qw;
+    const int n_qb = p.Hq / qw;
+    int qb = blockIdx.x % n_qb;
+    int b = (blockIdx.x / n_qb) % p.B;
+    int part = blockIdx.x / n_qb / p.B;
+    int T = p.part_tokens;                      // tokens per partition
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int n = lane & 15, q = lane >> 4;
-    const int g = h0 / (p.Hq / p.Hkv);
 
     // Page ids of the partition's token range are fetched without waiting for
     // the sequence length (entries past the sequence's end are never used),
@@ -70,19 +200,63 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
         L = clampi(p.ctx[b], 0, p.max_blk * p.P);
         window_bounds(p, L, t_begin, t_base);
     }
-    const int ts = t_base + part * p.part_tokens;
     extern __shared__ int s_pages[];
-    int pg0, lp_hi, unused;
-    page_slot(p, ts, pg0, unused);
-    page_slot(p, ts + p.part_tokens - 1, lp_hi, unused);
-    fetch_pages(p, b, pg0, lp_hi, s_pages, tid);
-    // Q does not depend on the length either: its load goes out with the
-    // others (a partition past the end drops it).
     u32x4 qop[KK];
-    load_q<D, HALF, KV>(p, b, h0, qw, n, q, qop);
-    if (p.window <= 0) L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+    int len[kFitChunks];
+    if (p.fit_part && wave == 0) fit_lengths(p, len);
+    int ts, pg0;
+    auto fetch = [&]() {
+        ts = t_base + part * T;
+        int lp_hi, unused;
+        page_slot(p, ts, pg0, unused);
+        page_slot(p, ts + T - 1, lp_hi, unused);
+        fetch_pages(p, b, pg0, lp_hi, s_pages, tid);
+        // Q does not depend on the length either: its load goes out with the
+        // others (a partition past the end drops it).
+        load_q<D, HALF, KV>(p, b, qb * qw, qw, n, q, qop);
+    };
+    fetch();
+    if (p.fit_part) {
+        // Fitted partitions (never with a window).  The fetch above took the
+        // fixed-partition slot of this workgroup; when the lengths keep the
+        // largest size and every sequence has as many partitions, that is
+        // the triple it is given, else the fetch is made again (each thread
+        // rewrites the page-id entries it wrote, so no barrier is needed
+        // before the one that precedes their use).  Wave 0 alone reads the
+        // lengths and locates the triple (one read of the lengths per
+        // workgroup); the others take it from LDS.
+        __shared__ int s_fit[6];                // b, qb, part, T, L, state
+        if (wave == 0) {
+            int fb = 0, fqb = 0, fpart = 0, fT = T, fL = 0;
+            const bool live = fit_locate(p, (int)blockIdx.x, len, fb, fqb, fpart, fT, fL);
+            if (lane == 0) {
+                s_fit[0] = fb;
+                s_fit[1] = fqb;
+                s_fit[2] = fpart;
+                s_fit[3] = fT;
+                s_fit[4] = fL;
+                // 0: past the last triple, 1: the slot fetched, 2: another one
+                s_fit[5] = !live ? 0 : (fb == b && fqb == qb && fpart == part && fT == T) ? 1 : 2;
+            }
+        }
+        __syncthreads();
+        const int state = __builtin_amdgcn_readfirstlane(s_fit[5]);
+        if (state == 0) return;                 // the whole workgroup
+        L = __builtin_amdgcn_readfirstlane(s_fit[4]);
+        if (state == 2) {
+            b = __builtin_amdgcn_readfirstlane(s_fit[0]);
+            qb = __builtin_amdgcn_readfirstlane(s_fit[1]);
+            part = __builtin_amdgcn_readfirstlane(s_fit[2]);
+            T = __builtin_amdgcn_readfirstlane(s_fit[3]);
+            fetch();
+        }
+    } else if (p.window <= 0) {
+        L = clampi(p.ctx[b], 0, p.max_blk * p.P);
+    }
     if (ts >= L && part > 0) return;
-    const int te = min(L, ts + p.part_tokens);
+    const int h0 = qb * qw;
+    const int g = h0 / (p.Hq / p.Hkv);
+    const int te = min(L, ts + T);
     const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
     __syncthreads();
 
@@ -347,7 +521,7 @@ bool mfma_lean_supported(int head_dim, int qw, int kv_dtype) {
 
 template <int D, bool SPLIT, bool PAGE16, typename KV>
 static hipError_t launch_mfma_t(const DecodeParams& p, int qw, hipStream_t s) {
-    dim3 grid((uint32_t)((int64_t)p.n_part * (p.Hq / qw) * p.B));
+    dim3 grid(p.fit_part ? (uint32_t)p.n_wg : (uint32_t)((int64_t)p.n_part * (p.Hq / qw) * p.B));
     // Tiles in flight per wave: three 8 KB tiles at d128, two at d256 and
     // d512 (a d512 tile is 32 KB and 128 registers; the accumulators go to
     // AGPRs, one wave per SIMD).

@@ -283,11 +283,22 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
 template <int D>
 __global__ __launch_bounds__(64) void pa_lse_merge_kernel(DecodeParams p) {
     const int h = blockIdx.x, b = blockIdx.y;
+    const int64_t first = ((int64_t)b * p.Hq + h) * p.n_part;
+    // The first four partials (those of the n_part slots that exist) are read
+    // with the length, not after it: one round trip to memory for most rows.
+    LseMerge<D> m;
+    float l[4];
+    typename LseMerge<D>::vec_t v[4];
+    LseMerge<D>::read(p, first, 1, 0, p.n_part, l, v);
+    // fitted partitions: the size the decode kernel chose for this call
+    const int T = p.fit_part ? *p.fit_part : p.part_tokens;
     const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     int t_begin, t_base;
     window_bounds(p, L, t_begin, t_base);
-    const int n_used = (L - t_base + p.part_tokens - 1) / p.part_tokens;
-    merge_partials<D>(p, ((int64_t)b * p.Hq + h) * p.n_part, 1, n_used, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
+    const int n_used = min((L - t_base + T - 1) / T, p.n_part);
+    m.add(l, v, n_used);
+    m.add_range(p, first, 1, 4, n_used);
+    m.store(p, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
 }
 
 // ------------------------------------------------------------------ launch

@@ -148,14 +148,29 @@ def test_opts_are_validated():
     assert check(args(), o) == pa.PA_EINVAL
     o = pa.make_opts("valu", -5)
     assert check(args(), o) == pa.PA_EINVAL
-    o = pa.make_opts("mfma", 0, 4)
+    o = pa.make_opts("mfma", 0, 5)
     assert check(args(), o) == pa.PA_EINVAL
     o = pa.make_opts("mfma", 0, "staged")                 # several queries only
     assert check(args(), o) == pa.PA_ENOTSUP
     assert check(args(), pa.make_opts(window=-1)) == pa.PA_EINVAL
     assert check(args(), pa.make_opts(window=7)) == pa.PA_OK
-    for sched in ("auto", "partitions", "balanced"):
+    for sched in ("auto", "partitions", "balanced", "fitted"):
         assert check(args(), pa.make_opts("mfma", 0, sched)) == pa.PA_OK
+
+
+def test_fitted_schedule_preconditions():
+    """Fitted partitions: MFMA only, no window, no partition size given, at
+    most 256 sequences (every workgroup reads all lengths)."""
+    fit = lambda **kw: pa.make_opts(schedule="fitted", **kw)
+    assert check(args(), fit(variant="mfma")) == pa.PA_OK
+    assert check(args(), fit(variant="valu")) == pa.PA_ENOTSUP
+    assert "fitted" in pa.last_error()
+    assert check(args(), fit(window=64)) == pa.PA_ENOTSUP
+    assert check(args(), fit(partition_tokens=256)) == pa.PA_ENOTSUP
+    assert check(args(B=256), fit()) == pa.PA_OK
+    assert check(args(B=257), fit()) == pa.PA_ENOTSUP
+    assert check(args(), fit(shares=1024)) == pa.PA_OK
+    assert check(args(), fit(shares=1025)) == pa.PA_EINVAL
 
 
 def test_balanced_schedule_needs_mfma_and_bounded_batch():
@@ -230,9 +245,24 @@ def test_workspace_bytes():
     auto = pa.pa_decode_workspace_bytes(64, 64, 8, 128, 2048, 16, None)
     valu = HDR + rnd(64 * 64 * 32 * 128 * 4) + rnd(64 * 64 * 32 * 4)
     assert auto == max(big, valu)
+    # fitted partitions when asked for: 16 sequences x 8 query blocks of up
+    # to 1152 tokens give a largest size of 576, a smallest of 256 (max(256,
+    # 576 / 4)), so 5 partial slots, plus the slot of the size picked
+    fit = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, pa.make_opts("mfma", 0, "fitted"))
+    assert fit == HDR + rnd(16 * 16 * 5 * 128 * 4) + rnd(16 * 16 * 5 * 4) + 256
+    # the automatic choice keeps the 2 fixed partitions there (fewer than 4)
     small = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, pa.make_opts("mfma"))
     assert small == pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16,
                                                  pa.make_opts("mfma", 0, "partitions"))
+    assert small == HDR + rnd(16 * 16 * 2 * 128 * 4) + rnd(16 * 16 * 2 * 4)
+    # one 1152-token sequence: the fixed size is already the floor (256), so
+    # the automatic choice keeps fixed partitions (5 of them)
+    one = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma"))
+    assert one == HDR + rnd(16 * 5 * 128 * 4) + rnd(16 * 5 * 4)
+    # 32 sequences x 2 query blocks in a 4096-token table (head_dim 256):
+    # 4 fixed partitions of 1024, so the automatic choice fits them
+    hd = pa.pa_decode_workspace_bytes(32, 8, 2, 256, 128, 32, pa.make_opts("mfma"))
+    assert hd == pa.pa_decode_workspace_bytes(32, 8, 2, 256, 128, 32, pa.make_opts("mfma", 0, "fitted"))
     # a window bounds the span a sequence's work covers (W + 15 tokens): the
     # same large call with a 4096-token window falls below the balanced
     # threshold and splits into ceil(4111 / 4096) = 2 partitions of 4096
@@ -242,6 +272,12 @@ def test_workspace_bytes():
     n = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma", 64))
     assert n == HDR + rnd(1 * 16 * 18 * 128 * 4) + rnd(1 * 16 * 18 * 4)
     assert pa.pa_decode_workspace_bytes(1, 15, 8, 128, 4, 32, None) == 0
+    # fitted partitions: the fixed schedule's size T (here 4096 * 64 groups /
+    # 256 = 1024 tokens) is the largest the device may pick, max(128, T / 4)
+    # = 256 the smallest, so the partial slots cover 4096 / 256 = 16
+    # partitions; one more 256-byte slot holds the size picked
+    n = pa.pa_decode_workspace_bytes(32, 8, 2, 256, 128, 32, pa.make_opts("mfma", 0, "fitted"))
+    assert n == HDR + rnd(32 * 8 * 16 * 256 * 4) + rnd(32 * 8 * 16 * 4) + 256
 
 
 def test_stats_roundtrip():
@@ -345,7 +381,8 @@ def test_prefill_validation():
     assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, "balanced")) == pa.PA_ENOTSUP
     assert call_prefill(ts, out, dims, pa.make_opts(window=-2)) == pa.PA_EINVAL
     assert call_prefill(ts, out, dims, pa.make_opts("auto", 64, "staged")) == pa.PA_EINVAL   # no partitions
-    assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, 4)) == pa.PA_EINVAL
+    assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, "fitted")) == pa.PA_ENOTSUP
+    assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, 5)) == pa.PA_EINVAL
     ts4, out4, dims4 = prefill_args(R=0, B=2)
     ts4[5] = torch.zeros(3, dtype=torch.int32)
     assert call_prefill(ts4, out4, dims4) == pa.PA_OK           # no rows: nothing to do

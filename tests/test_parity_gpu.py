@@ -19,14 +19,20 @@ from workloads import WORKLOADS, custom, make_inputs, to_device
 pytestmark = pytest.mark.gpu
 
 # Kernel variant and work schedule: vector-ALU kernel on fixed partitions,
-# MFMA kernel on fixed partitions, MFMA kernel on balanced shares.
-VARIANTS = ["valu", "mfma", "mfma-bal"]
+# MFMA kernel on fixed partitions, MFMA kernel on balanced shares, MFMA
+# kernel on fitted partitions (size picked on the device; no window).
+VARIANTS = ["valu", "mfma", "mfma-bal", "mfma-fit"]
+VARIANTS_W = ["valu", "mfma", "mfma-bal"]            # those that take a window
 _MODE = {"valu": ("valu", "partitions"), "mfma": ("mfma", "partitions"),
-         "mfma-bal": ("mfma", "balanced")}
+         "mfma-bal": ("mfma", "balanced"), "mfma-fit": ("mfma", "fitted")}
 # Share counts the balanced schedule is exercised with: automatic, a single
 # share (every group written directly), and counts whose boundaries fall
 # mid-group, mid-sequence and on 16-token tiles of different sequences.
 SHARES = (0, 1, 3, 37, 1024)
+# Workgroup targets of the fitted schedule: automatic (one per compute unit),
+# one (no size fits: the largest is taken), a few, and more than any
+# partitioning needs (the smallest size is taken).
+FIT_TARGETS = (0, 1, 5, 64, 1024)
 
 
 def bits(t):
@@ -45,6 +51,8 @@ def knobs(variant, tokens):
     """Split settings to sweep: partition sizes, or share counts when balanced."""
     if _MODE[variant][1] == "balanced":
         return [dict(shares=n) for n in SHARES]
+    if _MODE[variant][1] == "fitted":
+        return [dict(shares=n) for n in FIT_TARGETS]
     return [dict(partition_tokens=T) for T in tokens]
 
 
@@ -59,8 +67,10 @@ def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0, o
     s = pa.pa_get_stats()
     assert s["calls"] == 1
     assert s[f"{kernel}_launches"] == 1, s
-    assert s["last_schedule"] == (pa.PA_SCHEDULE_BALANCED if schedule == "balanced"
-                                  else pa.PA_SCHEDULE_PARTITIONS), s
+    expect = {"balanced": pa.PA_SCHEDULE_BALANCED, "partitions": pa.PA_SCHEDULE_PARTITIONS,
+              # a call that does not split runs one partition per sequence
+              "fitted": pa.PA_SCHEDULE_FITTED if s["split_calls"] else pa.PA_SCHEDULE_PARTITIONS}
+    assert s["last_schedule"] == expect[schedule], s
     if schedule == "balanced":
         assert s["balanced_calls"] == 1 and s["merge_launches"] == 1, s
         if shares:
@@ -225,7 +235,7 @@ def test_split_sizes_agree(variant):
         y, s = gpu_run(d, variant=variant, **kn)
         seen.add(s["split_calls"])
         assert_parity(y, ref, f"{kn}")
-    assert seen == ({1} if variant == "mfma-bal" else {0, 1})
+    assert seen == ({1} if variant in ("mfma-bal", "mfma-fit") else {0, 1})
 
 
 # ------------------------------------------------------------------ layouts
@@ -302,7 +312,7 @@ def test_device_errors_do_not_stick():
     assert_parity(y, oracle_run(inp), "after error")
 
 
-@pytest.mark.parametrize("schedule", ["partitions", "balanced"])
+@pytest.mark.parametrize("schedule", ["partitions", "balanced", "fitted"])
 def test_graph_capture_replays_match_eager(schedule):
     """Calls captured in a HIP graph: every replay, with eager work and
     synchronisations in between, equals the eager result bit for bit (the
@@ -382,7 +392,7 @@ def test_balanced_workspace_reuse_and_counters():
     NP, P, Hkv, _ = k.shape
     n = max(pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, pa.make_opts(var, T, sch))
             for var, sch, T in (("mfma", "partitions", 0), ("mfma", "balanced", 0), ("mfma", "partitions", 256),
-                                ("valu", "partitions", 256)))
+                                ("valu", "partitions", 256), ("mfma", "fitted", 0)))
     raw = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
     off = (-raw.data_ptr()) % 256
     ws = raw[off:off + n]
@@ -392,7 +402,9 @@ def test_balanced_workspace_reuse_and_counters():
             ("mfma", "balanced", 0, 0), ("mfma", "partitions", 0, 0), ("mfma", "balanced", 256, 0),
             ("mfma", "partitions", 0, 256), ("mfma", "balanced", 7, 0), ("valu", "partitions", 0, 256),
             ("mfma", "balanced", 256, 0), ("mfma", "partitions", 0, 0), ("mfma", "partitions", 0, 1024),
-            ("mfma", "balanced", 1024, 0), ("mfma", "partitions", 0, 256), ("mfma", "balanced", 256, 0)]):
+            ("mfma", "balanced", 1024, 0), ("mfma", "partitions", 0, 256), ("mfma", "balanced", 256, 0),
+            ("mfma", "fitted", 0, 0), ("mfma", "fitted", 3, 0), ("mfma", "balanced", 256, 0),
+            ("mfma", "fitted", 1024, 0), ("mfma", "partitions", 0, 0)]):
         out = torch.full_like(q, float("nan"))
         pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, variant=var,
                   schedule=sch, shares=shares, partition_tokens=T, workspace=ws)
@@ -420,7 +432,7 @@ def poison_before_window(inp, W):
     return workloads.Inputs(inp.w, inp.q, k, v, inp.layout)
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS_W)
 @pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 16), (256, 8, 2, 32), (128, 64, 8, 16),
                                         (128, 16, 4, 7)])
 def test_window_parity_poisoned(variant, D, Hq, Hkv, P):
@@ -439,7 +451,7 @@ def test_window_parity_poisoned(variant, D, Hq, Hkv, P):
             assert_parity(y, ref, f"W={W} {kn}")
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", VARIANTS_W)
 def test_window_covering_every_sequence_is_bitwise_unwindowed(variant):
     inp = make_inputs("hd256_gqa4", seed=5)
     d = to_device(inp)
@@ -564,7 +576,7 @@ def test_dtype_parity_poisoned(variant, qt, kt, ot, D):
         y, _ = gpu_run(d, variant=variant, out_dtype=TORCH_DT[ot], **kn)
         assert np.all(np.isfinite(y.astype(np.float64) if ot != "bf16" else workloads_f32(y)))
         assert_parity(y, ref, f"q {qt} kv {kt} out {ot} D={D} {kn}")
-    for W in (7, 500):
+    for W in ((7, 500) if variant in VARIANTS_W else ()):
         y, _ = gpu_run(d, variant=variant, out_dtype=TORCH_DT[ot], window=W)
         assert_parity(y, oracle_run(inp, window=W), f"q {qt} kv {kt} out {ot} D={D} W={W}")
 
