@@ -365,6 +365,30 @@ def test_balanced_max_batch_ragged():
         assert_parity(y, ref, f"B=4096 shares={n}")
 
 
+# ------------------------------------------------------------------ fitted partitions
+@pytest.mark.parametrize("B,Hq,Hkv,D", [(65, 4, 1, 128), (200, 4, 1, 128), (100, 8, 2, 256)])
+def test_fitted_many_sequences_ragged(B, Hq, Hkv, D):
+    """Batches past one wave's 64 lanes (each lane holds sequences i, i + 64,
+    ...): the size search and the triple numbering run over several chunks
+    of lengths, with empty sequences and lengths on and off page boundaries,
+    for workgroup targets from one (largest size) to more than any partitioning
+    needs (smallest size)."""
+    rng = np.random.default_rng(B + D)
+    lens = rng.integers(0, 2001, B)
+    lens[rng.choice(B, 5, replace=False)] = 0
+    lens[rng.choice(B, 5, replace=False)] = 2000
+    lens[rng.choice(B, 5, replace=False)] = 1
+    w = custom(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=16,
+               ctx=tuple(int(x) for x in lens))
+    inp = make_inputs(w, seed=B, poison_unused=True)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for n in FIT_TARGETS + (256, 300):
+        y, s = gpu_run(d, variant="mfma-fit", shares=n)
+        assert s["split_calls"] == 1, s
+        assert_parity(y, ref, f"B={B} D={D} target={n}")
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 8), (256, 32, 4), (128, 64, 4)])
 def test_balanced_share_sweep(D, Hq, Hkv):
     """Many share counts over a length mix with one long sequence: share
