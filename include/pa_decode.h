@@ -105,7 +105,10 @@ typedef struct pa_tensor {
  * sequence or, on the MFMA variant, as equal shares of all sequences' work
  * (chosen automatically for large calls: at most 4096 sequences and at
  * least 262144 units of (sequence, query block, 16 tokens of capacity
- * MaxBlk * P, or of the window)); partial results are
+ * MaxBlk * P, or of the window)), or as partitions whose size the kernel
+ * fits to the actual lengths (chosen automatically, without a window and
+ * for at most 256 sequences, where fixed partitions would cut the tables
+ * into 4 or more and the tables hold at least 192 MB of K/V); partial results are
  * merged with the log-sum-exp rule by a second kernel.  The library keeps a
  * per-device workspace for the partials, grown on demand with hipMalloc and
  * freed by pa_release(); calls that use it must not overlap in time on one
@@ -181,7 +184,10 @@ int pa_cache_append(const pa_tensor* k_new,
                                       context lengths, so that the partitions
                                       fill `shares` workgroups (0 = one per
                                       compute unit); partitions of no work are
-                                      never launched                          */
+                                      never launched.  The workspace keeps, per
+                                      workgroup, the partition it took in the
+                                      last call as a starting guess for the
+                                      next; any content there is valid.       */
 
 typedef struct pa_opts {
     int32_t variant;            /* PA_VARIANT_*                                */

@@ -74,6 +74,7 @@ struct Plan {
 constexpr int kFitMinTokens = 256;
 constexpr int kFitRange = 4;
 constexpr int kFitAutoMinParts = 4;
+constexpr double kFitAutoMinBytes = 192e6;
 
 // Balanced schedule: at most this many shares (workgroups) per call, so the
 // workspace size does not depend on the device it runs on.
@@ -288,7 +289,15 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         // units idle (measured: 32 sequences of 512..4096 tokens in a
         // 4096-token table, decode kernel 31.7 -> 29.0 us; 16 sequences of
         // 1024..1152 tokens in a 1152-token table, 14.4 -> 15.4 us).
-        if (sched == PA_SCHEDULE_AUTO && (pl.fit_lo == T || pl.n_part < kFitAutoMinParts)) pl.fit = false;
+        // The gain grows with the call, the cost does not: the KV the
+        // block tables can hold must also take at least ~24 us at HBM peak
+        // (measured: the same batch at half the lengths, 2048-token tables,
+        // ran 20.6 us on fixed and 21.3 us on fitted partitions).
+        const double cap_bytes = (double)g.B * (double)max_ctx * (double)g.Hkv * (double)g.D * 2.0 *
+                                 (double)elem_size(g.kv_dtype);
+        if (sched == PA_SCHEDULE_AUTO &&
+            (pl.fit_lo == T || pl.n_part < kFitAutoMinParts || cap_bytes < kFitAutoMinBytes))
+            pl.fit = false;
     }
     if (pl.fit) {
         pl.fit_grid = (int64_t)pl.n_part * groups;
@@ -302,8 +311,10 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         pl.lse_offset = pl.o_offset + align_up(n * g.D * sizeof(float), kAlign);
         pl.ws_bytes = pl.lse_offset + align_up(n * sizeof(float), kAlign);
         if (pl.fit) {
+            // the size picked, then one hint (the triple taken by the same
+            // workgroup in the previous call) per workgroup the grid can have
             pl.fit_offset = pl.ws_bytes;
-            pl.ws_bytes += kAlign;
+            pl.ws_bytes += kAlign + align_up((size_t)std::max<int64_t>(pl.fit_grid, kLeanMaxShares) * 16, kAlign);
         }
     }
     return pl;
@@ -442,6 +453,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     }
     if (pl.fit) {
         p.fit_part = reinterpret_cast<int*>(static_cast<char*>(ws) + pl.fit_offset);
+        p.fit_hint = reinterpret_cast<int*>(static_cast<char*>(ws) + pl.fit_offset + kAlign);
         p.fit_lo = pl.fit_lo;
         p.fit_target = opts && opts->shares > 0 ? opts->shares : cu_count(dev);
         p.n_wg = (int)std::max<int64_t>(pl.fit_grid, p.fit_target);

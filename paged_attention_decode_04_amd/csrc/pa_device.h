@@ -39,6 +39,9 @@ struct DecodeParams {
     int   fit_lo;                                           // fitted partitions: smallest size (multiple of 64)
     int   fit_target;                                       // fitted partitions: workgroups live partitions may fill
     int   n_wg;                                             // fitted partitions: workgroups in the grid
+    int*  fit_hint;                                         // fitted partitions: [n_wg][4] triple (b, query
+                                                            // block, partition, size) each workgroup took in
+                                                            // the previous call (a hint: checked before use)
     float scale_log2;                                       // scale * log2(e)
 };
 

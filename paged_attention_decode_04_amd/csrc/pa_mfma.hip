@@ -185,6 +185,21 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     int b = (blockIdx.x / n_qb) % p.B;
     int part = blockIdx.x / n_qb / p.B;
     int T = p.part_tokens;                      // tokens per partition
+    if (p.fit_part) {
+        // Fitted partitions: start from the triple this workgroup took in the
+        // previous call when it is a valid one (decode lengths grow by a token
+        // per step, so the plan seldom changes); else the fixed-grid slot.
+        const int4 h = *reinterpret_cast<const int4*>(p.fit_hint + 4 * (int64_t)blockIdx.x);
+        const int hb = __builtin_amdgcn_readfirstlane(h.x), hq = __builtin_amdgcn_readfirstlane(h.y);
+        const int hp = __builtin_amdgcn_readfirstlane(h.z), ht = __builtin_amdgcn_readfirstlane(h.w);
+        if (hb >= 0 && hb < p.B && hq >= 0 && hq < n_qb && ht >= p.fit_lo && ht <= p.part_tokens &&
+            (ht & 63) == 0 && hp >= 0 && (int64_t)hp * ht < (int64_t)p.max_blk * p.P) {
+            b = hb;
+            qb = hq;
+            part = hp;
+            T = ht;
+        }
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -218,9 +233,9 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     fetch();
     if (p.fit_part) {
         // Fitted partitions (never with a window).  The fetch above took the
-        // fixed-partition slot of this workgroup; when the lengths keep the
-        // largest size and every sequence has as many partitions, that is
-        // the triple it is given, else the fetch is made again (each thread
+        // hinted triple or the fixed-partition slot; when that is the triple
+        // this workgroup is given, nothing is fetched again, else the fetch
+        // is made again (each thread
         // rewrites the page-id entries it wrote, so no barrier is needed
         // before the one that precedes their use).  Wave 0 alone reads the
         // lengths and locates the triple (one read of the lengths per
@@ -237,6 +252,9 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
                 s_fit[4] = fL;
                 // 0: past the last triple, 1: the slot fetched, 2: another one
                 s_fit[5] = !live ? 0 : (fb == b && fqb == qb && fpart == part && fT == T) ? 1 : 2;
+                // the next call's hint (no triple: an invalid one)
+                *reinterpret_cast<int4*>(p.fit_hint + 4 * (int64_t)blockIdx.x) =
+                    live ? make_int4(fb, fqb, fpart, fT) : make_int4(-1, -1, -1, -1);
             }
         }
         __syncthreads();

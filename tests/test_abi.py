@@ -248,8 +248,9 @@ def test_workspace_bytes():
     # fitted partitions when asked for: 16 sequences x 8 query blocks of up
     # to 1152 tokens give a largest size of 576, a smallest of 256 (max(256,
     # 576 / 4)), so 5 partial slots, plus the slot of the size picked
+    # and one 16-byte hint per workgroup the grid can have (at least 1024)
     fit = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, pa.make_opts("mfma", 0, "fitted"))
-    assert fit == HDR + rnd(16 * 16 * 5 * 128 * 4) + rnd(16 * 16 * 5 * 4) + 256
+    assert fit == HDR + rnd(16 * 16 * 5 * 128 * 4) + rnd(16 * 16 * 5 * 4) + 256 + 1024 * 16
     # the automatic choice keeps the 2 fixed partitions there (fewer than 4)
     small = pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16, pa.make_opts("mfma"))
     assert small == pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16,
@@ -260,9 +261,13 @@ def test_workspace_bytes():
     one = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma"))
     assert one == HDR + rnd(16 * 5 * 128 * 4) + rnd(16 * 5 * 4)
     # 32 sequences x 2 query blocks in a 4096-token table (head_dim 256):
-    # 4 fixed partitions of 1024, so the automatic choice fits them
+    # 4 fixed partitions of 1024 and 268 MB of KV capacity, so the automatic
+    # choice fits them; in 2048-token tables (134 MB) it keeps them fixed
     hd = pa.pa_decode_workspace_bytes(32, 8, 2, 256, 128, 32, pa.make_opts("mfma"))
     assert hd == pa.pa_decode_workspace_bytes(32, 8, 2, 256, 128, 32, pa.make_opts("mfma", 0, "fitted"))
+    half = pa.pa_decode_workspace_bytes(32, 8, 2, 256, 64, 32, pa.make_opts("mfma"))
+    assert half == pa.pa_decode_workspace_bytes(32, 8, 2, 256, 64, 32, pa.make_opts("mfma", 0, "partitions"))
+    assert half != pa.pa_decode_workspace_bytes(32, 8, 2, 256, 64, 32, pa.make_opts("mfma", 0, "fitted"))
     # a window bounds the span a sequence's work covers (W + 15 tokens): the
     # same large call with a 4096-token window falls below the balanced
     # threshold and splits into ceil(4111 / 4096) = 2 partitions of 4096
@@ -273,11 +278,12 @@ def test_workspace_bytes():
     assert n == HDR + rnd(1 * 16 * 18 * 128 * 4) + rnd(1 * 16 * 18 * 4)
     assert pa.pa_decode_workspace_bytes(1, 15, 8, 128, 4, 32, None) == 0
     # fitted partitions: the fixed schedule's size T (here 4096 * 64 groups /
-    # 256 = 1024 tokens) is the largest the device may pick, max(128, T / 4)
+    # 256 = 1024 tokens) is the largest the device may pick, max(256, T / 4)
     # = 256 the smallest, so the partial slots cover 4096 / 256 = 16
-    # partitions; one more 256-byte slot holds the size picked
+    # partitions; one more 256-byte slot holds the size picked, then the
+    # workgroups' hints
     n = pa.pa_decode_workspace_bytes(32, 8, 2, 256, 128, 32, pa.make_opts("mfma", 0, "fitted"))
-    assert n == HDR + rnd(32 * 8 * 16 * 256 * 4) + rnd(32 * 8 * 16 * 4) + 256
+    assert n == HDR + rnd(32 * 8 * 16 * 256 * 4) + rnd(32 * 8 * 16 * 4) + 256 + 1024 * 16
 
 
 def test_stats_roundtrip():
