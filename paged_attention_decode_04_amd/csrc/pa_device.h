@@ -263,11 +263,10 @@ struct LseMerge {
         o *= a;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (j < live && lj[j] != -INFINITY) {
-                const float w = fast_exp2(lj[j] - mn);
-                wsum += w;
-                o += w * v[j];
-            }
+            const float w = fast_exp2(lj[j] - mn);      // 0 for an ignored slot
+            wsum += w;
+            const vec_t add = w * v[j];
+            o = j < live ? o + add : o;
         }
         M = mn;
     }
