@@ -179,7 +179,8 @@ int pa_cache_append(const pa_tensor* k_new,
                                       query blocks of one sequence, which share
                                       every K/V stage through LDS; no split   */
 #define PA_SCHEDULE_FITTED      4  /* MFMA only, no window, at most 256
-                                      sequences: split-KV partitions whose size
+                                      sequences, MaxBlk * P < 2^24 tokens:
+                                      split-KV partitions whose size
                                       the kernel picks per call from the
                                       context lengths, so that the partitions
                                       fill `shares` workgroups (0 = one per

@@ -195,11 +195,12 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
 }
 
 // Whether a call may take fitted partitions: the MFMA kernel, no window,
-// lengths few enough for every workgroup to read, and no partition size
-// given by the caller.
+// lengths few enough for every workgroup to read, block tables of fewer than
+// 2^24 tokens (the kernel's float-estimated divisions are exact below that),
+// and no partition size given by the caller.
 bool fit_allowed(const Geometry& g, const Plan& pl, const pa_opts* opts) {
-    return pl.variant == PA_VARIANT_MFMA && g.B <= pa::kFitMaxBatch && !(opts && opts->window > 0) &&
-           !(opts && opts->partition_tokens > 0);
+    return pl.variant == PA_VARIANT_MFMA && g.B <= pa::kFitMaxBatch && g.max_blk * g.P < pa::kFitMaxTokens &&
+           !(opts && opts->window > 0) && !(opts && opts->partition_tokens > 0);
 }
 
 // The automatic schedule takes fitted partitions where it would split them
@@ -381,8 +382,8 @@ int check_plan(const Geometry& g, const Plan& pl, const pa_opts* opts) {
         return fail(PA_ENOTSUP, "balanced schedule needs the MFMA variant, head_dim 128/256 and at most %d sequences",
                     kLeanMaxBatch);
     if (opts && opts->schedule == PA_SCHEDULE_FITTED && !fit_allowed(g, pl, opts))
-        return fail(PA_ENOTSUP, "fitted partitions need the MFMA variant, no window, no partition size and at most "
-                    "%d sequences", pa::kFitMaxBatch);
+        return fail(PA_ENOTSUP, "fitted partitions need the MFMA variant, no window, no partition size, at most "
+                    "%d sequences and block tables of fewer than %d tokens", pa::kFitMaxBatch, pa::kFitMaxTokens);
     return PA_OK;
 }
 

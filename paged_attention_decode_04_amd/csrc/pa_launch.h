@@ -67,6 +67,7 @@ hipError_t launch_append(const AppendParams& a, hipStream_t s);
 // fill a given number of workgroups; every workgroup reads all lengths, so
 // the batch is bounded.
 constexpr int kFitMaxBatch = 256;
+constexpr int kFitMaxTokens = 1 << 24;       // block-table capacity MaxBlk * P below this
 
 // Log-sum-exp merge of split partials into bf16 output.
 hipError_t launch_merge(const DecodeParams& p, int head_dim, hipStream_t s);

@@ -92,8 +92,9 @@ __device__ __forceinline__ bool fit_locate(const DecodeParams& p, int x, int (&l
     const int nc = (p.B + 63) >> 6;
 #pragma unroll
     for (int c = 0; c < NC; ++c) len[c] = clampi(len[c], 0, cap);
-    // ceil(len / t) for 0 <= len < 2^24, 64 <= t: a float estimate off by at
-    // most one, made exact by two integer corrections
+    // ceil(len / t) for 0 <= len < 2^24 (the host bounds the block tables
+    // so), 64 <= t: a float estimate off by at most one, made exact by two
+    // integer corrections
     auto ceil_div = [](int len, int t, float rcp) {
         int d = (int)((float)len * rcp);
         d -= d * t > len ? 1 : 0;

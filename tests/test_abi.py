@@ -170,6 +170,9 @@ def test_fitted_schedule_preconditions():
     assert check(args(B=256), fit()) == pa.PA_OK
     assert check(args(B=257), fit()) == pa.PA_ENOTSUP
     assert check(args(), fit(shares=1024)) == pa.PA_OK
+    # block tables of 2^24 tokens or more keep fixed partitions
+    assert check(args(P=16, maxblk=(1 << 20) - 1), fit()) == pa.PA_OK
+    assert check(args(P=16, maxblk=1 << 20), fit()) == pa.PA_ENOTSUP
     assert check(args(), fit(shares=1025)) == pa.PA_EINVAL
 
 
