@@ -68,9 +68,10 @@ struct Plan {
 };
 
 // Fitted partitions: sizes from max(kFitMinTokens, T / kFitRange) up to the
-// size T the fixed schedule would take (its floor of 256 tokens holds here
-// too: shorter partitions cost more in per-workgroup overhead than they
-// gain in balance).
+// size T the fixed schedule would take.  Fitted partitions serve calls of
+// hundreds of MB, whose best fixed sizes are 512 tokens and more; below 256
+// tokens a partition's own cost (page-id fetch, LDS merge, partial write)
+// outweighs the balance it buys there.
 constexpr int kFitMinTokens = 256;
 constexpr int kFitRange = 4;
 constexpr int kFitAutoMinParts = 4;
@@ -258,10 +259,12 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     } else if (pl.variant == PA_VARIANT_MFMA) {
         // Few, long partitions: each workgroup's fixed cost (page-table
         // fetch, LDS merge, partial write) is paid per partition, so aim for
-        // about one workgroup per CU of work, partitions of 256..4096 tokens
-        // (measured: a 1152-token sequence runs 9.4 us at 256, 11.3 at 512).
+        // about one workgroup per CU of work, partitions of 128..4096 tokens
+        // (measured per call: one 1152-token sequence, 8 KV heads, runs 9.4 us
+        // at 128, 11.2 at 256; four of them 10.5 at 128, 9.9 at 192, 11.0 at
+        // 256; one 4096-token sequence 14.4 at 64, 11.0 at 128, 11.4 at 256).
         T = (max_ctx * groups + 255) / 256;
-        T = std::max<int64_t>(256, std::min<int64_t>(T, 4096));
+        T = std::max<int64_t>(128, std::min<int64_t>(T, 4096));
     } else {
         // Aim for ~1024 workgroups; partitions of 64..1024 tokens.
         T = (max_ctx * groups + 1023) / 1024;
