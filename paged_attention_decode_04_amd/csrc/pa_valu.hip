@@ -280,24 +280,34 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
 }
 
 // Log-sum-exp merge of the split-KV partials: one 64-thread group per (h, b).
+// Partials read before the row's count is known: 32 at head_dim 128 (5
+// registers each), 16 above.
+template <int D>
+constexpr int kMergeEager = D == 128 ? 32 : 16;
 template <int D>
 __global__ __launch_bounds__(64) void pa_lse_merge_kernel(DecodeParams p) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int64_t first = ((int64_t)b * p.Hq + h) * p.n_part;
-    // The first four partials (those of the n_part slots that exist) are read
-    // with the length, not after it: one round trip to memory for most rows.
+    // The partials of up to kMergeEager<D> slots (those of the n_part slots that
+    // exist) are all read with the length, not after it: one round trip to
+    // memory per row.  Slots past the row's count are read and ignored.
+    constexpr int NB = kMergeEager<D> / 4;
     LseMerge<D> m;
-    float l[4];
-    typename LseMerge<D>::vec_t v[4];
-    LseMerge<D>::read(p, first, 1, 0, p.n_part, l, v);
+    float l[NB][4];
+    typename LseMerge<D>::vec_t v[NB][4];
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+        if (4 * k < p.n_part) LseMerge<D>::read(p, first, 1, 4 * k, p.n_part, l[k], v[k]);
     // fitted partitions: the size the decode kernel chose for this call
     const int T = p.fit_part ? *p.fit_part : p.part_tokens;
     const int L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     int t_begin, t_base;
     window_bounds(p, L, t_begin, t_base);
     const int n_used = min((L - t_base + T - 1) / T, p.n_part);
-    m.add(l, v, n_used);
-    m.add_range(p, first, 1, 4, n_used);
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+        if (4 * k < n_used) m.add(l[k], v[k], n_used - 4 * k);
+    m.add_range(p, first, 1, kMergeEager<D>, n_used);
     m.store(p, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
 }
 
