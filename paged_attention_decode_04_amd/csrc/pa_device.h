@@ -290,12 +290,25 @@ struct LseMerge {
 };
 
 // Log-sum-exp merge of n split partials at slots first, first + step, ...
-// into the output row at element offset out_off (in the output's type).
+// into the output row at element offset out_off (in the output's type).  The
+// first 16 partials (8 at head_dim 512) are all read before any is added:
+// one round trip to memory for them.
 template <int D>
 __device__ __forceinline__ void merge_partials(const DecodeParams& p, int64_t first, int64_t step, int n,
                                                int64_t out_off) {
+    constexpr int NB = D <= 256 ? 4 : 2;        // batches of four read at once
     LseMerge<D> m;
-    m.add_range(p, first, step, 0, n);
+    float l[NB][4];
+    typename LseMerge<D>::vec_t v[NB][4];
+    if (n > 0) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (4 * k < n) LseMerge<D>::read(p, first, step, 4 * k, n, l[k], v[k]);
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (4 * k < n) m.add(l[k], v[k], n - 4 * k);
+    }
+    m.add_range(p, first, step, 4 * NB, n);
     m.store(p, out_off);
 }
 
