@@ -389,6 +389,44 @@ def test_fitted_many_sequences_ragged(B, Hq, Hkv, D):
         assert_parity(y, ref, f"B={B} D={D} target={n}")
 
 
+def test_fitted_workspace_garbage_and_foreign_hints():
+    """Fitted partitions keep each workgroup's last partition in the workspace
+    as the next call's guess.  Any content there must give the same result:
+    a workspace of random bytes, hints left by a batch of another shape, and
+    reruns (hints that hit) -- all against the oracle, reruns bitwise."""
+    ws_n = 0
+    cases = []
+    for B, lens_hi, seed in ((32, 4096, 21), (9, 3000, 22)):
+        rng = np.random.default_rng(seed)
+        lens = tuple(int(x) for x in rng.integers(1, lens_hi + 1, B))
+        w = custom(batch=B, num_q_heads=8, num_kv_heads=2, head_dim=256, page_size=32, ctx=lens)
+        inp = make_inputs(w, seed=seed)
+        d = to_device(inp)
+        q, k, v = d.call(0)
+        opts = pa.make_opts("mfma", 0, "fitted")
+        ws_n = max(ws_n, pa.pa_decode_workspace_bytes(B, 8, 2, 256, d.block_tables.shape[1], 32, opts))
+        cases.append((inp, d, q, k, v))
+    raw = torch.randint(0, 256, (ws_n + 256,), dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + ws_n]
+    first = {}
+    for rnd in range(3):
+        for i, (inp, d, q, k, v) in enumerate(cases):
+            out = torch.full_like(q, float("nan"))
+            pa.pa_reset_stats()
+            pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, variant="mfma",
+                      schedule="fitted", workspace=ws)
+            torch.cuda.synchronize()
+            st = pa.pa_get_stats()
+            assert st["last_schedule"] == pa.PA_SCHEDULE_FITTED and st["split_calls"] == 1, st
+            y = bits(out)
+            if rnd == 0:
+                assert_parity(y, oracle_run(inp), f"fitted case {i}, workspace of random bytes")
+                first[i] = y
+            else:
+                assert np.array_equal(y, first[i]), f"fitted case {i} round {rnd}: result depends on the hints"
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 8), (256, 32, 4), (128, 64, 4)])
 def test_balanced_share_sweep(D, Hq, Hkv):
     """Many share counts over a length mix with one long sequence: share
