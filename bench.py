@@ -326,7 +326,13 @@ def cpu_baseline(d, w, target_s, workloads_mod):
         if t_total >= target_s:
             break
     gbs = bytes_done / t_total / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": cpu,
             "seconds": round(t_total, 2),
             "us_per_call_equiv": round(1e6 * t_total * w.batch / b_done, 1),
             "sample": f"{b_done} of {w.batch} sequences of {w.name} ({tok} tokens, all "
