@@ -105,7 +105,7 @@ def test_config_parity(name, variant):
     assert_parity(y, oracle_run(inp), f"{name}/{variant} T={s['last_partition_tokens']}")
 
 
-@pytest.mark.parametrize("variant", ["valu", "mfma"])
+@pytest.mark.parametrize("variant", ["valu", "mfma", "mfma-fit"])
 def test_hd512_full_size(variant):
     """The head_dim-512 workload timed by the benchmark (16 seqs, ctx
     U[1024,4096], Hq8/Hkv2), all rows against the oracle, on both kernels
@@ -670,6 +670,10 @@ def test_head_dim_512(kt, Hq, Hkv):
             assert_parity(y, ref, f"D=512 {var} kv {kt} Hq={Hq} Hkv={Hkv} T={T}")
         y, _ = gpu_run(d, variant=var, window=100)
         assert_parity(y, ref_w, f"D=512 {var} kv {kt} W=100")
+    if kt != "f32":
+        for n in FIT_TARGETS:
+            y, _ = gpu_run(d, variant="mfma-fit", shares=n)
+            assert_parity(y, ref, f"D=512 fitted kv {kt} Hq={Hq} Hkv={Hkv} target={n}")
     # the automatic choice: MFMA for 16-bit caches, vector ALU for fp32
     pa.pa_reset_stats()
     q, k, v = d.call(0)
