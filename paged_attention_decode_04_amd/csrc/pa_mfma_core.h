@@ -204,11 +204,17 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - m_run);
-    // P.V takes P in the KV type; the normaliser sums the same rounded weights, so
-    // the output stays an exact weighted mean of V rows (weights off by at
-    // most 2^-9 relative) rather than picking up the rounding as a bias.
-    const u32x2 pb = {KV::pack2(pr[0], pr[1]), KV::pack2(pr[2], pr[3])};
-    l_run += (KV::lo(pb[0]) + KV::hi(pb[0])) + (KV::lo(pb[1]) + KV::hi(pb[1]));
+    // P.V takes P in the KV type, as the sum of two such values: hi = P
+    // rounded, lo = (P - hi) rounded.  The weights are then exact to about
+    // 2^-17 relative (2^-22 for fp16) instead of the 2^-9 of one rounding,
+    // so the output is close to correctly rounded.  The path is bound by
+    // the K/V reads; the second P.V MFMA per dim block costs no time there.
+    // The normaliser sums the same hi + lo.
+    const u32x2 ph = {KV::pack2(pr[0], pr[1]), KV::pack2(pr[2], pr[3])};
+    const u32x2 pl = {KV::pack2(pr[0] - KV::lo(ph[0]), pr[1] - KV::hi(ph[0])),
+                      KV::pack2(pr[2] - KV::lo(ph[1]), pr[3] - KV::hi(ph[1]))};
+    l_run += ((KV::lo(ph[0]) + KV::hi(ph[0])) + (KV::lo(ph[1]) + KV::hi(ph[1]))) +
+             ((KV::lo(pl[0]) + KV::hi(pl[0])) + (KV::lo(pl[1]) + KV::hi(pl[1])));
 
     // O^T += V^T . P^T, V transposed in registers (4 tokens x 8 dims per lane)
 #pragma unroll
@@ -221,7 +227,7 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
             const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
             const u32x2 va = {__builtin_amdgcn_perm(cur.v[1][hh][x], cur.v[0][hh][x], sel),
                               __builtin_amdgcn_perm(cur.v[3][hh][x], cur.v[2][hh][x], sel)};
-            o[hh * 8 + mm] = KV::mma_pv(va, pb, o[hh * 8 + mm]);
+            o[hh * 8 + mm] = KV::mma_pv(va, pl, KV::mma_pv(va, ph, o[hh * 8 + mm]));
         }
 }
 

@@ -557,15 +557,22 @@ def test_comparator_selftest_matches_pages():
 
 def test_comparator_quantization_bound_elements():
     """|r| >= 4: the correctly rounded bf16 value may be more than 1e-2 away
-    (r = -4.11025..., nearest bf16 -4.125); within one ULP it passes, two
-    ULPs off it fails.  Below 4 the 1e-2 bar stays."""
-    from oracle.compare import compare, f64_to_bf16_bits, bump_ulp
+    (r = -4.11025..., nearest bf16 -4.125, 0.472 ULP off); it passes, and so
+    does the other neighbour of this near-tie (-4.09375, 0.528 ULP), but one
+    ULP past the correct rounding (-4.15625, 1.47 ULPs) fails.  Below 4 the
+    1e-2 bar stays."""
+    from oracle.compare import BIG_ULPS_TOL, compare, f64_to_bf16_bits, bump_ulp
     r = np.array([-4.110250183701639, 0.5, -1.25, 3.0])
     y = f64_to_bf16_bits(r)
     rep = compare(y, r)
-    assert rep.n_big == 1 and rep.max_abs > 1e-2 and rep.big_ulps <= 1.0 and rep.ok()
-    y2 = bump_ulp(y, [0], 2)
-    assert not compare(y2, r).ok()
+    assert rep.n_big == 1 and rep.max_abs > 1e-2 and abs(rep.big_ulps - 0.472) < 1e-3 and rep.ok()
+    y1 = bump_ulp(y, [0], -1)                                 # -4.09375
+    assert abs(compare(y1, r).big_ulps - 0.528) < 1e-3 and compare(y1, r).ok()
+    y2 = bump_ulp(y, [0], 1)                                  # -4.15625
+    assert compare(y2, r).big_ulps > BIG_ULPS_TOL and not compare(y2, r).ok()
+    y4 = f64_to_bf16_bits(np.array([4.5, 0.5, -1.25, 3.0]))
+    r4 = np.array([4.5 + 0.6 * 2.0 ** -5, 0.5, -1.25, 3.0])   # 0.6 ULP from 4.5: not a correct rounding
+    assert not compare(y4, r4).ok()
     y3 = y.copy()
     y3[1] = f64_to_bf16_bits(np.array([0.5 + 0.02]))[0]      # 0.02 off where |r| < 4
     assert not compare(y3, r).ok()
