@@ -21,9 +21,13 @@
  *   x_t  = scale * dot(q[b][h][:], k_cache[page][slot][g][:])
  *   out[b][h][:] = sum_t softmax(x)_t * v_cache[page][slot][g][:]
  *
- * computed with fp32 arithmetic (online softmax, fp32 accumulation) and
- * written as bf16 rounded to nearest even.  L == 0 writes zeros.  There is no
- * mask, window or positional term.
+ * over t in [0, L), or with a sliding window of W tokens (pa_opts.window)
+ * over t in [max(0, L - W), L).  Q, the K/V cache and out are each bf16,
+ * IEEE binary16 or binary32 (K and V share one type).  Arithmetic is fp32
+ * (online softmax, fp32 accumulation; on the matrix cores the products take
+ * Q and P in the cache's 16-bit type, P as the sum of two such values); the
+ * output is rounded to its type, nearest even.  L == 0 writes zeros.  There
+ * is no mask other than the window and no positional term.
  *
  * All functions are plain C, never throw, and make no HIP call before their
  * arguments have been validated.  Calls are asynchronous on the given stream:
@@ -45,13 +49,17 @@ extern "C" {
 /* ---------------------------------------------------------------- errors */
 #define PA_OK       0  /* success                                                  */
 #define PA_EINVAL   1  /* null pointer, bad shape/dtype/stride, Hq % Hkv != 0,
-                          non-finite scale, page_size < 1                          */
+                          infinite scale, page_size < 1, a library workspace
+                          asked for on a stream under capture                      */
 #define PA_ENOTSUP  2  /* head_dim not 128/256/512, Hq/Hkv not 1, 2, 4, 8 or 16, or a
                           kernel/schedule that does not take the call's shape      */
 #define PA_EALIGN   3  /* a base pointer or a row stride not 16-byte aligned       */
 #define PA_ENODEV   4  /* no HIP device available                                  */
 #define PA_ENOMEM   5  /* workspace could not be allocated, or is too small        */
 #define PA_EHIP     6  /* a HIP runtime call failed; text in pa_last_error()        */
+
+/* The scale argument's request for the default 1/sqrt(head_dim). */
+#define PA_SCALE_DEFAULT (__builtin_nanf(""))
 
 /* ---------------------------------------------------------------- tensors */
 #define PA_DTYPE_BF16  1
@@ -75,24 +83,29 @@ typedef struct pa_tensor {
 /*
  * pa_decode -- enqueue one decode paged-attention call.
  *
- *  q             [B, Hq, D]        bf16; stride[2] == 1; stride[0], stride[1]
- *                                  multiples of 8 (16 bytes).
- *  k_cache       [NP, P, Hkv, D]   bf16 NHD pool: page, slot, KV head, dim;
- *                                  stride[3] == 1, other strides multiples of
- *                                  8 elements.  Pages may lie anywhere in the
- *                                  pool: block_tables gives the order.
- *  v_cache       same shape as k_cache (its own strides, same rules).
+ *  q             [B, Hq, D]        bf16, fp16 or fp32; stride[2] == 1;
+ *                                  stride[0], stride[1] multiples of 16 bytes.
+ *  k_cache       [NP, P, Hkv, D]   NHD pool (page, slot, KV head, dim) of
+ *                                  bf16, fp16 or fp32; stride[3] == 1, other
+ *                                  strides multiples of 16 bytes.  Pages may
+ *                                  lie anywhere in the pool: block_tables
+ *                                  gives the order.
+ *  v_cache       same shape and element type as k_cache (its own strides,
+ *                same rules).
  *  block_tables  [B, MaxBlk]       int32, stride[1] == 1.  Entry j of row b is
  *                                  the physical page of tokens
  *                                  [j*P, (j+1)*P) of sequence b.  Entries at
  *                                  or past ceil(L_b / P) are never read and
  *                                  may hold anything (e.g. -1).
  *  context_lens  [B]               int32, stride[0] == 1.  L_b tokens.
- *  scale         fp32 multiplier of the logits (normally 1/sqrt(D)).
+ *  scale         fp32 multiplier of the logits, or PA_SCALE_DEFAULT (a NaN)
+ *                for the method's 1/sqrt(D) (the fp32 value nearest to it).
+ *                An infinite scale is PA_EINVAL.
  *  num_q_heads, num_kv_heads, head_dim, page_size
  *                must equal q.shape[1], k_cache.shape[2], q.shape[2] and
  *                k_cache.shape[1].
- *  out           [B, Hq, D]        bf16, stride[2] == 1, 16-byte aligned rows.
+ *  out           [B, Hq, D]        bf16, fp16 or fp32, stride[2] == 1,
+ *                                  16-byte aligned rows.
  *  stream        hipStream_t to enqueue on; NULL is the null stream.
  *
  * Device-side preconditions, not checked on the host (the host never reads
@@ -110,10 +123,13 @@ typedef struct pa_tensor {
  * for at most 256 sequences, where fixed partitions would cut the tables
  * into 4 or more and the tables hold at least 192 MB of K/V); partial results are
  * merged with the log-sum-exp rule by a second kernel.  The library keeps a
- * per-device workspace for the partials, grown on demand with hipMalloc and
- * freed by pa_release(); calls that use it must not overlap in time on one
- * device (callers that overlap calls pass their own workspaces to
- * pa_decode_ex).  Returns PA_OK or an error code above.
+ * per-device workspace for the partials, grown on demand with hipMalloc
+ * (an outgrown buffer is kept until pa_release(), which frees them all);
+ * calls that use it must not overlap in time on one device (callers that
+ * overlap calls pass their own workspaces to pa_decode_ex).  A call on a
+ * stream that is being captured into a graph cannot use that workspace and
+ * returns PA_EINVAL (captured calls use pa_decode_ex with a workspace).
+ * Returns PA_OK or an error code above.
  */
 int pa_decode(const pa_tensor* q,
               const pa_tensor* k_cache,

@@ -9,13 +9,15 @@ package raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
 
 PA_OK, PA_EINVAL, PA_ENOTSUP, PA_EALIGN, PA_ENODEV, PA_ENOMEM, PA_EHIP = range(7)
+# scale argument asking the library for 1/sqrt(head_dim)
+PA_SCALE_DEFAULT = float("nan")
+
 PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32, PA_DTYPE_F16 = 1, 2, 3, 4
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 VARIANTS = {"auto": PA_VARIANT_AUTO, "valu": PA_VARIANT_VALU, "mfma": PA_VARIANT_MFMA}
@@ -173,6 +175,50 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _torch_stream(stream, device):
+    """The torch stream the call's work goes to (a torch.cuda.Stream, or a
+    raw hipStream_t handle wrapped as an external stream)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+# Workspaces of the convenience calls, one per (device, stream): zeroed once
+# when made (every call leaves the balanced schedule's counters zero, and the
+# rest is written before it is read), grown when a call needs more.  Calls on
+# one stream are ordered, so sharing a workspace there is safe; calls on
+# different streams get different workspaces.
+_WORKSPACES = {}
+
+
+def _workspace(nbytes, device, tstream):
+    """A 256-byte-aligned uint8 device buffer of at least nbytes for work on
+    tstream, allocated (and zero-filled) on that stream so the caching
+    allocator orders its reuse after that stream's work."""
+    import torch
+    capturing = torch.cuda.is_current_stream_capturing()
+    key = (device.index, tstream.cuda_stream)
+    have = None if capturing else _WORKSPACES.get(key)
+    if have is not None and have.numel() >= nbytes:
+        return have
+    with torch.cuda.stream(tstream):
+        raw = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + nbytes]
+    if not capturing:
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def release_workspaces() -> None:
+    """Drop the convenience calls' cached workspaces (the caching allocator
+    reuses their memory after the work queued on their streams)."""
+    _WORKSPACES.clear()
+
+
 # ------------------------------------------------------------------ C-ABI mirror
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
               num_kv_heads, head_dim, page_size, out, stream=None):
@@ -245,16 +291,16 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale=
     R, Hq, D = q.shape
     NP, P, Hkv, _ = k_cache.shape
     if scale is None:
-        scale = 1.0 / math.sqrt(D)
+        scale = PA_SCALE_DEFAULT
+    ts = _torch_stream(stream, q.device)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        with torch.cuda.stream(ts):
+            out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     opts = make_opts("auto", partition_tokens, schedule, 0, window)
     if workspace is None:
         n = pa_prefill_workspace_bytes(R, block_tables.shape[0], Hq, Hkv, D, block_tables.shape[1], P, opts)
         if n:
-            workspace = torch.zeros(n + 256, dtype=torch.uint8, device=q.device)
-            off = (-workspace.data_ptr()) % 256
-            workspace = workspace[off:off + n]
+            workspace = _workspace(n, q.device, ts)
     return pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, Hq, Hkv, D, P,
                       out, stream, opts, workspace)
 
@@ -317,24 +363,26 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
     q [B, Hq, D]; k_cache/v_cache [NP, P, Hkv, D] (NHD pool) -- each bf16, fp16
     or fp32 (K and V alike); out defaults to q's type (``out_dtype`` overrides);
     block_tables [B, MaxBlk] int32; context_lens [B] int32; scale defaults to
-    1/sqrt(D); ``window`` > 0 attends to each sequence's last ``window``
-    tokens only.  Returns out [B, Hq, D].  The split-KV workspace comes
-    zero-filled from torch's caching allocator unless one is given (a given
-    one must start with 256 zero bytes; see pa_decode_ex).
+    1/sqrt(D) (chosen by the library); ``window`` > 0 attends to each
+    sequence's last ``window`` tokens only.  Returns out [B, Hq, D].  Work
+    and any allocation go to ``stream`` (default: the current stream).
+    Without a given workspace, the split-KV workspace is one kept per device
+    and stream (zeroed when made; a given one must start with 256 zero
+    bytes; see pa_decode_ex).
     """
     import torch
     B, Hq, D = q.shape
     NP, P, Hkv, _ = k_cache.shape
     if scale is None:
-        scale = 1.0 / math.sqrt(D)
+        scale = PA_SCALE_DEFAULT
+    ts = _torch_stream(stream, q.device)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        with torch.cuda.stream(ts):
+            out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     opts = make_opts(variant, partition_tokens, schedule, shares, window)
     if workspace is None:
         n = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], P, opts)
         if n:
-            workspace = torch.zeros(n + 256, dtype=torch.uint8, device=q.device)
-            off = (-workspace.data_ptr()) % 256
-            workspace = workspace[off:off + n]
+            workspace = _workspace(n, q.device, ts)
     return pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, Hq, Hkv, D, P,
                         out, stream, opts, workspace)

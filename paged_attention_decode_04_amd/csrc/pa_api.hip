@@ -100,6 +100,12 @@ constexpr int kMaxDevices = 64;               // CU-count cache entries
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The logit multiplier: the caller's, or for PA_SCALE_DEFAULT (a NaN) the
+// method's 1/sqrt(head_dim), as the fp32 value nearest to it.
+float effective_scale(float scale, int64_t head_dim) {
+    return std::isnan(scale) ? (float)(1.0 / std::sqrt((double)head_dim)) : scale;
+}
+
 int check_tensor(const pa_tensor* t, const char* name, int32_t dtype, int ndim) {
     if (!t) return fail(PA_EINVAL, "%s: descriptor is NULL", name);
     if (dtype == kAnyFloat ? !float_type(t->dtype) : t->dtype != dtype)
@@ -140,7 +146,7 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
     if ((rc = check_tensor(ctx, "context_lens", PA_DTYPE_INT32, 1))) return rc;
     if ((rc = check_tensor(out, "out", kAnyFloat, 3))) return rc;
     if (k->dtype != v->dtype) return fail(PA_EINVAL, "k_cache and v_cache element types differ");
-    if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+    if (std::isinf(scale)) return fail(PA_EINVAL, "scale is infinite");
     if (page_size < 1) return fail(PA_EINVAL, "page_size %d < 1", page_size);
     if (num_q_heads < 1 || num_kv_heads < 1) return fail(PA_EINVAL, "head counts must be >= 1");
     if (num_q_heads % num_kv_heads) return fail(PA_EINVAL, "num_q_heads %d not a multiple of num_kv_heads %d",
@@ -324,40 +330,52 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     return pl;
 }
 
-// Library-owned per-device workspace.
+// Library-owned per-device workspace.  A buffer that is outgrown is kept,
+// not freed, until pa_release: work enqueued earlier may still use it, and
+// freeing it here would need a device-wide synchronisation.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    std::vector<void*> retired;
 };
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
 
-int library_workspace(int dev, size_t need, void** out) {
+int library_workspace(int dev, size_t need, hipStream_t stream, void** out) {
+    // A captured call would bake the library's buffer into the graph; the
+    // buffer can be outgrown (and released) by later calls, so captured calls
+    // must bring their own workspace (pa_decode_ex, pa_prefill).
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return fail(PA_EHIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(PA_EINVAL, "the stream is being captured: the library's own workspace cannot be used in a "
+                               "graph; pass a workspace (pa_decode_ex / pa_prefill)");
     std::lock_guard<std::mutex> lk(g_ws_mu);
     if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
     Workspace& w = g_ws[dev];
     if (w.bytes < need) {
-        if (w.ptr) {
-            hipError_t e = hipDeviceSynchronize();   // old buffer may still be in use
-            if (e != hipSuccess) return fail(PA_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        size_t sz = align_up(need + need / 2, 1 << 20);
-        hipError_t e = hipMalloc(&w.ptr, sz);
-        if (e != hipSuccess) {
-            w.ptr = nullptr;
-            return fail(PA_ENOMEM, "hipMalloc(%zu): %s", sz, hipGetErrorString(e));
-        }
+        const size_t sz = align_up(need + need / 2, 1 << 20);
+        void* ptr = nullptr;
+        e = hipMalloc(&ptr, sz);
+        if (e != hipSuccess) return fail(PA_ENOMEM, "hipMalloc(%zu): %s", sz, hipGetErrorString(e));
         // The balanced schedule's counters must start at zero (every call
-        // leaves them so).
-        e = hipMemset(w.ptr, 0, pa::kLeanCounterBytes);
+        // leaves them so); the zeroing is ordered before the call's kernels
+        // by the stream.
+        e = hipMemsetAsync(ptr, 0, pa::kLeanCounterBytes, stream);
         if (e != hipSuccess) {
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            return fail(PA_EHIP, "hipMemset: %s", hipGetErrorString(e));
+            (void)hipFree(ptr);
+            return fail(PA_EHIP, "hipMemsetAsync: %s", hipGetErrorString(e));
         }
+        if (w.ptr) {
+            try {
+                w.retired.push_back(w.ptr);
+            } catch (...) {
+                (void)hipFree(ptr);
+                return fail(PA_ENOMEM, "host allocation failed");
+            }
+        }
+        w.ptr = ptr;
         w.bytes = sz;
     }
     *out = w.ptr;
@@ -428,7 +446,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
     p.n_part = pl.n_part;
     p.qw = pl.qw;
     p.window = opts ? opts->window : 0;
-    p.scale_log2 = scale * pa::kLog2e;
+    p.scale_log2 = effective_scale(scale, g.D) * pa::kLog2e;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     hipError_t e;
@@ -512,7 +530,7 @@ int decode_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, cons
                 return fail(PA_EALIGN, "workspace not %zu-byte aligned", kAlign);
             ws = workspace;
         } else {
-            rc = library_workspace(dev, pl.ws_bytes, &ws);
+            rc = library_workspace(dev, pl.ws_bytes, static_cast<hipStream_t>(stream), &ws);
             if (rc) return rc;
         }
     }
@@ -594,7 +612,7 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
     if ((rc = check_tensor(qs, "query_start", PA_DTYPE_INT32, 1))) return rc;
     if ((rc = check_tensor(out, "out", kAnyFloat, 3))) return rc;
     if (k->dtype != v->dtype) return fail(PA_EINVAL, "k_cache and v_cache element types differ");
-    if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale is not finite");
+    if (std::isinf(scale)) return fail(PA_EINVAL, "scale is infinite");
     if (page_size < 1) return fail(PA_EINVAL, "page_size %d < 1", page_size);
     if (num_q_heads < 1 || num_kv_heads < 1) return fail(PA_EINVAL, "head counts must be >= 1");
     if (num_q_heads % num_kv_heads)
@@ -735,7 +753,7 @@ int prefill_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, con
                 return fail(PA_EALIGN, "workspace not %zu-byte aligned", kAlign);
             ws = workspace;
         } else {
-            rc = library_workspace(dev, pl.ws_bytes, &ws);
+            rc = library_workspace(dev, pl.ws_bytes, static_cast<hipStream_t>(stream), &ws);
             if (rc) return rc;
         }
     }
@@ -778,7 +796,7 @@ int prefill_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, con
     p.qw = 16;
     p.lean_page_slots = pa::lean_page_slots(p.P);
     p.window = opts ? opts->window : 0;
-    p.scale_log2 = scale * pa::kLog2e;
+    p.scale_log2 = effective_scale(scale, g.D) * pa::kLog2e;
     e = pl.staged ? pa::launch_prefill_staged(p, (int)g.D, g.kv_dtype, static_cast<hipStream_t>(stream))
                   : pa::launch_prefill(p, (int)g.D, g.kv_dtype, pl.split, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PA_EHIP, "several-query launch: %s", hipGetErrorString(e));
@@ -970,12 +988,15 @@ int pa_release(void) {
     int cur = -1;
     bool have_cur = hipGetDevice(&cur) == hipSuccess;
     for (size_t d = 0; d < g_ws.size(); ++d) {
-        if (!g_ws[d].ptr) continue;
-        if (hipSetDevice((int)d) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-            hipFree(g_ws[d].ptr) != hipSuccess)
-            rc = fail(PA_EHIP, "releasing workspace of device %zu failed", d);
-        g_ws[d].ptr = nullptr;
-        g_ws[d].bytes = 0;
+        Workspace& w = g_ws[d];
+        if (!w.ptr && w.retired.empty()) continue;
+        bool ok = hipSetDevice((int)d) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+        for (void* r : w.retired) ok = ok && hipFree(r) == hipSuccess;
+        if (w.ptr) ok = ok && hipFree(w.ptr) == hipSuccess;
+        if (!ok) rc = fail(PA_EHIP, "releasing workspace of device %zu failed", d);
+        w.ptr = nullptr;
+        w.bytes = 0;
+        w.retired.clear();
     }
     if (have_cur) (void)hipSetDevice(cur);
     return rc;

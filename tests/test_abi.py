@@ -73,7 +73,7 @@ def test_valid_arguments_pass():
     (lambda a: a.update(v_cache=a["v_cache"].half()), pa.PA_EINVAL),   # K and V types differ
     (lambda a: a.update(out=a["out"].to(torch.int32)), pa.PA_EINVAL),
     (lambda a: a.update(num_q_heads=15), pa.PA_EINVAL),
-    (lambda a: a.update(scale=float("nan")), pa.PA_EINVAL),
+    (lambda a: a.update(scale=float("-inf")), pa.PA_EINVAL),
     (lambda a: a.update(scale=float("inf")), pa.PA_EINVAL),
     (lambda a: a.update(page_size=0), pa.PA_EINVAL),
     (lambda a: a.update(page_size=32), pa.PA_EINVAL),
@@ -89,6 +89,13 @@ def test_bad_arguments_are_rejected(mutate, code):
     mutate(a)
     assert check(a) == code
     assert pa.last_error() != ""
+
+
+def test_default_scale_sentinel_is_accepted():
+    """PA_SCALE_DEFAULT (a NaN) asks the library for 1/sqrt(head_dim)."""
+    a = args()
+    a.update(scale=pa.PA_SCALE_DEFAULT)
+    assert check(a) == pa.PA_OK
 
 
 def test_element_types_and_head_sizes():
