@@ -128,8 +128,8 @@ typedef struct pa_tensor {
  * calls that use it must not overlap in time on one device (callers that
  * overlap calls pass their own workspaces to pa_decode_ex).  A call on a
  * stream that is being captured into a graph cannot use that workspace and
- * returns PA_EINVAL (captured calls use pa_decode_ex with a workspace).
- * Returns PA_OK or an error code above.
+ * returns PA_EINVAL (captured calls use pa_decode_ex with a workspace, or
+ * pa_decode_noalloc).  Returns PA_OK or an error code above.
  */
 int pa_decode(const pa_tensor* q,
               const pa_tensor* k_cache,
@@ -262,6 +262,41 @@ int pa_decode_ex(const pa_tensor* q,
                  const pa_opts* opts,
                  void* workspace,
                  size_t workspace_bytes);
+
+/*
+ * pa_decode_noalloc -- pa_decode_ex (workspace NULL aside) for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Not an operation of the source
+ * pages: the same decode, whose split-KV partials, work counters and
+ * partition hints go to a static per-device scratch array of
+ * PA_NOALLOC_SCRATCH_BYTES inside the library instead of a workspace.
+ *
+ * Arguments, layouts and results as pa_decode_ex with opts (may be NULL).
+ * Makes no hipMalloc / hipFree call.  A call whose split-KV plan needs more
+ * scratch than PA_NOALLOC_SCRATCH_BYTES (pa_decode_workspace_bytes tells,
+ * for the call's variant) returns PA_ENOMEM before any launch.  Each device
+ * the library runs on holds the array from its first pa_decode_noalloc call
+ * until the process ends.  That first call on a device sets the scratch up
+ * (looks up its address, clears its work counters on the call's stream) and
+ * must not be captured (PA_EINVAL); later calls may be.  Every call on one
+ * device shares that device's array: calls that overlap in time on one
+ * device (other streams, other threads, graphs replayed concurrently) race
+ * and give unspecified results.  Every call leaves the work counters zero.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_noalloc(const pa_tensor* q,
+                      const pa_tensor* k_cache,
+                      const pa_tensor* v_cache,
+                      const pa_tensor* block_tables,
+                      const pa_tensor* context_lens,
+                      float scale,
+                      int num_q_heads,
+                      int num_kv_heads,
+                      int head_dim,
+                      int page_size,
+                      const pa_tensor* out,
+                      void* stream,
+                      const pa_opts* opts);
 
 /*
  * pa_check_args -- run only the host-side validation of pa_decode_ex and

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
 PA_OK, PA_EINVAL, PA_ENOTSUP, PA_EALIGN, PA_ENODEV, PA_ENOMEM, PA_EHIP = range(7)
 # scale argument asking the library for 1/sqrt(head_dim)
 PA_SCALE_DEFAULT = float("nan")
-
+# static split-KV scratch of pa_decode_noalloc, per device
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 PA_DTYPE_BF16, PA_DTYPE_INT32, PA_DTYPE_FP32, PA_DTYPE_F16 = 1, 2, 3, 4
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 VARIANTS = {"auto": PA_VARIANT_AUTO, "valu": PA_VARIANT_VALU, "mfma": PA_VARIANT_MFMA}
@@ -65,6 +66,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_decode_ex.argtypes = args12 + [ctypes.c_void_p, ctypes.POINTER(PaOpts),
                                           ctypes.c_void_p, ctypes.c_size_t]
     lib.pa_decode_ex.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = args12 + [ctypes.c_void_p, ctypes.POINTER(PaOpts)]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_check_args.argtypes = args12 + [ctypes.POINTER(PaOpts)]
     lib.pa_check_args.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
@@ -328,6 +331,21 @@ def pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_h
                               _stream_handle(stream, q.device),
                               ctypes.byref(opts) if opts else None, ws_ptr, ws_len)
     _check(rc, "pa_decode_ex")
+    return out
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+                      num_kv_heads, head_dim, page_size, out, stream=None, opts: PaOpts | None = None):
+    """C ``pa_decode_noalloc``: the split-KV partials go to the library's
+    static per-device scratch; nothing is allocated."""
+    import torch
+    _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
+    with torch.cuda.device(q.device):
+        rc = LIB.pa_decode_noalloc(tensor_desc(q), tensor_desc(k_cache), tensor_desc(v_cache),
+                                   tensor_desc(block_tables), tensor_desc(context_lens), float(scale),
+                                   num_q_heads, num_kv_heads, head_dim, page_size, tensor_desc(out),
+                                   _stream_handle(stream, q.device), ctypes.byref(opts) if opts else None)
+    _check(rc, "pa_decode_noalloc")
     return out
 
 

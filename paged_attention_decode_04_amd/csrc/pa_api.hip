@@ -344,13 +344,14 @@ std::vector<Workspace> g_ws;
 int library_workspace(int dev, size_t need, hipStream_t stream, void** out) {
     // A captured call would bake the library's buffer into the graph; the
     // buffer can be outgrown (and released) by later calls, so captured calls
-    // must bring their own workspace (pa_decode_ex, pa_prefill).
+    // must bring their own workspace (pa_decode_ex, pa_prefill) or use the
+    // static one of pa_decode_noalloc.
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(stream, &cs);
     if (e != hipSuccess) return fail(PA_EHIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
     if (cs != hipStreamCaptureStatusNone)
         return fail(PA_EINVAL, "the stream is being captured: the library's own workspace cannot be used in a "
-                               "graph; pass a workspace (pa_decode_ex / pa_prefill)");
+                               "graph; pass a workspace (pa_decode_ex / pa_prefill) or call pa_decode_noalloc");
     std::lock_guard<std::mutex> lk(g_ws_mu);
     if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
     Workspace& w = g_ws[dev];
@@ -538,6 +539,81 @@ int decode_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, cons
         return launch(q, k, v, bt, ctx, scale, out, stream, g, pl, opts, ws, dev);
     } catch (const std::bad_alloc&) {
         return fail(PA_ENOMEM, "host allocation failed");
+    } catch (...) {
+        return fail(PA_EHIP, "unexpected exception");
+    }
+}
+
+// ---------------------------------------------------------------- static scratch
+// The split-KV scratch of pa_decode_noalloc, for callers that cannot
+// allocate: one array per device, held until the process ends.  Host code
+// never uses the name `scratch` as an address (in host code it is a
+// stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Zero the first n dwords (the balanced schedule's work counters).
+__global__ void pa_scratch_clear_kernel(uint32_t* p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];               // device address of `scratch` per device
+
+int device_scratch(int dev, hipStream_t stream, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(PA_ENODEV, "device %d beyond the library's %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        // Set-up, once per device (the current one): outside stream capture,
+        // since the runtime may load the module's data here.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return fail(PA_EHIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(PA_EINVAL, "the first pa_decode_noalloc call on a device sets up its scratch and must "
+                                   "not be captured; make one uncaptured call first");
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(PA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        // The array starts zeroed; the counters are cleared once more here,
+        // ordered before this call's kernels by the stream.
+        hipLaunchKernelGGL(pa_scratch_clear_kernel, dim3(1), dim3(64), 0, stream, static_cast<uint32_t*>(ptr),
+                           (int)(pa::kLeanCounterBytes / sizeof(uint32_t)));
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(PA_EHIP, "scratch clear launch: %s", hipGetErrorString(e));
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return PA_OK;
+}
+
+int decode_noalloc_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_tensor* bt,
+                        const pa_tensor* ctx, float scale, int num_q_heads, int num_kv_heads, int head_dim,
+                        int page_size, const pa_tensor* out, void* stream, const pa_opts* opts) {
+    t_err.clear();
+    Geometry g;
+    int rc = validate(q, k, v, bt, ctx, scale, num_q_heads, num_kv_heads, head_dim, page_size, out, opts, g);
+    if (rc) return rc;
+    Plan pl = make_plan(g, opts);
+    rc = check_plan(g, pl, opts);
+    if (rc) return rc;
+    if (pl.split && pl.ws_bytes > kScratchBytes)
+        return fail(PA_ENOMEM, "the call needs %zu bytes of split-KV scratch; pa_decode_noalloc has %zu "
+                    "(use pa_decode_ex with a workspace)", pl.ws_bytes, kScratchBytes);
+    if (g.B == 0) return PA_OK;
+    int dev = 0, ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(PA_ENODEV, "no HIP device");
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ENODEV, "hipGetDevice: %s", hipGetErrorString(e));
+    void* ws = nullptr;
+    if (pl.split) {
+        rc = device_scratch(dev, static_cast<hipStream_t>(stream), &ws);
+        if (rc) return rc;
+    }
+    try {
+        return launch(q, k, v, bt, ctx, scale, out, stream, g, pl, opts, ws, dev);
     } catch (...) {
         return fail(PA_EHIP, "unexpected exception");
     }
@@ -899,6 +975,14 @@ int pa_decode_ex(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* 
     return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
                        num_kv_heads, head_dim, page_size, out, stream, opts, workspace,
                        workspace_bytes);
+}
+
+int pa_decode_noalloc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                      const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                      int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                      const pa_tensor* out, void* stream, const pa_opts* opts) {
+    return decode_noalloc_impl(q, k_cache, v_cache, block_tables, context_lens, scale, num_q_heads,
+                               num_kv_heads, head_dim, page_size, out, stream, opts);
 }
 
 int pa_check_args(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
