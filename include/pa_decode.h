@@ -206,6 +206,16 @@ int pa_cache_append(const pa_tensor* k_new,
                                       last call as a starting guess for the
                                       next; any content there is valid.       */
 
+/* How split partitions are merged (log-sum-exp): */
+#define PA_MERGE_AUTO    0   /* the library picks                              */
+#define PA_MERGE_KERNEL  1   /* a second kernel merges them after the decode   */
+#define PA_MERGE_FUSED   2   /* inside the decode kernel: the last partition of
+                                each (sequence, query block) group to finish
+                                merges the group's partials (MFMA variant,
+                                partition or fitted schedule, at most
+                                PA_FUSE_MAX_GROUPS groups)                     */
+#define PA_FUSE_MAX_GROUPS 16320
+
 typedef struct pa_opts {
     int32_t variant;            /* PA_VARIANT_*                                */
     int32_t partition_tokens;   /* 0 = automatic; else tokens per split-KV
@@ -221,7 +231,8 @@ typedef struct pa_opts {
                                    W >= 1 = only the last W, tokens
                                    [max(0, L - W), L) (page 3, LIMITATIONS,
                                    the windowed variant)                       */
-    int32_t reserved[3];        /* must be zero                                */
+    int32_t merge;              /* PA_MERGE_*                                  */
+    int32_t reserved[2];        /* must be zero                                */
 } pa_opts;
 
 /*
@@ -232,6 +243,7 @@ typedef struct pa_opts {
  * the larger of the two plans, enough for any element type.  Returns 0 on
  * bad arguments as well.
  */
+#define PA_WORKSPACE_ZERO_BYTES 65536
 size_t pa_decode_workspace_bytes(int64_t num_seqs, int num_q_heads, int num_kv_heads,
                                  int head_dim, int64_t max_blocks_per_seq, int page_size,
                                  const pa_opts* opts);
@@ -242,9 +254,9 @@ size_t pa_decode_workspace_bytes(int64_t num_seqs, int num_q_heads, int num_kv_h
  * pa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the caller
  * and in use until the enqueued work finishes; if workspace is NULL the
  * library's own per-device workspace is used (as in pa_decode).  Its first
- * 256 bytes hold the balanced schedule's work counters: they must be zero
+ * PA_WORKSPACE_ZERO_BYTES hold work and arrival counters: they must be zero
  * before the workspace's first use (e.g. allocate it zeroed), and every call
- * leaves them zero, so a workspace can be reused by any later call of either
+ * leaves them zero, so a workspace can be reused by any later call of any
  * schedule.  Returns PA_ENOMEM if the given workspace is too small.
  */
 int pa_decode_ex(const pa_tensor* q,
@@ -392,6 +404,8 @@ typedef struct pa_stats {
     uint64_t last_schedule;         /* PA_SCHEDULE_* of the last call          */
     uint64_t append_launches;       /* pa_cache_append kernel launches         */
     uint64_t prefill_launches;      /* pa_prefill kernel launches              */
+    uint64_t fused_calls;           /* split calls merged inside the decode
+                                       kernel (no merge kernel launched)      */
 } pa_stats;
 
 int  pa_get_stats(pa_stats* stats);   /* PA_EINVAL if stats is NULL            */

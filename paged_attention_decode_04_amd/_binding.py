@@ -26,6 +26,9 @@ PA_SCHEDULE_AUTO, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED, PA_SCHEDULE_STAG
     0, 1, 2, 3, 4
 SCHEDULES = {"auto": PA_SCHEDULE_AUTO, "partitions": PA_SCHEDULE_PARTITIONS,
              "balanced": PA_SCHEDULE_BALANCED, "staged": PA_SCHEDULE_STAGED, "fitted": PA_SCHEDULE_FITTED}
+PA_MERGE_AUTO, PA_MERGE_KERNEL, PA_MERGE_FUSED = 0, 1, 2
+MERGES = {"auto": PA_MERGE_AUTO, "kernel": PA_MERGE_KERNEL, "fused": PA_MERGE_FUSED}
+PA_WORKSPACE_ZERO_BYTES = 65536
 
 
 class PaTensor(ctypes.Structure):
@@ -36,14 +39,14 @@ class PaTensor(ctypes.Structure):
 class PaOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("partition_tokens", ctypes.c_int32),
                 ("schedule", ctypes.c_int32), ("shares", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("window", ctypes.c_int32), ("merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 class PaStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
         "last_partition_tokens", "last_num_partitions", "last_variant", "balanced_calls",
-        "last_schedule", "append_launches", "prefill_launches")]
+        "last_schedule", "append_launches", "prefill_launches", "fused_calls")]
 
 
 class PaError(RuntimeError):
@@ -161,10 +164,11 @@ def _require_device(*ts):
 
 
 def make_opts(variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0,
-              window: int = 0) -> PaOpts:
+              window: int = 0, merge="auto") -> PaOpts:
     o = PaOpts()
     o.shares = int(shares)
     o.window = int(window)
+    o.merge = MERGES[merge] if isinstance(merge, str) else int(merge)
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     o.partition_tokens = int(partition_tokens)
     o.schedule = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
@@ -375,7 +379,7 @@ def pa_release() -> None:
 # ------------------------------------------------------------------ convenience
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None, *,
            variant="auto", partition_tokens: int = 0, schedule="auto", shares: int = 0,
-           window: int = 0, workspace=None, stream=None, out_dtype=None):
+           window: int = 0, merge="auto", workspace=None, stream=None, out_dtype=None):
     """Decode paged attention on torch tensors.
 
     q [B, Hq, D]; k_cache/v_cache [NP, P, Hkv, D] (NHD pool) -- each bf16, fp16
@@ -385,8 +389,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
     sequence's last ``window`` tokens only.  Returns out [B, Hq, D].  Work
     and any allocation go to ``stream`` (default: the current stream).
     Without a given workspace, the split-KV workspace is one kept per device
-    and stream (zeroed when made; a given one must start with 256 zero
-    bytes; see pa_decode_ex).
+    and stream (zeroed when made; a given one must start with
+    PA_WORKSPACE_ZERO_BYTES zero bytes; see pa_decode_ex).
     """
     import torch
     B, Hq, D = q.shape
@@ -397,7 +401,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale=None, out=None
     if out is None:
         with torch.cuda.stream(ts):
             out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
-    opts = make_opts(variant, partition_tokens, schedule, shares, window)
+    opts = make_opts(variant, partition_tokens, schedule, shares, window, merge)
     if workspace is None:
         n = pa_decode_workspace_bytes(B, Hq, Hkv, D, block_tables.shape[1], P, opts)
         if n:

@@ -2,7 +2,9 @@
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 VALU
 instructions disabled in the device code, then linked into one shared
-library next to this file.  Usage: ``python -m paged_attention_decode_04_amd.build``.
+library next to this file.  The streaming-read probes (``include/pa_probe.h``,
+measurement aids of the benchmark) go to a library of their own,
+``libpa_probe.so``.  Usage: ``python -m paged_attention_decode_04_amd.build``.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpa_decode.so")
 SOURCES = ["pa_api.hip", "pa_valu.hip", "pa_mfma.hip", "pa_append.hip", "pa_prefill.hip"]
+PROBE_SOURCES = ["pa_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -55,18 +59,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

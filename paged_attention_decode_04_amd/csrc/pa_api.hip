@@ -19,6 +19,9 @@
 #include "pa_decode.h"
 #include "pa_launch.h"
 
+static_assert(PA_WORKSPACE_ZERO_BYTES == pa::kWorkspaceZeroBytes, "workspace zero region");
+static_assert(PA_FUSE_MAX_GROUPS == pa::kFuseMaxGroups, "in-kernel merge groups");
+
 namespace {
 
 thread_local std::string t_err;
@@ -35,7 +38,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 struct Counters {
-    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0}, lean{0}, append{0}, prefill{0};
+    std::atomic<uint64_t> calls{0}, valu{0}, mfma{0}, split{0}, merge{0}, lean{0}, append{0}, prefill{0}, fused{0};
     std::atomic<uint64_t> last_t{0}, last_np{0}, last_variant{0}, last_schedule{0};
 } g_stats;
 
@@ -65,6 +68,7 @@ struct Plan {
     int fit_lo;         // fitted partitions: smallest size
     int64_t fit_grid;   // fitted partitions: workgroups partitions of part_tokens may need
     size_t fit_offset;  // fitted partitions: byte offset of the chosen size
+    bool fuse;          // partitions merged in the decode kernel (no merge kernel)
 };
 
 // Fitted partitions: sizes from max(kFitMinTokens, T / kFitRange) up to the
@@ -168,8 +172,10 @@ int validate(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const p
     if (out->shape[0] != B || out->shape[1] != num_q_heads || out->shape[2] != head_dim)
         return fail(PA_EINVAL, "out shape does not match q");
     if (opts) {
-        for (int i = 0; i < 3; ++i)
+        for (int i = 0; i < 2; ++i)
             if (opts->reserved[i]) return fail(PA_EINVAL, "pa_opts.reserved must be zero");
+        if (opts->merge < PA_MERGE_AUTO || opts->merge > PA_MERGE_FUSED)
+            return fail(PA_EINVAL, "unknown merge %d", opts->merge);
         if (opts->variant < PA_VARIANT_AUTO || opts->variant > PA_VARIANT_MFMA)
             return fail(PA_EINVAL, "unknown variant %d", opts->variant);
         if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
@@ -214,6 +220,31 @@ bool fit_allowed(const Geometry& g, const Plan& pl, const pa_opts* opts) {
 // and a smaller size than the fixed one is allowed.
 constexpr bool kFitAuto = true;
 
+// Whether a split call's partitions may be merged inside the decode kernel:
+// the matrix-core partition kernel (fixed or fitted), and few enough
+// (sequence, query block) groups for the workspace's counters.
+bool fuse_allowed(const Geometry& g, const Plan& pl) {
+    return pl.variant == PA_VARIANT_MFMA && !pl.lean && g.B * (g.Hq / pl.qw) <= pa::kFuseMaxGroups;
+}
+
+// The automatic choice of the in-kernel merge: fixed partitions, at most
+// two per group, and a grid of at most one workgroup per compute unit of the
+// MI355X (256).  Each partition of a merged group waits for its partial
+// stores to be written through before it counts itself in, and the last one
+// then reads the others' partials: a serial tail of about three memory round
+// trips.  That beats the merge kernel's launch and round trip only where the
+// tail merges two partials and no workgroup waits for a compute unit behind
+// one that is waiting (measured, per call in graphs of 64: batch16 (two
+// partitions, 256 workgroups) 17.8 -> 17.0 us warm, 18.8 -> 18.2 us cold;
+// slower elsewhere: single_seq (nine) 8.2 -> 8.6, hd256_gqa4 fitted 33.8 ->
+// 35.1, hd512_gqa4 fitted 37.2 -> 47.6, the 4096-token window on the
+// long-context batch (two partitions, 1024 workgroups) 177 -> 183).
+constexpr int64_t kFuseAutoMaxWorkgroups = 256;
+bool fuse_auto(const Geometry& g, const Plan& pl) {
+    const int64_t groups = g.B * (g.Hq / pl.qw);
+    return !pl.fit && pl.n_part <= 2 && groups * pl.n_part <= kFuseAutoMaxWorkgroups;
+}
+
 Plan make_plan(const Geometry& g, const pa_opts* opts) {
     Plan pl{};
     const int qw_mfma = g.qg < 16 ? g.qg : 16;
@@ -252,7 +283,7 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         pl.split = true;
         // One partial slot row per (group, unit) piece: groups + units at most.
         const size_t slots = (size_t)(groups + kLeanMaxUnits) * pl.qw;
-        pl.o_offset = pa::kLeanCounterBytes;
+        pl.o_offset = pa::kWorkspaceZeroBytes;
         pl.lse_offset = pl.o_offset + align_up(slots * g.D * sizeof(float), kAlign);
         pl.meta_offset = pl.lse_offset + align_up(slots * sizeof(float), kAlign);
         pl.ws_bytes = pl.meta_offset + align_up((size_t)(g.B + 4) * sizeof(int), kAlign);
@@ -313,11 +344,17 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
         pl.fit_grid = (int64_t)pl.n_part * groups;
         pl.n_part = (int)((max_ctx + pl.fit_lo - 1) / pl.fit_lo);
     }
+    // Partitions merged inside the decode kernel: the matrix-core partition
+    // kernel only, one arrival counter per group in the workspace's zero
+    // region.
+    const int merge = opts ? opts->merge : PA_MERGE_AUTO;
+    pl.fuse = pl.split && merge != PA_MERGE_KERNEL && fuse_allowed(g, pl) &&
+              (merge == PA_MERGE_FUSED || fuse_auto(g, pl));
     if (pl.split) {
-        // The balanced schedule's counters keep their place at the start, so
-        // one workspace can serve both schedules.
+        // The counters keep their place at the start, so one workspace can
+        // serve every schedule.
         const size_t n = (size_t)g.B * g.Hq * pl.n_part;
-        pl.o_offset = pa::kLeanCounterBytes;
+        pl.o_offset = pa::kWorkspaceZeroBytes;
         pl.lse_offset = pl.o_offset + align_up(n * g.D * sizeof(float), kAlign);
         pl.ws_bytes = pl.lse_offset + align_up(n * sizeof(float), kAlign);
         if (pl.fit) {
@@ -360,10 +397,10 @@ int library_workspace(int dev, size_t need, hipStream_t stream, void** out) {
         void* ptr = nullptr;
         e = hipMalloc(&ptr, sz);
         if (e != hipSuccess) return fail(PA_ENOMEM, "hipMalloc(%zu): %s", sz, hipGetErrorString(e));
-        // The balanced schedule's counters must start at zero (every call
-        // leaves them so); the zeroing is ordered before the call's kernels
-        // by the stream.
-        e = hipMemsetAsync(ptr, 0, pa::kLeanCounterBytes, stream);
+        // The workspace's counters must start at zero (every call leaves
+        // them so); the zeroing is ordered before the call's kernels by the
+        // stream.
+        e = hipMemsetAsync(ptr, 0, pa::kWorkspaceZeroBytes, stream);
         if (e != hipSuccess) {
             (void)hipFree(ptr);
             return fail(PA_EHIP, "hipMemsetAsync: %s", hipGetErrorString(e));
@@ -403,6 +440,9 @@ int check_plan(const Geometry& g, const Plan& pl, const pa_opts* opts) {
     if (opts && opts->schedule == PA_SCHEDULE_BALANCED && !pl.lean)
         return fail(PA_ENOTSUP, "balanced schedule needs the MFMA variant, head_dim 128/256 and at most %d sequences",
                     kLeanMaxBatch);
+    if (opts && opts->merge == PA_MERGE_FUSED && !fuse_allowed(g, pl))
+        return fail(PA_ENOTSUP, "the in-kernel merge needs the MFMA partition schedules (fixed or fitted) and at "
+                    "most %d (sequence, query block) groups", pa::kFuseMaxGroups);
     if (opts && opts->schedule == PA_SCHEDULE_FITTED && !fit_allowed(g, pl, opts))
         return fail(PA_ENOTSUP, "fitted partitions need the MFMA variant, no window, no partition size, at most "
                     "%d sequences and block tables of fewer than %d tokens", pa::kFitMaxBatch, pa::kFitMaxTokens);
@@ -481,6 +521,7 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
         p.fit_target = opts && opts->shares > 0 ? opts->shares : cu_count(dev);
         p.n_wg = (int)std::max<int64_t>(pl.fit_grid, p.fit_target);
     }
+    if (pl.fuse) p.fuse_ctr = reinterpret_cast<int*>(static_cast<char*>(ws) + pa::kFuseCounterOffset);
     if (pl.variant == PA_VARIANT_MFMA) {
         e = pa::launch_mfma(p, (int)g.D, g.kv_dtype, pl.qw, pl.split, s);
         if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma) launch: %s", hipGetErrorString(e));
@@ -491,9 +532,13 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
         g_stats.valu++;
     }
     if (pl.split) {
-        e = pa::launch_merge(p, (int)g.D, s);
-        if (e != hipSuccess) return fail(PA_EHIP, "merge launch: %s", hipGetErrorString(e));
-        g_stats.merge++;
+        if (pl.fuse) {
+            g_stats.fused++;
+        } else {
+            e = pa::launch_merge(p, (int)g.D, s);
+            if (e != hipSuccess) return fail(PA_EHIP, "merge launch: %s", hipGetErrorString(e));
+            g_stats.merge++;
+        }
         g_stats.split++;
     }
     g_stats.calls++;
@@ -553,9 +598,10 @@ int decode_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, cons
 constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-// Zero the first n dwords (the balanced schedule's work counters).
+// Zero the first n dwords (the workspace's counters).
 __global__ void pa_scratch_clear_kernel(uint32_t* p, int n) {
-    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0u;
 }
 
 std::mutex g_scratch_mu;
@@ -579,8 +625,9 @@ int device_scratch(int dev, hipStream_t stream, void** out) {
             return fail(PA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
         // The array starts zeroed; the counters are cleared once more here,
         // ordered before this call's kernels by the stream.
-        hipLaunchKernelGGL(pa_scratch_clear_kernel, dim3(1), dim3(64), 0, stream, static_cast<uint32_t*>(ptr),
-                           (int)(pa::kLeanCounterBytes / sizeof(uint32_t)));
+        constexpr int kWords = pa::kWorkspaceZeroBytes / (int)sizeof(uint32_t);
+        hipLaunchKernelGGL(pa_scratch_clear_kernel, dim3((kWords + 255) / 256), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(ptr), kWords);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(PA_EHIP, "scratch clear launch: %s", hipGetErrorString(e));
         g_scratch[dev] = ptr;
@@ -709,8 +756,12 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
     if (out->shape[0] != rows || out->shape[1] != num_q_heads || out->shape[2] != head_dim)
         return fail(PA_EINVAL, "out shape does not match q");
     if (opts) {
-        for (int i = 0; i < 3; ++i)
+        for (int i = 0; i < 2; ++i)
             if (opts->reserved[i]) return fail(PA_EINVAL, "pa_opts.reserved must be zero");
+        if (opts->merge == PA_MERGE_FUSED)
+            return fail(PA_ENOTSUP, "several-query attention merges split partitions in a kernel of its own");
+        if (opts->merge < PA_MERGE_AUTO || opts->merge > PA_MERGE_FUSED)
+            return fail(PA_EINVAL, "unknown merge %d", opts->merge);
         if (opts->variant != PA_VARIANT_AUTO && opts->variant != PA_VARIANT_MFMA)
             return fail(PA_ENOTSUP, "several-query attention runs on the MFMA kernel only");
         if (opts->partition_tokens < 0) return fail(PA_EINVAL, "partition_tokens < 0");
@@ -792,7 +843,7 @@ PrefillPlan plan_prefill(const Geometry& g, int64_t rows, const pa_opts* opts, b
     pl.split = pl.n_part > 1;
     if (pl.split) {
         const size_t n = (size_t)rows * g.Hq * pl.n_part;
-        pl.o_offset = pa::kLeanCounterBytes;
+        pl.o_offset = pa::kWorkspaceZeroBytes;
         pl.lse_offset = pl.o_offset + align_up(n * g.D * sizeof(float), kAlign);
         pl.ws_bytes = pl.lse_offset + align_up(n * sizeof(float), kAlign);
     }
@@ -1033,6 +1084,7 @@ int pa_get_stats(pa_stats* s) {
     s->append_launches = g_stats.append;
     s->prefill_launches = g_stats.prefill;
     s->last_schedule = g_stats.last_schedule;
+    s->fused_calls = g_stats.fused;
     return PA_OK;
 }
 
@@ -1045,6 +1097,7 @@ void pa_reset_stats(void) {
     g_stats.lean = 0;
     g_stats.append = 0;
     g_stats.prefill = 0;
+    g_stats.fused = 0;
     g_stats.last_schedule = 0;
     g_stats.last_t = 0;
     g_stats.last_np = 0;

@@ -42,6 +42,9 @@ struct DecodeParams {
     int*  fit_hint;                                         // fitted partitions: [n_wg][4] triple (b, query
                                                             // block, partition, size) each workgroup took in
                                                             // the previous call (a hint: checked before use)
+    int*  fuse_ctr;                                         // partitions merged in the decode kernel: one
+                                                            // arrival counter per (sequence, query block),
+                                                            // zero between calls; null = separate merge kernel
     float scale_log2;                                       // scale * log2(e)
 };
 
@@ -226,11 +229,24 @@ __device__ __forceinline__ void page_slot(const DecodeParams& p, int t, int& lp,
     }
 }
 
+// Partials that another workgroup merges in the same kernel (on any XCD, so
+// through any L2): stored and loaded as relaxed agent-scope atomics, i.e.
+// written through to and read from the device's point of coherence.
+// Ordering comes from waiting for the stores (s_waitcnt 0) before the
+// arrival count is taken, and from the count being read before the loads.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Running log-sum-exp merge of split partials (o_p fp32 rows of D, lse_p
-// base 2), by 64 threads holding D / 64 elements each.  Partials are added
-// four at a time, with their lse and o rows read together; the running
-// maximum rescales between batches.
-template <int D>
+// base 2), by 64 threads (lane = threadIdx.x % 64) holding D / 64 elements
+// each.  Partials are added four at a time, with their lse and o rows read
+// together; the running maximum rescales between batches.  COHERENT: the
+// partials were written in the same kernel (load_coherent).
+template <int D, bool COHERENT = false>
 struct LseMerge {
     static constexpr int EPT = D / 64;
     typedef float vec_t __attribute__((ext_vector_type(EPT)));
@@ -241,12 +257,18 @@ struct LseMerge {
     // (n_read >= 1 slots exist there).
     __device__ __forceinline__ static void read(const DecodeParams& p, int64_t first, int64_t step, int i0,
                                                 int n_read, float (&l)[4], vec_t (&v)[4]) {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x & 63;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t slot = first + (int64_t)min(i0 + j, n_read - 1) * step;
-            l[j] = p.part_lse[slot];
-            v[j] = *reinterpret_cast<const vec_t*>(p.part_o + slot * D + t * EPT);
+            if constexpr (COHERENT) {
+                l[j] = load_coherent(p.part_lse + slot);
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) v[j][e] = load_coherent(p.part_o + slot * D + t * EPT + e);
+            } else {
+                l[j] = p.part_lse[slot];
+                v[j] = *reinterpret_cast<const vec_t*>(p.part_o + slot * D + t * EPT);
+            }
         }
     }
     // Add the first `live` (0..4) of a batch; the others are ignored whatever
@@ -281,7 +303,7 @@ struct LseMerge {
     }
     // Normalised row into the output at element offset out_off (n == 0 writes zeros).
     __device__ __forceinline__ void store(const DecodeParams& p, int64_t out_off) const {
-        const int t = threadIdx.x;
+        const int t = threadIdx.x & 63;
         const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
         for (int e = 0; e < EPT; e += 2)
@@ -293,17 +315,18 @@ struct LseMerge {
 // into the output row at element offset out_off (in the output's type).  The
 // first 16 partials (8 at head_dim 512) are all read before any is added:
 // one round trip to memory for them.
-template <int D>
+template <int D, bool COHERENT = false>
 __device__ __forceinline__ void merge_partials(const DecodeParams& p, int64_t first, int64_t step, int n,
                                                int64_t out_off) {
     constexpr int NB = D <= 256 ? 4 : 2;        // batches of four read at once
-    LseMerge<D> m;
+    typedef LseMerge<D, COHERENT> M;
+    M m;
     float l[NB][4];
-    typename LseMerge<D>::vec_t v[NB][4];
+    typename M::vec_t v[NB][4];
     if (n > 0) {
 #pragma unroll
         for (int k = 0; k < NB; ++k)
-            if (4 * k < n) LseMerge<D>::read(p, first, step, 4 * k, n, l[k], v[k]);
+            if (4 * k < n) M::read(p, first, step, 4 * k, n, l[k], v[k]);
 #pragma unroll
         for (int k = 0; k < NB; ++k)
             if (4 * k < n) m.add(l[k], v[k], n - 4 * k);

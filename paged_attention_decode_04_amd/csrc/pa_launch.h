@@ -43,8 +43,14 @@ constexpr int kLeanDynPerWg = 6;
 constexpr int kLeanMinUnit = 16;
 // Below this many tiles per workgroup the static units cover all the work.
 constexpr int kLeanDynMinPerWg = 256;
-// Workspace: two int counters at its start, zero between calls.
+// Workspace: its first kWorkspaceZeroBytes are counters that are zero
+// between calls (every call leaves them so): the balanced schedule's two at
+// byte 0, then one arrival counter per (sequence, query block) group for
+// partitions merged inside the decode kernel, at most kFuseMaxGroups.
 constexpr int kLeanCounterBytes = 256;
+constexpr int kWorkspaceZeroBytes = 65536;
+constexpr int kFuseCounterOffset = kLeanCounterBytes;
+constexpr int kFuseMaxGroups = (kWorkspaceZeroBytes - kFuseCounterOffset) / 4;
 
 // Several queries per sequence (MFMA, 16-column query blocks), followed by
 // the per-row merge when split.

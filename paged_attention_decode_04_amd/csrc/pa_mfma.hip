@@ -245,6 +245,23 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
         if (wave == 0) {
             int fb = 0, fqb = 0, fpart = 0, fT = T, fL = 0;
             const bool live = fit_locate(p, (int)blockIdx.x, len, fb, fqb, fpart, fT, fL);
+            if (p.fuse_ctr && blockIdx.x == 0) {
+                // Merged in this kernel, a sequence with no tokens has no
+                // partition and no merge to write its zero rows: this wave
+                // writes them (len[] holds the clamped lengths now).
+                const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < kFitChunks; ++c) {
+                    uint64_t m = __ballot(c * 64 + lane < p.B && len[c] == 0);
+                    while (m) {
+                        const int bb = c * 64 + __builtin_ctzll(m);
+                        m &= m - 1;
+                        for (int idx = lane; idx < p.Hq * (D / 8); idx += 64)
+                            store8(p.out, p.out_dtype, (int64_t)bb * p.o_sb + (int64_t)(idx / (D / 8)) * p.o_sh +
+                                   (idx % (D / 8)) * 8, z);
+                    }
+                }
+            }
             if (lane == 0) {
                 s_fit[0] = fb;
                 s_fit[1] = fqb;
@@ -277,6 +294,12 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     const int g = h0 / (p.Hq / p.Hkv);
     const int te = min(L, ts + T);
     const bool col_live = HALF ? (n < 8 && n < qw) : (n < qw);
+    // Partitions merged in this kernel (p.fuse_ctr): the group's partition
+    // count (partition 0 runs even for an empty sequence); a group of one
+    // partition writes its output directly, the others write partials and
+    // the last of them to arrive merges them.
+    const int n_used = SPLIT && p.fuse_ctr ? max(1, (L - t_base + T - 1) / T) : 0;
+    const bool direct = !SPLIT || n_used == 1;
     __syncthreads();
 
     f32x4 o[NO];
@@ -295,14 +318,45 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     merge_waves<D>(lds, o, m_run, l_run, qw, n, q, wave, tid,
                    [&](int jq, int d0, const float (&ov)[8], float lse) {
         const int h = h0 + jq;
-        if constexpr (!SPLIT) {
+        if (direct) {
             store8(p.out, p.out_dtype, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d0, ov);
         } else {
             const int64_t slot = ((int64_t)b * p.Hq + h) * p.n_part + part;
-            store_f32x8(p.part_o + slot * D + d0, ov);
-            if (d0 == 0) p.part_lse[slot] = lse;
+            if (p.fuse_ctr) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) store_coherent(p.part_o + slot * D + d0 + i, ov[i]);
+                if (d0 == 0) store_coherent(p.part_lse + slot, lse);
+            } else {
+                store_f32x8(p.part_o + slot * D + d0, ov);
+                if (d0 == 0) p.part_lse[slot] = lse;
+            }
         }
     });
+    if constexpr (SPLIT) {
+        if (p.fuse_ctr && n_used > 1) {
+            // Count this partition in once all its partial stores are
+            // complete; the partition that arrives last merges the group
+            // (and sets the counter back to zero for the next call).
+            __shared__ int s_last;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                int* ctr = p.fuse_ctr + (b * n_qb + qb);
+                const bool last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                                  n_used - 1;
+                if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_last = last;
+            }
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(s_last)) {
+                for (int r = wave; r < qw; r += kMWaves) {
+                    const int h = h0 + r;
+                    merge_partials<D, true>(p, ((int64_t)b * p.Hq + h) * p.n_part, 1, n_used,
+                                            (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
+                }
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -35,6 +35,40 @@ def test_library_exports_every_declared_symbol():
     assert not missing, f"not exported: {missing}"
 
 
+PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "pa_probe.h")
+
+
+def test_probe_library_exports_and_validates():
+    """libpa_probe.so (the benchmark's streaming-read probes) exports every
+    function pa_probe.h declares and refuses bad arguments before any HIP
+    call."""
+    from paged_attention_decode_04_amd import probe
+    lib = ctypes.CDLL(probe.PROBE_LIB_PATH)
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(pa_probe_[a-z_]+)\s*\(", text, flags=re.M)))
+    assert names == ["pa_probe_read_contiguous", "pa_probe_read_paged"]
+    assert all(hasattr(lib, n) for n in names)
+    plib = probe._load()
+    assert plib.pa_probe_read_contiguous(None, 16, 1, None, None) == 1
+    assert plib.pa_probe_read_contiguous(0x1008, 16, 1, 0x2000, None) == 1      # misaligned base
+    assert plib.pa_probe_read_contiguous(0x1000, 17, 1, 0x2000, None) == 1      # not whole 16-byte chunks
+    d = probe.PaProbePaged()
+    assert plib.pa_probe_read_paged(ctypes.byref(d), 256, 0x2000, None) == 1   # null pools
+    d.k = d.v = 0x1000
+    d.block_tables = d.context_lens = 0x3000
+    d.row_bytes, d.batch, d.num_kv_heads, d.num_pages, d.max_blocks, d.bt_sb = 256, 4, 2, 8, 4, 4
+    d.k_sp = d.v_sp = 16 * 2 * 256
+    d.k_ss = d.v_ss = 2 * 256
+    d.k_sh = d.v_sh = 256
+    d.page_size = 24                                                            # not a power of two
+    assert plib.pa_probe_read_paged(ctypes.byref(d), 256, 0x2000, None) == 1
+    d.page_size = 16
+    d.row_bytes = 128
+    assert plib.pa_probe_read_paged(ctypes.byref(d), 256, 0x2000, None) == 1
+    d.row_bytes = 256
+    assert plib.pa_probe_read_paged(ctypes.byref(d), 0, 0x2000, None) == 1     # no workgroups
+
+
 def test_version_and_strerror():
     assert pa.version() == "0.1.0"
     for code in range(7):
@@ -149,8 +183,15 @@ def test_strided_nhd_views_are_accepted():
 def test_opts_are_validated():
     o = pa.make_opts("valu", 0)
     assert check(args(), o) == pa.PA_OK
-    o.reserved[2] = 1
+    o.reserved[1] = 1
     assert check(args(), o) == pa.PA_EINVAL
+    assert check(args(), pa.make_opts(merge=3)) == pa.PA_EINVAL
+    # the in-kernel merge: MFMA partition schedules only
+    assert check(args(), pa.make_opts("mfma", 64, merge="fused")) == pa.PA_OK
+    assert check(args(), pa.make_opts("mfma", 0, "fitted", merge="fused")) == pa.PA_OK
+    assert check(args(), pa.make_opts("valu", 64, merge="fused")) == pa.PA_ENOTSUP
+    assert check(args(), pa.make_opts("mfma", 0, "balanced", merge="fused")) == pa.PA_ENOTSUP
+    assert check(args(), pa.make_opts("mfma", 64, merge="kernel")) == pa.PA_OK
     o = pa.make_opts(7, 0)
     assert check(args(), o) == pa.PA_EINVAL
     o = pa.make_opts("valu", -5)
@@ -233,7 +274,7 @@ def test_workspace_bytes():
     o_bytes = 1 * 16 * parts * 128 * 4
     lse_bytes = 1 * 16 * parts * 4
     rnd = lambda x: (x + 255) // 256 * 256
-    HDR = 256                    # the balanced schedule's counters, kept in both layouts
+    HDR = pa.PA_WORKSPACE_ZERO_BYTES   # the counters (balanced schedule, in-kernel merge), in every layout
     assert n == HDR + rnd(o_bytes) + rnd(lse_bytes)
     assert pa.pa_decode_workspace_bytes(-1, 16, 8, 128, 4, 32, None) == 0
     # balanced schedule: one partial slot per (group, unit) piece it can
@@ -302,7 +343,8 @@ def test_stats_roundtrip():
     assert s["calls"] == 0 and s["valu_launches"] == 0
     assert set(s) == {"calls", "valu_launches", "mfma_launches", "split_calls", "merge_launches",
                       "last_partition_tokens", "last_num_partitions", "last_variant",
-                      "balanced_calls", "last_schedule", "append_launches", "prefill_launches"}
+                      "balanced_calls", "last_schedule", "append_launches", "prefill_launches",
+                      "fused_calls"}
 
 
 # ------------------------------------------------------------------ KV-cache append
@@ -410,7 +452,7 @@ def test_prefill_workspace_bytes():
     # -> split: T = clamp(1024 * 64 / 256 = 256) = 256 -> 4 partitions
     n = pa.pa_prefill_workspace_bytes(4, 4, 16, 8, 128, 64, 16, None)
     parts = 4
-    assert n == 256 + rnd(4 * 16 * parts * 128 * 4) + rnd(4 * 16 * parts * 4)
+    assert n == pa.PA_WORKSPACE_ZERO_BYTES + rnd(4 * 16 * parts * 128 * 4) + rnd(4 * 16 * parts * 4)
     # many query rows: enough blocks, no split
     assert pa.pa_prefill_workspace_bytes(4096, 4, 16, 8, 128, 64, 16, None) == 0
     assert pa.pa_prefill_workspace_bytes(4, 4, 12, 8, 128, 64, 16, None) == 0   # Hq % Hkv

@@ -23,10 +23,14 @@ pytestmark = pytest.mark.gpu
 # Kernel variant and work schedule: vector-ALU kernel on fixed partitions,
 # MFMA kernel on fixed partitions, MFMA kernel on balanced shares, MFMA
 # kernel on fitted partitions (size picked on the device; no window).
-VARIANTS = ["valu", "mfma", "mfma-bal", "mfma-fit"]
-VARIANTS_W = ["valu", "mfma", "mfma-bal"]            # those that take a window
+# "-fused": the same partitions merged inside the decode kernel by the last
+# partition of each group to finish (no merge kernel).
+VARIANTS = ["valu", "mfma", "mfma-bal", "mfma-fit", "mfma-fused", "mfma-fit-fused"]
+VARIANTS_W = ["valu", "mfma", "mfma-bal", "mfma-fused"]   # those that take a window
 _MODE = {"valu": ("valu", "partitions"), "mfma": ("mfma", "partitions"),
-         "mfma-bal": ("mfma", "balanced"), "mfma-fit": ("mfma", "fitted")}
+         "mfma-bal": ("mfma", "balanced"), "mfma-fit": ("mfma", "fitted"),
+         "mfma-fused": ("mfma", "partitions"), "mfma-fit-fused": ("mfma", "fitted")}
+_MERGE = {"mfma-fused": "fused", "mfma-fit-fused": "fused"}
 # Share counts the balanced schedule is exercised with: automatic, a single
 # share (every group written directly), and counts whose boundaries fall
 # mid-group, mid-sequence and on 16-token tiles of different sequences.
@@ -55,20 +59,29 @@ def knobs(variant, tokens):
         return [dict(shares=n) for n in SHARES]
     if _MODE[variant][1] == "fitted":
         return [dict(shares=n) for n in FIT_TARGETS]
+    if variant == "mfma-fused":
+        # every split size, and one partition (no split: nothing to merge)
+        return [dict(partition_tokens=T) for T in tokens + (64, 1 << 20)]
     return [dict(partition_tokens=T) for T in tokens]
 
 
-def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0, out_dtype=None):
+def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0, out_dtype=None, workspace=None):
     kernel, schedule = _MODE[variant]
+    merge = _MERGE.get(variant, "kernel")
     q, k, v = d.call(call)
     out = torch.full(q.shape, float("nan"), dtype=out_dtype or q.dtype, device=q.device)   # every row must be written
     pa.pa_reset_stats()
     pa.decode(q, k, v, d.block_tables, d.context_lens, d.w.scale, out=out, variant=kernel,
-              partition_tokens=partition_tokens, schedule=schedule, shares=shares, window=window)
+              partition_tokens=partition_tokens, schedule=schedule, shares=shares, window=window,
+              merge=merge if kernel == "mfma" and schedule != "balanced" else "auto", workspace=workspace)
     torch.cuda.synchronize()
     s = pa.pa_get_stats()
     assert s["calls"] == 1
     assert s[f"{kernel}_launches"] == 1, s
+    if merge == "fused":
+        assert s["merge_launches"] == 0 and s["fused_calls"] == s["split_calls"], s
+    elif s["split_calls"]:
+        assert s["merge_launches"] == 1 and s["fused_calls"] == 0, s
     expect = {"balanced": pa.PA_SCHEDULE_BALANCED, "partitions": pa.PA_SCHEDULE_PARTITIONS,
               # a call that does not split runs one partition per sequence
               "fitted": pa.PA_SCHEDULE_FITTED if s["split_calls"] else pa.PA_SCHEDULE_PARTITIONS}
@@ -252,7 +265,7 @@ def test_split_sizes_agree(variant):
         y, s = gpu_run(d, variant=variant, **kn)
         seen.add(s["split_calls"])
         assert_parity(y, ref, f"{kn}")
-    assert seen == ({1} if variant in ("mfma-bal", "mfma-fit") else {0, 1})
+    assert seen == ({1} if variant in ("mfma-bal", "mfma-fit", "mfma-fit-fused") else {0, 1})
 
 
 # ------------------------------------------------------------------ layouts
@@ -439,15 +452,17 @@ def test_schedule_batch_caps(schedule, B):
     assert_parity(bits(out), ref, f"automatic past the {schedule} cap B={B}")
 
 
-@pytest.mark.parametrize("schedule", ["partitions", "balanced", "fitted"])
-def test_graph_capture_replays_match_eager(schedule):
+@pytest.mark.parametrize("schedule,merge", [("partitions", "kernel"), ("balanced", "auto"), ("fitted", "kernel"),
+                                            ("partitions", "fused"), ("fitted", "fused")])
+def test_graph_capture_replays_match_eager(schedule, merge):
     """Calls captured in a HIP graph: every replay, with eager work and
     synchronisations in between, equals the eager result bit for bit (the
-    balanced schedule's work counters return to zero after every replay)."""
+    balanced schedule's work counters and the in-kernel merge's arrival
+    counters return to zero after every replay)."""
     inp = make_inputs("single_seq", seed=2)
     d = to_device(inp)
     q, k, v = d.call(3)
-    kw = dict(variant="mfma", schedule=schedule)
+    kw = dict(variant="mfma", schedule=schedule, merge=merge)
     eager = pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, **kw)
     torch.cuda.synchronize()
     out = torch.empty_like(q)
@@ -473,7 +488,7 @@ def test_graph_capture_replays_match_eager(schedule):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         assert not torch.equal(junk, eager)
-        assert torch.all(ws[:256] == 0), f"counters after replay {i}"
+        assert torch.all(ws[:pa.PA_WORKSPACE_ZERO_BYTES] == 0), f"counters after replay {i}"
 
 
 # ------------------------------------------------------------------ balanced schedule
@@ -536,6 +551,7 @@ def test_fitted_workspace_garbage_and_foreign_hints():
     raw = torch.randint(0, 256, (ws_n + 256,), dtype=torch.uint8, device="cuda")
     off = (-raw.data_ptr()) % 256
     ws = raw[off:off + ws_n]
+    ws[:pa.PA_WORKSPACE_ZERO_BYTES] = 0         # the counters must start at zero; the rest is garbage
     first = {}
     for rnd in range(3):
         for i, (inp, d, q, k, v) in enumerate(cases):
@@ -598,7 +614,7 @@ def test_balanced_workspace_reuse_and_counters():
         pa.decode(q, k, v, d.block_tables, d.context_lens, inp.w.scale, out=out, variant=var,
                   schedule=sch, shares=shares, partition_tokens=T, workspace=ws)
         torch.cuda.synchronize()
-        assert torch.all(ws[:256] == 0), f"call {i}: counters not reset"
+        assert torch.all(ws[:pa.PA_WORKSPACE_ZERO_BYTES] == 0), f"call {i}: counters not reset"
         y = bits(out)
         assert_parity(y, ref, f"reuse call {i} {var} {sch} {shares} T={T}")
         if sch == "balanced" and shares == 256:
@@ -1031,6 +1047,47 @@ def test_prefill_speculative_decode_full_size_all_rows():
     assert_parity(y2, ref, "speculative decode, all rows, per-block kernel")
     del d, host
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ in-kernel merge
+@pytest.mark.parametrize("name", ["tiny", "single_seq", "batch16", "hd256_gqa4", "hd512_gqa4"])
+def test_fused_merge_bitwise_equals_merge_kernel(name):
+    """Partitions merged inside the decode kernel (last arriver per group)
+    and by the separate merge kernel add the same partials in the same order:
+    bit-identical outputs, on fixed and fitted partitions, over one
+    workspace whose counters are zero after every call."""
+    inp = make_inputs(name, seed=7)
+    d = to_device(inp)
+    q, k, v = d.call(0)
+    B, Hq, D = q.shape
+    NP, P, Hkv, _ = k.shape
+    n = max(pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, pa.make_opts("mfma", T, sch))
+            for sch, T in (("partitions", 64), ("partitions", 0), ("fitted", 0)))
+    raw = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
+    ws = raw[(-raw.data_ptr()) % 256:][:n]
+    ref = oracle_run(inp)
+    for kn in (dict(partition_tokens=64), dict(partition_tokens=128), dict(), dict(shares=7), dict(shares=0),
+               dict(shares=300)):
+        fit = "shares" in kn
+        y_k, s_k = gpu_run(d, variant="mfma-fit" if fit else "mfma", workspace=ws, **kn)
+        y_f, s_f = gpu_run(d, variant="mfma-fit-fused" if fit else "mfma-fused", workspace=ws, **kn)
+        assert torch.all(ws[:pa.PA_WORKSPACE_ZERO_BYTES] == 0), f"{name} {kn}: counters not reset"
+        assert np.array_equal(y_f, y_k), f"{name} {kn}: in-kernel merge differs from the merge kernel"
+        assert_parity(y_f, ref, f"{name} fused {kn} (split {s_f['split_calls']})")
+
+
+def test_fused_merge_empty_sequences_fitted():
+    """Fitted partitions merged in the kernel: sequences with no tokens have
+    no partition, so their zero rows come from the first workgroup."""
+    lens = (0, 700, 0, 5, 2048, 0, 1)
+    w = custom(batch=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=256, page_size=32, ctx=lens)
+    inp = make_inputs(w, seed=41, poison_unused=True)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for n in (0, 1, 5, 64):
+        y, s = gpu_run(d, variant="mfma-fit-fused", shares=n)
+        assert s["split_calls"] == 1, s
+        assert_parity(y, ref, f"fitted fused, empty sequences, target {n}")
 
 
 # ------------------------------------------------------------------ numerics table

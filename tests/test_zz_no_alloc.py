@@ -55,7 +55,9 @@ def oracle_run(inp):
 CASES = [
     # (workload, knobs, schedule expected) -- each call smaller than the one before
     ("hd256_gqa4", dict(), pa.PA_SCHEDULE_FITTED),
+    ("hd256_gqa4", dict(merge="fused"), pa.PA_SCHEDULE_FITTED),
     ("batch16", dict(schedule="balanced"), pa.PA_SCHEDULE_BALANCED),
+    ("batch16", dict(merge="fused"), pa.PA_SCHEDULE_PARTITIONS),
     ("batch16", dict(), pa.PA_SCHEDULE_PARTITIONS),
     ("tiny", dict(partition_tokens=64), pa.PA_SCHEDULE_PARTITIONS),
 ]
