@@ -74,38 +74,57 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "partitions", "balanced", "fitted"])
     ap.add_argument("--shares", type=int, default=0, help="balanced schedule: shares; fitted: workgroups to fill (0 = automatic)")
+    ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "fused"],
+                    help="split partitions merged by a second kernel or inside the decode kernel")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the streaming-read probes")
     ap.add_argument("--profile", action="store_true",
                     help="timed steps only (no per-config sweep, no CPU baseline): for rocprofv3 runs")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a HIP graph (as the per-config lines are timed) instead of "
+                         "launching it eagerly: for kernel traces of the small, launch-bound workloads")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="only the several-query (chunked-prefill) line, printed as the JSON line: "
                          "for rocprofv3 runs over its kernel")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a plain device copy of this many MiB (HBM reference and the "
                          "calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="a headline oracle run longer than this is not repeated (else: median of 3)")
     return ap.parse_args()
 
 
 # ----------------------------------------------------------------------------
-def make_call(pa, d, call, knobs):
+def make_workspace(pa, d, knobs):
+    """A zeroed, 256-byte-aligned workspace for calls of d's shape (None when
+    they do not split)."""
+    import torch
+    q, k, v = d.call(0)
+    B, Hq, D = q.shape
+    NP, P, Hkv, _ = k.shape
+    n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, pa.make_opts(**knobs))
+    if not n:
+        return None
+    raw = torch.zeros(n + 256, dtype=torch.uint8, device=q.device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + n]
+
+
+def make_call(pa, d, call, knobs, ws=None):
     """A closure issuing one decode call on the current stream; knobs are
-    make_opts' keyword arguments (variant, partition_tokens, schedule, shares)."""
+    make_opts' keyword arguments (variant, partition_tokens, schedule, shares,
+    window, merge).  The calls of one workload share ws, as the layers of a
+    decode step share one workspace (a new one is made when none is given)."""
     import torch
     q, k, v = d.call(call)
     out = torch.empty_like(q)
     B, Hq, D = q.shape
     NP, P, Hkv, _ = k.shape
     opts = pa.make_opts(**knobs)
-    n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, opts)
-    ws = None
-    if n:
-        raw = torch.zeros(n + 256, dtype=torch.uint8, device=q.device)
-        off = (-raw.data_ptr()) % 256
-        ws = raw[off:off + n]
+    if ws is None:
+        ws = make_workspace(pa, d, knobs)
     scale = d.w.scale
 
     def run():
@@ -161,6 +180,8 @@ def launch_info(st):
     launch = {"variant": variant, "schedule": schedule,
               "partition_tokens": int(st["last_partition_tokens"]),
               ("shares" if balanced else "partitions"): int(st["last_num_partitions"])}
+    if st["split_calls"] and not balanced:
+        launch["merge"] = "fused" if st["fused_calls"] else "kernel"
     return kernel, (merge if st["merge_launches"] else None), launch
 
 
@@ -171,12 +192,54 @@ EXTRA = (("long_ctx_gqa8", 4096, "bf16"), ("hd256_gqa4", 1024, "bf16"),
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 
 
-def per_config(pa, knobs, torch, workloads_mod):
+def probe_sink(torch):
+    return torch.zeros(4096, dtype=torch.int32, device="cuda")
+
+
+def stream_probes(torch, d):
+    """Streaming-read references (libpa_probe.so): a 4 GiB contiguous read,
+    and the headline workload's own paged NHD pattern (256-byte K and V rows
+    of one KV head at the 2 KB slot stride, pages in block-table order), at
+    several workgroup counts.  GB/s = bytes read / event time per read."""
+    from paged_attention_decode_04_amd import probe
+    sink = probe_sink(torch)
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    res = {"contiguous_GBps": {}, "nhd_GBps": {}}
+    for n_wg in (256, 512, 1024, 2048):
+        fn = lambda: probe.read_contiguous(buf, n_wg, sink)
+        event_time_ms(fn, 2, torch)
+        ms = event_time_ms(fn, 10, torch) / 10
+        res["contiguous_GBps"][n_wg] = round(buf.numel() / (ms * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    desc = probe.paged_desc(d.k[0], d.v[0], d.block_tables, d.context_lens)
+    import workloads as wl
+    nbytes = wl.kv_bytes(d.w, d.layout.context_lens)
+    for n_wg in (256, 512):
+        fn = lambda: probe.read_paged(desc, n_wg, sink)
+        event_time_ms(fn, 2, torch)
+        ms = event_time_ms(fn, 10, torch) / 10
+        res["nhd_GBps"][n_wg] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    res["stream_peak_GBps"] = max(res["contiguous_GBps"].values())
+    res["nhd_peak_GBps"] = max(res["nhd_GBps"].values())
+    res["note"] = ("contiguous: 4 GiB read once per launch, n_wg workgroups of 256 threads; nhd: the K and V "
+                   "rows of the headline workload read through its block tables in equal shares (probe kernels "
+                   "of libpa_probe.so, event-timed)")
+    log(f"[probe] {res}")
+    return res
+
+
+def per_config(pa, knobs, torch, workloads_mod, probes=None):
     """Time every workload: warm (inputs reused, MALL may hold them) and, for
     footprints that fit the 256 MB MALL, cold (calls rotate over replicas of
     the KV pools totalling >= 1 GB).  Windowed lines count the KV bytes of
-    the attended tokens only."""
+    the attended tokens only.  Unwindowed 16-bit lines also time the paged
+    streaming-read probe over the same pools (warm and cold), the reference
+    for what the memory system gives that access pattern."""
     import numpy as np
+    from paged_attention_decode_04_amd import probe
+    sink = probe_sink(torch)
+    stream_peak = probes["stream_peak_GBps"] if probes else None
     res = {}
     runs = [(name, 0, "bf16") for name in workloads_mod.ORDER] + list(EXTRA)
     for name, window, dt in runs:
@@ -189,7 +252,9 @@ def per_config(pa, knobs, torch, workloads_mod):
         kn = dict(knobs, window=window)
         kvb = workloads_mod.kv_bytes(w, lens, window, ELEM_BYTES[dt])
         n_calls = w.calls if w.calls > 1 else 1
-        calls = [make_call(pa, d, i, kn)[0] for i in range(n_calls)]
+        pa.pa_reset_stats()
+        ws = make_workspace(pa, d, kn)
+        calls = [make_call(pa, d, i, kn, ws)[0] for i in range(n_calls)]
         entry = {"kv_bytes_per_call": kvb, "calls": n_calls}
         if window:
             entry["window"] = window
@@ -198,6 +263,9 @@ def per_config(pa, knobs, torch, workloads_mod):
             ms = event_time_ms(calls[0], 3, torch)
             ms = event_time_ms(calls[0], 10, torch) / 10
             entry["us_per_call"] = round(1e3 * ms, 2)
+            if probes and not window and dt == "bf16":
+                # the paged probe of this very pattern (stream_probes), its best workgroup count
+                entry["probe_us"] = round(kvb / (probes["nhd_peak_GBps"] * 1e3), 2)
         else:
             # one graph of at least 64 calls, so graph-launch cost is amortised
             warm = calls * max(1, -(-64 // n_calls))
@@ -213,14 +281,24 @@ def per_config(pa, knobs, torch, workloads_mod):
                     d2 = workloads_mod.DeviceInputs(w, d.q, k2, v2, d.block_tables, d.context_lens,
                                                     d.layout)
                     reps_k.append(d2)
-                cold_calls = []
-                for i in range(n_calls):
-                    for d2 in reps_k:
-                        cold_calls.append(make_call(pa, d2, i, kn)[0])
-                cold_calls = cold_calls[:min(len(cold_calls), max(R, 2048))]
+                # call k on replica k mod R: each replica's bytes were last
+                # read R - 1 calls (>= 1 GB) before; at least 64 calls per
+                # graph, so the graph's own launch is amortised as in the
+                # warm line
+                n_cold = max(64, min(n_calls * R, 2048))
+                cold_calls = [make_call(pa, reps_k[k % R], k % n_calls, kn, ws)[0] for k in range(n_cold)]
                 entry["us_per_call_cold"] = round(graph_time_us(cold_calls, 5, torch), 3)
                 entry["cold_replicas"] = R
+                if not window and dt != "f32" and w.head_dim <= 256:
+                    # the same bytes, read with no arithmetic, over the same replicas
+                    descs = [probe.paged_desc(d2.k[0], d2.v[0], d2.block_tables, d2.context_lens) for d2 in reps_k]
+                    pcalls = [(lambda dd=dd: probe.read_paged(dd, 256, sink)) for dd in descs]
+                    entry["probe_us_cold"] = round(graph_time_us(pcalls * max(1, 64 // len(pcalls)), 5, torch), 3)
                 del reps_k
+            if not window and dt != "f32" and w.head_dim <= 256:
+                desc = probe.paged_desc(d.k[0], d.v[0], d.block_tables, d.context_lens)
+                entry["probe_us"] = round(graph_time_us([lambda: probe.read_paged(desc, 256, sink)] * 64, 20,
+                                                        torch), 3)
         kernel, _, launch = launch_info(pa.pa_get_stats())
         entry["kernel"] = kernel
         entry.update(launch)
@@ -229,6 +307,13 @@ def per_config(pa, knobs, torch, workloads_mod):
                 gbs = kvb / (entry[key] * 1e-6) / 1e9
                 entry[key.replace("us_per_call", "kv_GBps")] = round(gbs, 1)
                 entry[key.replace("us_per_call", "hbm_frac")] = round(gbs / HBM_PEAK_GBS, 4)
+                if stream_peak:
+                    entry[key.replace("us_per_call", "stream_frac")] = round(gbs / stream_peak, 4)
+        for key in ("probe_us", "probe_us_cold"):
+            if key in entry:
+                # the probe's time as a fraction of the decode call's: 1.0 = as fast as streaming the bytes
+                call_key = key.replace("probe_us", "us_per_call")
+                entry[key.replace("probe_us", "frac_of_probe")] = round(entry[key] / entry[call_key], 4)
         key = name + (f"_w{window}" if window else "") + (f"_{dt}" if dt != "bf16" else "")
         res[key] = entry
         log(f"[per_config] {key}: {entry}")
@@ -305,38 +390,109 @@ def prefill_line(pa, torch, workloads_mod, B=8, ctx=4096, chunk=512, Hq=32, Hkv=
     return entry
 
 
-def cpu_baseline(d, w, target_s, workloads_mod):
-    """The oracle as it stands, on the host cores, over whole sequences of the
-    same workload (all query heads) until about target_s seconds."""
-    import numpy as np
-    import oracle
-    host = workloads_mod.host_copy(d)
-    threads = oracle.default_threads()
-    t_total, b_done, bytes_done, tok = 0.0, 0, 0, 0
-    lens = host.context_lens
-    for b in range(w.batch):
-        pairs = np.array([(b, h) for h in range(w.num_q_heads)], dtype=np.int32)
+def _median_time(fn, runs):
+    ts = []
+    for _ in range(runs):
         t0 = time.perf_counter()
-        oracle.attention_pairs(host.q[0], host.k[0], host.v[0], host.block_tables, lens, w.scale,
-                               w.num_kv_heads, pairs, threads=threads)
-        t_total += time.perf_counter() - t0
-        b_done += 1
-        tok += int(lens[b])
-        bytes_done += int(lens[b]) * w.num_kv_heads * w.head_dim * 4
-        if t_total >= target_s:
-            break
-    gbs = bytes_done / t_total / 1e9
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2], len(ts)
+
+
+def cpu_baseline(d, w, target_s, workloads_mod):
+    """The oracle as it stands (fp64, the plain definition) on the host cores:
+    the headline workload's whole call on all threads, and one call of each
+    other workload on all threads and, for the three small ones, on one
+    thread.  Median of 3 runs (one where a run takes longer than target_s);
+    input generation and host copies are not timed.  Unit: KV-read GB/s."""
+    import oracle
+    threads = oracle.default_threads()
+    host = workloads_mod.host_copy(d)
+    lens = host.context_lens
+    kvb = workloads_mod.kv_bytes(w, lens)
+
+    def head():
+        oracle.attention(host.q[0], host.k[0], host.v[0], host.block_tables, lens, w.scale, w.num_kv_heads,
+                         threads=threads)
+    t0 = time.perf_counter()
+    head()
+    first = time.perf_counter() - t0
+    t_med, runs = (first, 1) if first > target_s else _median_time(head, 3)
+    per = {}
+    for name in ("tiny", "single_seq", "batch16", "hd256_gqa4"):
+        wk = workloads_mod.WORKLOADS[name]
+        inp = workloads_mod.make_inputs(wk, seed=0)
+        q, k, v = inp.call(0)
+        nbytes = workloads_mod.kv_bytes(wk, inp.context_lens)
+        entry = {"kv_bytes_per_call": nbytes}
+        for label, nt in (("all", threads), ("1thread", 1)):
+            if label == "1thread" and name == "hd256_gqa4":
+                continue
+            tm, n = _median_time(lambda: oracle.attention(q, k, v, inp.block_tables, inp.context_lens, wk.scale,
+                                                          wk.num_kv_heads, threads=nt), 3)
+            sfx = "" if label == "all" else "_1thread"
+            entry["us_per_call" + sfx] = round(tm * 1e6, 1)
+            entry["GBps" + sfx] = round(nbytes / tm / 1e9, 4)
+        per[name] = entry
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": cpu,
-            "seconds": round(t_total, 2),
-            "us_per_call_equiv": round(1e6 * t_total * w.batch / b_done, 1),
-            "sample": f"{b_done} of {w.batch} sequences of {w.name} ({tok} tokens, all "
-                      f"{w.num_q_heads} query heads), fp64, {threads} threads"}
+    per[w.name] = {"kv_bytes_per_call": kvb, "us_per_call": round(t_med * 1e6, 1),
+                   "GBps": round(kvb / t_med / 1e9, 4)}
+    return {"value": round(kvb / t_med / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": cpu,
+            "seconds": round(t_med, 2), "runs": runs, "us_per_call_equiv": round(1e6 * t_med, 1),
+            "sample": f"the whole {w.name} call ({w.batch} sequences, {int(lens.sum())} tokens, all "
+                      f"{w.num_q_heads} query heads), fp64, {threads} threads, median of {runs}; per_config: "
+                      f"one call of each other workload, all threads and (tiny, single_seq, batch16) one thread, "
+                      f"median of 3",
+            "per_config": per}
+
+
+def advancing_line(pa, torch, workloads_mod, knobs, name="hd256_gqa4", n_calls=64, R=8):
+    """A decode loop: n_calls calls whose lengths advance by one token per
+    call (sequence b at L_b - n_calls + 1 + i in call i, inside the pages the
+    workload already holds), all on one workspace, so the fitted schedule's
+    per-workgroup hint is taken from the previous call as in a real decode.
+    Warm (one pool) and MALL-cold (call i on replica i mod R, R * footprint
+    >= 1 GB); microseconds per call averaged over the loop."""
+    import numpy as np
+    w = workloads_mod.WORKLOADS[name]
+    d = workloads_mod.to_device(workloads_mod.make_inputs(w, seed=0))
+    base = d.layout.context_lens.astype(np.int64)
+    lens = [np.maximum(base - (n_calls - 1) + i, 1).astype(np.int32) for i in range(n_calls)]
+    ctx = [torch.from_numpy(x).cuda() for x in lens]
+    kvb = float(np.mean([workloads_mod.kv_bytes(w, x) for x in lens]))
+    q, k, v = d.call(0)
+    B, Hq, D = q.shape
+    NP, P, Hkv, _ = k.shape
+    opts = pa.make_opts(**knobs)
+    n = pa.pa_decode_workspace_bytes(B, Hq, Hkv, D, d.block_tables.shape[1], P, opts)
+    raw = torch.zeros(n + 256, dtype=torch.uint8, device="cuda")
+    ws = raw[(-raw.data_ptr()) % 256:][:max(n, 1)]
+    out = torch.empty_like(q)
+    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(R - 1)]
+
+    def call(i, pool):
+        kk, vv = pool
+        return lambda: pa.pa_decode_ex(q, kk, vv, d.block_tables, ctx[i], w.scale, Hq, Hkv, D, P, out, None, opts,
+                                       ws if n else None)
+    warm = graph_time_us([call(i, pools[0]) for i in range(n_calls)], 20, torch)
+    cold = graph_time_us([call(i, pools[i % R]) for i in range(n_calls)], 20, torch)
+    _, _, launch = launch_info(pa.pa_get_stats())
+    entry = {"workload": f"{name}, lengths advancing one token per call over {n_calls} calls",
+             "kv_bytes_per_call": round(kvb), "us_per_call": round(warm, 3), "us_per_call_cold": round(cold, 3),
+             "cold_replicas": R, **launch}
+    for key in ("us_per_call", "us_per_call_cold"):
+        gbs = kvb / (entry[key] * 1e-6) / 1e9
+        entry[key.replace("us_per_call", "kv_GBps")] = round(gbs, 1)
+        entry[key.replace("us_per_call", "hbm_frac")] = round(gbs / HBM_PEAK_GBS, 4)
+    log(f"[advancing] {entry}")
+    del d, pools
+    torch.cuda.empty_cache()
+    return entry
 
 
 def copy_probe(mib, torch):
@@ -389,8 +545,9 @@ def main():
     kvb_per_call = wl.kv_bytes(w, d.layout.context_lens)
     n_calls = w.calls
     knobs = dict(variant=args.variant, partition_tokens=args.partition_tokens,
-                 schedule=args.schedule, shares=args.shares)
-    calls = [make_call(pa, d, i, knobs)[0] for i in range(n_calls)]
+                 schedule=args.schedule, shares=args.shares, merge=args.merge)
+    ws = make_workspace(pa, d, knobs)
+    calls = [make_call(pa, d, i, knobs, ws)[0] for i in range(n_calls)]
 
     def step():                       # one pass of the whole path over the batch
         for c in calls:
@@ -401,6 +558,19 @@ def main():
         step()
     torch.cuda.synchronize()
     st = pa.pa_get_stats()
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        step = graph.replay
     ev_s, ev_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -441,6 +611,7 @@ def main():
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
             "calls_per_step": n_calls, "kv_bytes_per_call": kvb_per_call, **launch,
         },
+        "launch_mode": "graph replay" if args.graph else "eager",
         "us_per_call": round(us_per_call_ev, 3),
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {
@@ -456,8 +627,17 @@ def main():
     if args.copy_probe_mib:
         result["copy_probe"] = copy_probe(args.copy_probe_mib, torch)
         log(f"[bench] copy probe: {result['copy_probe']}")
+    probes = None
+    if not args.profile and not args.no_probes:
+        probes = stream_probes(torch, d) if w.head_dim * 2 in (256, 512) else None
+        if probes:
+            result["stream_probe"] = probes
+            result["stream_peak_GBps"] = probes["stream_peak_GBps"]
+            result["stream_frac"] = round(achieved / probes["stream_peak_GBps"], 4)
+            result["nhd_stream_frac"] = round(achieved / probes["nhd_peak_GBps"], 4)
     if not args.profile and not args.no_per_config:
-        result["per_config"] = per_config(pa, knobs, torch, wl)
+        result["per_config"] = per_config(pa, knobs, torch, wl, probes)
+        result["advancing"] = advancing_line(pa, torch, wl, knobs)
         result["append"] = append_line(pa, torch, wl)
         result["prefill"] = prefill_line(pa, torch, wl)
         # several queries per sequence in a decode step (speculative decoding)
