@@ -358,8 +358,11 @@ int pa_check_args(const pa_tensor* q,
  * Sequence b's n_b = query_start[b+1] - query_start[b] queries are its last
  * n_b tokens: query i sits at position pos = L_b - n_b + i and attends to the
  * tokens [0, pos] (with a window W: [max(0, pos - W + 1), pos]).  n_b = 1 is
- * the decode of pa_decode.  Runs on the matrix cores only: head_dim 128 or
- * 256 and a bf16 or fp16 cache (else PA_ENOTSUP), at most 4096 sequences.
+ * the decode of pa_decode.  Runs on the matrix cores only: head_dim 128, 256
+ * or 512 (STAGED: 128 or 256) and a bf16 or fp16 cache (else PA_ENOTSUP), at
+ * most 4096 sequences (at head_dim 512 fewer when the pages are very small:
+ * the per-block kernel keeps a fill of page ids and the sequences' block
+ * counts in LDS beside its merge buffer; PA_ENOTSUP past that).
  * Device-side preconditions, not checked on the host: query_start as above
  * and n_b <= L_b (a query at a negative position gives zeros).  Workspace
  * rules as in pa_decode_ex (workspace NULL = the library's own).

@@ -296,12 +296,16 @@ Plan make_plan(const Geometry& g, const pa_opts* opts) {
     } else if (pl.variant == PA_VARIANT_MFMA) {
         // Few, long partitions: each workgroup's fixed cost (page-table
         // fetch, LDS merge, partial write) is paid per partition, so aim for
-        // about one workgroup per CU of work, partitions of 128..4096 tokens
-        // (measured per call: one 1152-token sequence, 8 KV heads, runs 9.4 us
-        // at 128, 11.2 at 256; four of them 10.5 at 128, 9.9 at 192, 11.0 at
+        // about one workgroup per CU of work, partitions of 64..4096 tokens
+        // (measured per call: one 1152-token sequence, 8 KV heads, runs 7.7 us
+        // at 64, 8.6 at 128; four of them 10.5 at 128, 9.9 at 192, 11.0 at
         // 256; one 4096-token sequence 14.4 at 64, 11.0 at 128, 11.4 at 256).
+        // Partitions of 64 tokens only where they give at least four per
+        // table: a call that would split into two or three (the tiny
+        // batch: 5.1 us unsplit at 128, 6.4 us at 64) stays at 128.
         T = (max_ctx * groups + 255) / 256;
-        T = std::max<int64_t>(128, std::min<int64_t>(T, 4096));
+        T = std::max<int64_t>(64, std::min<int64_t>(T, 4096));
+        if (T <= 64 && (max_ctx + 63) / 64 < 4) T = 128;
     } else {
         // Aim for ~1024 workgroups; partitions of 64..1024 tokens.
         T = (max_ctx * groups + 1023) / 1024;
@@ -778,7 +782,7 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
     if (qg != 1 && qg != 2 && qg != 4 && qg != 8 && qg != 16)
         return fail(PA_ENOTSUP, "Hq/Hkv = %d (supported: 1, 2, 4, 8, 16)", qg);
     if (!pa::prefill_supported(head_dim, k->dtype))
-        return fail(PA_ENOTSUP, "several-query attention needs head_dim 128/256 and a bf16 or fp16 cache");
+        return fail(PA_ENOTSUP, "several-query attention needs head_dim 128/256/512 and a bf16 or fp16 cache");
     if (B > kLeanMaxBatch) return fail(PA_ENOTSUP, "batch %lld > %d", (long long)B, kLeanMaxBatch);
     if (rows > INT32_MAX / 4) return fail(PA_ENOTSUP, "too many query rows");
     if (bt->shape[1] > (int64_t)1 << 24 || (int64_t)bt->shape[1] * page_size > INT32_MAX / 2)
@@ -861,11 +865,16 @@ int prefill_impl(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, con
                               opts, g, rows);
     if (rc) return rc;
     const bool staged_ok = staged_strides_ok(k->stride[0], k->stride[1], g.P) &&
-                           staged_strides_ok(v->stride[0], v->stride[1], g.P);
+                           staged_strides_ok(v->stride[0], v->stride[1], g.P) && pa::prefill_staged_supported(head_dim);
     if (opts && opts->schedule == PA_SCHEDULE_STAGED && !staged_ok)
-        return fail(PA_ENOTSUP, "staged schedule: page stride >= 2^32 or slot stride >= 2^23 elements");
+        return fail(PA_ENOTSUP, "staged schedule: head_dim 128/256, page stride < 2^32 and slot stride < 2^23 "
+                    "elements");
     const PrefillPlan pl = plan_prefill(g, rows, opts, staged_ok);
     if ((int64_t)pl.n_slots * g.Hkv * pl.n_part > INT32_MAX) return fail(PA_ENOTSUP, "grid too large");
+    if (!pl.staged && sizeof(int) * (size_t)(pa::lean_page_slots((int)g.P) + g.B + 1) >
+                          pa::prefill_dynamic_lds_limit((int)g.D))
+        return fail(PA_ENOTSUP, "head_dim %lld: %lld sequences of pages of %lld tokens leave no room in LDS",
+                    (long long)g.D, (long long)g.B, (long long)g.P);
     if (rows == 0 || g.B == 0) return PA_OK;
     int ndev = 0, dev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(PA_ENODEV, "no HIP device");

@@ -23,8 +23,12 @@ bool valu_supported(int head_dim, int qw, int kv_dtype);
 hipError_t launch_mfma(const DecodeParams& p, int head_dim, int kv_dtype, int qw, bool split, hipStream_t s);
 bool mfma_supported(int head_dim, int qw, int kv_dtype);
 bool mfma_lean_supported(int head_dim, int qw, int kv_dtype);
-// Several queries per sequence: head_dim 128 or 256, bf16 or fp16 K/V.
+// Several queries per sequence: head_dim 128, 256 or 512, bf16 or fp16 K/V;
+// the staged kernel at 128 and 256; the per-block kernel's dynamic LDS (page
+// ids and block prefix sums) at most prefill_dynamic_lds_limit bytes.
 bool prefill_supported(int head_dim, int kv_dtype);
+bool prefill_staged_supported(int head_dim);
+size_t prefill_dynamic_lds_limit(int head_dim);
 
 // Matrix-core decode over a balanced schedule (the sequence-major list of
 // (sequence, query block, 16-token tile) cut into one static unit per

@@ -21,7 +21,19 @@
 namespace pa {
 
 bool prefill_supported(int head_dim, int kv_dtype) {
-    return (head_dim == 128 || head_dim == 256) && (kv_dtype == kDtBF16 || kv_dtype == kDtF16);
+    return (head_dim == 128 || head_dim == 256 || head_dim == 512) && (kv_dtype == kDtBF16 || kv_dtype == kDtF16);
+}
+
+// The staged kernel keeps NB stages of K and V in LDS and every wave's
+// accumulators in registers: head_dim 128 and 256.
+bool prefill_staged_supported(int head_dim) { return head_dim == 128 || head_dim == 256; }
+
+// Dynamic LDS (page ids of a fill and the B + 1 block prefix sums) the
+// per-block kernel can take beside its static wave-merge buffer: at head_dim
+// 512 that buffer is 130 KB of the CU's 160 KB.
+size_t prefill_dynamic_lds_limit(int head_dim) {
+    const size_t merge = sizeof(MergeLds<512>) + 64;      // + the prefix scan's own
+    return head_dim == 512 ? (size_t)160 * 1024 - merge : (size_t)64 * 1024;
 }
 
 template <int D, bool SPLIT, bool PAGE16, int NBUF, typename KV>
@@ -497,7 +509,8 @@ static hipError_t launch_staged_d(DecodeParams p, hipStream_t s) {
 }
 
 hipError_t launch_prefill_staged(const DecodeParams& p, int head_dim, int kv_dtype, hipStream_t s) {
-    if (!prefill_supported(head_dim, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
+    if (!prefill_supported(head_dim, kv_dtype) || !prefill_staged_supported(head_dim) || 16 % (p.Hq / p.Hkv))
+        return hipErrorInvalidValue;
     constexpr int NW = kStagedWaves, NB1 = kStagedBuffers128, NB2 = kStagedBuffers256;
     if (kv_dtype == kDtF16)
         return head_dim == 128 ? launch_staged_d<128, NW, NB1, KvF16>(p, s) : launch_staged_d<256, NW, NB2, KvF16>(p, s);
@@ -525,6 +538,10 @@ static hipError_t launch_prefill_d(const DecodeParams& p, bool split, hipStream_
 
 hipError_t launch_prefill(const DecodeParams& p, int head_dim, int kv_dtype, bool split, hipStream_t s) {
     if (!prefill_supported(head_dim, kv_dtype) || 16 % (p.Hq / p.Hkv)) return hipErrorInvalidValue;
+    if (sizeof(int) * (size_t)(p.lean_page_slots + p.B + 1) > prefill_dynamic_lds_limit(head_dim))
+        return hipErrorInvalidValue;
+    if (head_dim == 512)
+        return kv_dtype == kDtF16 ? launch_prefill_d<512, KvF16>(p, split, s) : launch_prefill_d<512, KvBF16>(p, split, s);
     if (kv_dtype == kDtF16)
         return head_dim == 128 ? launch_prefill_d<128, KvF16>(p, split, s) : launch_prefill_d<256, KvF16>(p, split, s);
     return head_dim == 128 ? launch_prefill_d<128, KvBF16>(p, split, s) : launch_prefill_d<256, KvBF16>(p, split, s);

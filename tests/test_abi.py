@@ -307,10 +307,12 @@ def test_workspace_bytes():
     assert small == pa.pa_decode_workspace_bytes(16, 16, 8, 128, 72, 16,
                                                  pa.make_opts("mfma", 0, "partitions"))
     assert small == HDR + rnd(16 * 16 * 2 * 128 * 4) + rnd(16 * 16 * 2 * 4)
-    # one 1152-token sequence: the fixed size is the floor (128 tokens), so
-    # the automatic choice keeps fixed partitions (9 of them)
+    # one 1152-token sequence: the fixed size is the floor (64 tokens), so
+    # the automatic choice keeps fixed partitions (18 of them)
     one = pa.pa_decode_workspace_bytes(1, 16, 8, 128, 72, 16, pa.make_opts("mfma"))
-    assert one == HDR + rnd(16 * 9 * 128 * 4) + rnd(16 * 9 * 4)
+    assert one == HDR + rnd(16 * 18 * 128 * 4) + rnd(16 * 18 * 4)
+    # a 128-token table would split in two at 64 tokens: it stays whole
+    assert pa.pa_decode_workspace_bytes(4, 16, 8, 128, 4, 32, pa.make_opts("mfma")) == 0
     # 32 sequences x 2 query blocks in a 4096-token table (head_dim 256):
     # 4 fixed partitions of 1024 and 268 MB of KV capacity, so the automatic
     # choice fits them; in 2048-token tables (134 MB) it keeps them fixed

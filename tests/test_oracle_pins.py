@@ -406,10 +406,10 @@ def run_queries(c, qs, **kw):
                                     c["context_lens"], qs, c["scale"], c["num_kv_heads"], **kw)
 
 
-@pytest.mark.parametrize("W", [0, 3, 40])
-def test_queries_match_dense_causal_bruteforce(W):
-    rng = np.random.default_rng(110 + W)
-    c, qs = query_case(rng, [1, 9, 40, 33, 17], [1, 9, 5, 33, 0])
+@pytest.mark.parametrize("W,D", [(0, 32), (3, 32), (40, 32), (0, 512), (7, 512)])
+def test_queries_match_dense_causal_bruteforce(W, D):
+    rng = np.random.default_rng(110 + W + D)
+    c, qs = query_case(rng, [1, 9, 40, 33, 17], [1, 9, 5, 33, 0], D=D)
     ref = brute.dense_queries(c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
                               c["context_lens"], qs, c["scale"], c["num_kv_heads"], window=W)
     assert rel_err(run_queries(c, qs, window=W), ref) <= 1e-12

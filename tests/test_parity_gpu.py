@@ -909,6 +909,28 @@ def test_prefill_parity(D, Hq, Hkv, P):
                                   f"(x{s['last_num_partitions']})")
 
 
+@pytest.mark.parametrize("Hq,Hkv,P,kt", [(8, 2, 16, "bf16"), (16, 16, 32, "bf16"), (16, 1, 7, "bf16"),
+                                         (8, 2, 16, "f16")])
+def test_prefill_head_dim_512(Hq, Hkv, P, kt):
+    """Several queries per sequence at head_dim 512 (per-block kernel, split
+    and unsplit, with and without a window; unused slots NaN) against the
+    causal oracle; the staged schedule answers ENOTSUP there."""
+    lens = (1, 17, 40, 300, 1000)
+    chunks = (1, 17, 1, 100, 64)
+    inp, q, qs = queries_case(lens, chunks, Hq, Hkv, 512, P, dtype=kt, seed=512 + Hq + P)
+    d = to_device(inp)
+    for W in (0, 7, 200):
+        ref = oracle_queries(inp, q, qs, window=W)
+        for sched, T in (("partitions", 0), ("partitions", 64), ("auto", 0)):
+            y, s = prefill_run(d, q, qs, window=W, partition_tokens=T, schedule=sched)
+            assert s["last_schedule"] == pa.PA_SCHEDULE_PARTITIONS, s
+            assert_parity(y, ref, f"prefill d512 Hq={Hq} Hkv={Hkv} P={P} {kt} W={W} {sched} T={T} "
+                                  f"(x{s['last_num_partitions']})")
+    with pytest.raises(pa.PaError) as e:
+        prefill_run(d, q, qs, schedule="staged")
+    assert e.value.code == pa.PA_ENOTSUP
+
+
 @pytest.mark.parametrize("kt,qt,ot", [("f16", "f16", "f16"), ("bf16", "f32", "f32"), ("f16", "bf16", "f32")])
 def test_prefill_element_types(kt, qt, ot):
     inp, q, qs = queries_case((64, 900, 33), (64, 40, 1), 16, 4, 128, 16, dtype=kt, q_dtype=qt, seed=5)
