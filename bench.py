@@ -295,6 +295,17 @@ def per_config(pa, knobs, torch, workloads_mod, probes=None):
                     pcalls = [(lambda dd=dd: probe.read_paged(dd, 256, sink)) for dd in descs]
                     entry["probe_us_cold"] = round(graph_time_us(pcalls * max(1, 64 // len(pcalls)), 5, torch), 3)
                 del reps_k
+                if not window and dt != "f32" and kvb >= (64 << 20):
+                    # as many bytes read contiguously (no block table, no page
+                    # scatter), best of 256 / 512 workgroups, same rotation
+                    bufs = [torch.empty(kvb // 16 * 16, dtype=torch.uint8, device="cuda") for _ in range(R)]
+                    best = None
+                    for n_wg in (256, 512):
+                        cc = [(lambda bb=bufs[k % R]: probe.read_contiguous(bb, n_wg, sink)) for k in range(64)]
+                        t = graph_time_us(cc, 5, torch)
+                        best = t if best is None else min(best, t)
+                    entry["contig_probe_us_cold"] = round(best, 3)
+                    del bufs
             if not window and dt != "f32" and w.head_dim <= 256:
                 desc = probe.paged_desc(d.k[0], d.v[0], d.block_tables, d.context_lens)
                 entry["probe_us"] = round(graph_time_us([lambda: probe.read_paged(desc, 256, sink)] * 64, 20,
@@ -309,11 +320,12 @@ def per_config(pa, knobs, torch, workloads_mod, probes=None):
                 entry[key.replace("us_per_call", "hbm_frac")] = round(gbs / HBM_PEAK_GBS, 4)
                 if stream_peak:
                     entry[key.replace("us_per_call", "stream_frac")] = round(gbs / stream_peak, 4)
-        for key in ("probe_us", "probe_us_cold"):
+        for key in ("probe_us", "probe_us_cold", "contig_probe_us_cold"):
             if key in entry:
                 # the probe's time as a fraction of the decode call's: 1.0 = as fast as streaming the bytes
-                call_key = key.replace("probe_us", "us_per_call")
-                entry[key.replace("probe_us", "frac_of_probe")] = round(entry[key] / entry[call_key], 4)
+                call_key = "us_per_call_cold" if key.endswith("_cold") else "us_per_call"
+                entry[key.replace("_us", "").replace("probe", "frac_of_probe")] = round(entry[key] / entry[call_key], 4)
+                entry[key.replace("_us", "_hbm_frac")] = round(kvb / (entry[key] * 1e3) / HBM_PEAK_GBS, 4)
         key = name + (f"_w{window}" if window else "") + (f"_{dt}" if dt != "bf16" else "")
         res[key] = entry
         log(f"[per_config] {key}: {entry}")
