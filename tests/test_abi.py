@@ -436,7 +436,11 @@ def test_prefill_validation():
     ts2, out2, dims2 = prefill_args(kv=torch.float32)
     assert call_prefill(ts2, out2, dims2) == pa.PA_ENOTSUP      # fp32 cache: no MFMA path
     ts3, out3, dims3 = prefill_args(Hq=16, Hkv=16, D=512)
-    assert call_prefill(ts3, out3, dims3) == pa.PA_ENOTSUP
+    if not torch.cuda.is_available():
+        assert call_prefill(ts3, out3, dims3) == pa.PA_ENODEV   # head_dim 512: per-block kernel
+    assert call_prefill(ts3, out3, dims3, pa.make_opts("auto", 0, "staged")) == pa.PA_ENOTSUP
+    ts5, out5, dims5 = prefill_args(D=64)
+    assert call_prefill(ts5, out5, dims5) == pa.PA_ENOTSUP
     assert call_prefill(ts, out, dims, pa.make_opts("valu")) == pa.PA_ENOTSUP
     assert call_prefill(ts, out, dims, pa.make_opts("auto", 0, "balanced")) == pa.PA_ENOTSUP
     assert call_prefill(ts, out, dims, pa.make_opts(window=-2)) == pa.PA_EINVAL
