@@ -191,8 +191,15 @@ __global__ __launch_bounds__(64) void pa_prefill_merge_kernel(DecodeParams p) {
 // The stages arrive by direct global-to-LDS loads (no registers on the way),
 // NB - 1 stages ahead of the one being consumed, into NB rotating buffers.
 // LDS rows are D elements with no padding; the 16-byte chunk c of row r sits
-// at chunk position c ^ (r & 15), so the K reads (16 rows, one chunk each)
-// and the V reads (16 chunks of one row) both spread over all banks.
+// at chunk position c ^ f(r & 15): f moves row bits 0, 1, 2 to bits 3, 2, 1
+// and maps row bit 3 to 3 (0b0011).  Each half-wave of a transposing V read
+// takes 2 chunks of 8 consecutive rows (LDS serves 32 lanes of such a read
+// per cycle from 64 four-byte banks): f sends those rows to 8 distinct
+// values of chunk bits 1..3, so the 16 chunks read are distinct and hit
+// every bank once; a plain XOR with the row would use 8 chunks twice (a
+// 2-way conflict).  The K reads (16 rows, one chunk each) stay conflict-free
+// with this f as with the XOR, where a plain rotation of the row bits would
+// not (both measured with LDS counters).
 template <int D, int NW, int NB>
 struct Staged {
     static constexpr int NT = NW * 64;
@@ -214,7 +221,10 @@ __device__ __forceinline__ u32x2 lds_tr(const uint16_t* p) {
         (lds_s16x4*)(__attribute__((address_space(3))) void*)(p)));
 }
 // Element offset, inside its row, of chunk `chunk` of row `row`.
-__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 15)) << 3; }
+__device__ __forceinline__ int swz_row(int row) {
+    return (((row & 1) << 3) | ((row & 2) << 1) | ((row & 4) >> 1)) ^ (((row >> 3) & 1) * 3);
+}
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ swz_row(row)) << 3; }
 
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and its LDS operations are done, then meet the workgroup.  The
@@ -316,7 +326,7 @@ __device__ __forceinline__ void pair_update(const DecodeParams& p, const uint16_
     // of dim 16t + j: the A operand of output tile t (rows = dims 16t ..
     // 16t + 15), one read per half.  Rows are swizzled like the K reads.
     const int vx = 4 * q + (n >> 2);            // row inside the half (= row & 15)
-    const int vy = ((n >> 1) & 1) ^ vx;
+    const int vy = ((n >> 1) & 1) ^ swz_row(vx);
     const int vrow = vx * D + 4 * (n & 1);
 #pragma unroll
     for (int t = 0; t < NO; ++t) {
@@ -328,12 +338,72 @@ __device__ __forceinline__ void pair_update(const DecodeParams& p, const uint16_
     }
 }
 
+// This wave's share of stage s of the fill starting at token c0: blocks
+// j * NW + wave of K and of V, by direct global-to-LDS loads.  Rows are
+// clamped into [lo_min, te), which lies in this fill's pages.
+template <int D, int NW, int NB>
+__device__ __forceinline__ void staged_issue(const DecodeParams& p, const uint16_t* __restrict__ kb,
+                                             const uint16_t* __restrict__ vb, const int* __restrict__ s_pages,
+                                             uint16_t* __restrict__ kd, uint16_t* __restrict__ vd, int c0, int s,
+                                             int pg0, int lo_min, int te, int wave, int lane) {
+    using C = Staged<D, NW, NB>;
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) {
+        const int cb = j * NW + wave;
+        const int lin = cb * 64 + lane;
+        const int row = lin / C::CPR;
+        const int chunk = (lin % C::CPR) ^ swz_row(row);
+        const int t = clampi(c0 + s * C::ST + row, lo_min, te - 1);
+        int lp, sl;
+        page_slot(p, t, lp, sl);
+        // 32-bit page stride, 24-bit slot stride (the host checks both)
+        const uint32_t page = (uint32_t)s_pages[lp - pg0];
+        const uint64_t ko = (uint64_t)page * (uint32_t)p.k_sp + (uint32_t)(__mul24(sl, (int)p.k_ss) + chunk * 8);
+        const uint64_t vo = (uint64_t)page * (uint32_t)p.v_sp + (uint32_t)(__mul24(sl, (int)p.v_ss) + chunk * 8);
+        __builtin_amdgcn_global_load_lds(kb + ko, kd + cb * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + vo, vd + cb * 512, 16, 0, 0);
+    }
+}
+
+// One stage: issue stage st + NB - 1 into the free buffer (kd, vd) when
+// do_issue, then consume stage st from (kl, vl).  The two buffer pairs are
+// distinct (restrict): the compiler then knows that the stage reads do not
+// depend on the loads just issued and adds no wait for them; the wait for
+// stage st itself is the explicit one before the call.
+template <int D, int NW, int NB, typename KV>
+__device__ __forceinline__ void staged_stage(const DecodeParams& p, const uint16_t* __restrict__ kb,
+                                             const uint16_t* __restrict__ vb, const int* __restrict__ s_pages,
+                                             uint16_t* __restrict__ kd, uint16_t* __restrict__ vd, bool do_issue,
+                                             const uint16_t* __restrict__ kl, const uint16_t* __restrict__ vl,
+                                             int c0, int st, int pg0, int lo_min, int te, int wave, int lane,
+                                             int ntok, const u32x4 (&qop)[D / 32], int n, int q, int free_lo,
+                                             int free_hi, int mask_lo, int mask_hi, bool col_live,
+                                             f32x4 (&o)[D / 16], float& m_run, f32x4& l_acc) {
+    using C = Staged<D, NW, NB>;
+    if (do_issue) staged_issue<D, NW, NB>(p, kb, vb, s_pages, kd, vd, c0, st + NB - 1, pg0, lo_min, te, wave, lane);
+    // A wave with no query (the last workgroup of a sequence, or few queries
+    // per sequence) only loads its share of every stage.
+    if (ntok == 0) return;                                          // wave-uniform
+    const int sb0 = c0 + st * C::ST;
+    constexpr int NPAIR = C::ST / 32;
+    f32x4 sa[NPAIR], sb[NPAIR];
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) pair_logits<D, KV>(kl + 32 * i * D, qop, n, q, sa[i], sb[i]);
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+        const int tb = sb0 + 32 * i;
+        const bool mask = !(tb >= free_lo && tb + 32 <= free_hi);   // wave-uniform
+        pair_update<D, KV>(p, vl + 32 * i * D, sa[i], sb[i], tb, mask, mask_lo, mask_hi, n, q, col_live, o, m_run,
+                           l_acc);
+    }
+}
+
 template <int D, int NW, int NB, typename KV>
 __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams p) {
     using C = Staged<D, NW, NB>;
     constexpr int KK = D / 32;
     constexpr int NO = D / 16;
-    constexpr int NT = C::NT, ST = C::ST, CPR = C::CPR, LPW = C::LPW;
+    constexpr int NT = C::NT, ST = C::ST, LPW = C::LPW;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -430,31 +500,11 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
         fetch_pages<NT>(p, b, pg0, lp1, s_pages, tid);
         __syncthreads();                        // page ids ready; every wave is done with the last chunk
         const int n_st = (c1 - c0 + ST - 1) / ST;
-        // This wave's share of stage s: blocks j * NW + wave of K and of V.
-        // Rows are clamped into [lo_min, te), which lies in this chunk's pages.
-        auto issue = [&](int s) {
-            uint16_t* kd = &s_kv[s % NB][0][0];
-            uint16_t* vd = &s_kv[s % NB][1][0];
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) {
-                const int cb = j * NW + wave;
-                const int lin = cb * 64 + lane;
-                const int row = lin / CPR;
-                const int chunk = (lin % CPR) ^ (row & 15);
-                const int t = clampi(c0 + s * ST + row, lo_min, te - 1);
-                int lp, sl;
-                page_slot(p, t, lp, sl);
-                // 32-bit page stride, 24-bit slot stride (the host checks both)
-                const uint32_t page = (uint32_t)s_pages[lp - pg0];
-                const uint64_t ko = (uint64_t)page * (uint32_t)p.k_sp + (uint32_t)(__mul24(sl, (int)p.k_ss) + chunk * 8);
-                const uint64_t vo = (uint64_t)page * (uint32_t)p.v_sp + (uint32_t)(__mul24(sl, (int)p.v_ss) + chunk * 8);
-                __builtin_amdgcn_global_load_lds(kb + ko, kd + cb * 512, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vb + vo, vd + cb * 512, 16, 0, 0);
-            }
-        };
 #pragma unroll
         for (int s = 0; s < NB - 1; ++s)
-            if (s < n_st) issue(s);
+            if (s < n_st)
+                staged_issue<D, NW, NB>(p, kb, vb, s_pages, &s_kv[s][0][0], &s_kv[s][1][0], c0, s, pg0, lo_min, te,
+                                        wave, lane);
         for (int st = 0; st < n_st; ++st) {
             // Stage st has landed once at most `ahead` later stages are in flight.
             const int ahead = min(NB - 2, n_st - 1 - st);
@@ -462,24 +512,11 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
             else if (NB >= 3 && ahead == 1) vm_wait_barrier<2 * LPW>();
             else vm_wait_barrier<0>();
             // The buffer of stage st - 1 is free: every wave has passed the barrier.
-            if (st + NB - 1 < n_st) issue(st + NB - 1);
-            const uint16_t* kl = &s_kv[st % NB][0][0];
-            const uint16_t* vl = &s_kv[st % NB][1][0];
-            // A wave with no query (the last workgroup of a sequence, or few
-            // queries per sequence) only loads its share of every stage.
-            if (ntok == 0) continue;                                        // wave-uniform
-            const int sb0 = c0 + st * ST;
-            constexpr int NPAIR = ST / 32;
-            f32x4 sa[NPAIR], sb[NPAIR];
-#pragma unroll
-            for (int i = 0; i < NPAIR; ++i) pair_logits<D, KV>(kl + 32 * i * D, qop, n, q, sa[i], sb[i]);
-#pragma unroll
-            for (int i = 0; i < NPAIR; ++i) {
-                const int tb = sb0 + 32 * i;
-                const bool mask = !(tb >= free_lo && tb + 32 <= free_hi);   // wave-uniform
-                pair_update<D, KV>(p, vl + 32 * i * D, sa[i], sb[i], tb, mask, mask_lo, mask_hi, n, q, col_live, o,
-                                   m_run, l_acc);
-            }
+            const int nx = (st + NB - 1) % NB, cu = st % NB;
+            staged_stage<D, NW, NB, KV>(p, kb, vb, s_pages, &s_kv[nx][0][0], &s_kv[nx][1][0], st + NB - 1 < n_st,
+                                        &s_kv[cu][0][0], &s_kv[cu][1][0], c0, st, pg0, lo_min, te, wave, lane,
+                                        ntok, qop, n, q, free_lo, free_hi, mask_lo, mask_hi, col_live, o, m_run,
+                                        l_acc);
         }
         __syncthreads();                        // every wave is done reading the stage buffers and page ids
     }
