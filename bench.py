@@ -37,14 +37,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# The sources compiled into the matrix-core decode kernels (the kernels whose
+# HBM traffic the profiles record); their launch geometry is compared apart.
+DECODE_KERNEL_SOURCES = ["pa_mfma.hip", "pa_mfma_core.h", "pa_device.h", "pa_launch.h"]
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources and build script; a profile's HBM
-    traffic is only reported while the kernels still hash to it."""
+    """sha256 over the decode kernels' sources and the build script; a
+    profile's HBM traffic is only reported while the kernels still hash to
+    it."""
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "paged_attention_decode_04_amd")
-    files = sorted(os.listdir(os.path.join(pkg, "csrc")))
-    for f in files:
+    for f in DECODE_KERNEL_SOURCES:
         h.update(f.encode())
         h.update(open(os.path.join(pkg, "csrc", f), "rb").read())
     h.update(open(os.path.join(pkg, "build.py"), "rb").read())

@@ -805,7 +805,7 @@ int validate_prefill(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
 // The staged kernel addresses the pool with a 32-bit page stride and a
 // 24-bit slot stride (P slots of at most 2^31 elements).
 bool staged_strides_ok(int64_t sp, int64_t ss, int64_t P) {
-    return sp >= 0 && sp < ((int64_t)1 << 32) && ss >= 0 && ss < ((int64_t)1 << 23) && P * ss < ((int64_t)1 << 31);
+    return sp >= 0 && sp < ((int64_t)1 << 32) && ss >= 0 && ss < ((int64_t)1 << 23) && P * ss + 512 <= ((int64_t)1 << 31);
 }
 
 PrefillPlan plan_prefill(const Geometry& g, int64_t rows, const pa_opts* opts, bool staged_ok = true) {
