@@ -93,6 +93,9 @@ def parse():
     ap.add_argument("--profile-prefill", action="store_true",
                     help="only the several-query (chunked-prefill) line, printed as the JSON line: "
                          "for rocprofv3 runs over its kernel")
+    ap.add_argument("--timeline", metavar="WORKLOAD", default=None,
+                    help="per-workgroup phase timeline (pa_trace_set) of one call of WORKLOAD on the "
+                         "partitioned MFMA decode, warm and MALL-cold, printed as a markdown summary")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a plain device copy of this many MiB (HBM reference and the "
                          "calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -407,6 +410,101 @@ def prefill_line(pa, torch, workloads_mod, B=8, ctx=4096, chunk=512, Hq=32, Hkv=
     return entry
 
 
+def _pct(a, q):
+    import numpy as np
+    return float(np.percentile(a, q)) if len(a) else float("nan")
+
+
+def timeline_summary(rec, khz, lens, D, elem):
+    """Phase statistics of one call's timeline records (PA_TRACE_WORDS uint64
+    per workgroup) in microseconds from the first workgroup's entry."""
+    import numpy as np
+    rec = rec[rec[:, 4] != 0]
+    flags = (rec[:, 7] >> np.uint64(32)).astype(np.int64)
+    T = (rec[:, 7] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+    t = rec[:, :5].astype(np.int64)
+    us = 1e3 / khz                                        # microseconds per tick
+    t0 = t[:, 0].min()
+    run = flags != 1
+    tr = (t[run] - t0) * us
+    b = (rec[run, 6] & np.uint64(0xFFFF)).astype(np.int64)
+    part = (rec[run, 6] >> np.uint64(32)).astype(np.int64)
+    Tr = T[run]
+    L = np.asarray(lens, dtype=np.int64)[b]
+    tokens = np.clip(L - part * Tr, 0, Tr)
+    stream_us = tr[:, 2] - tr[:, 1]
+    gbs = tokens * D * elem * 2 / np.maximum(stream_us, 1e-3) / 1e3    # K and V rows of one KV head
+    where = rec[:, 5]
+    xcc = (where >> np.uint64(32)).astype(np.int64)
+    cu = ((where >> np.uint64(8)) & np.uint64(0xFF)).astype(np.int64)
+    per_cu = {}
+    for x, c in zip(xcc.tolist(), cu.tolist()):
+        per_cu[(x, c)] = per_cu.get((x, c), 0) + 1
+    out = {
+        "workgroups": int(len(rec)), "ran_partition": int(run.sum()),
+        "partition_tokens": int(Tr[0]) if len(Tr) else 0,
+        "merged_in_kernel": int((flags == 2).sum()),
+        "cus_used": len(per_cu), "max_wgs_per_cu": max(per_cu.values()) if per_cu else 0,
+        "decode_span_us": round(float((t[:, 4].max() - t0) * us), 3),
+    }
+    def stat(name, v):
+        out[name] = {"min": round(float(v.min()), 3), "p50": round(_pct(v, 50), 3), "p90": round(_pct(v, 90), 3),
+                     "max": round(float(v.max()), 3)}
+    stat("entry_us", (t[:, 0] - t0) * us)
+    stat("prologue_us", tr[:, 1] - tr[:, 0])
+    stat("streaming_us", stream_us)
+    stat("stream_end_us", tr[:, 2])
+    stat("wave_merge_us", tr[:, 3] - tr[:, 2])
+    stat("exit_us", tr[:, 4])
+    stat("stream_GBps_per_wg", gbs)
+    if (flags == 2).any():
+        stat("kernel_merge_us", (t[flags == 2, 4] - t[flags == 2, 3]) * us)
+    last = {}
+    for x, e in zip(xcc.tolist(), ((t[:, 4] - t0) * us).tolist()):
+        last[x] = max(last.get(x, 0.0), e)
+    out["exit_by_xcd_us"] = {str(k): round(v, 3) for k, v in sorted(last.items())}
+    return out
+
+
+def timeline_line(pa, torch, workloads_mod, name, knobs):
+    """One traced call of `name` (warm and on the MALL-cold replica rotation)
+    with the per-phase statistics of its workgroups, and the untraced call
+    time of the same graphs for comparison."""
+    import numpy as np
+    w = workloads_mod.WORKLOADS[name]
+    d = workloads_mod.to_device(workloads_mod.make_inputs(w, seed=0))
+    lens = d.layout.context_lens
+    kvb = workloads_mod.kv_bytes(w, lens)
+    khz = pa.pa_trace_clock_khz()
+    ws = make_workspace(pa, d, knobs)
+    call = make_call(pa, d, 0, knobs, ws)[0]
+    R = min(int(np.ceil(1.0e9 / max(kvb, 1))), 64)
+    reps_k = [workloads_mod.DeviceInputs(w, d.q, d.k.clone(), d.v.clone(), d.block_tables, d.context_lens, d.layout)
+              for _ in range(R)]
+    cold = [make_call(pa, reps_k[k % R], 0, knobs, ws)[0] for k in range(max(64, R))]
+    res = {"workload": name, "kv_bytes_per_call": kvb, "clock_khz": khz, "cold_replicas": R}
+    res["warm_us_untraced"] = round(graph_time_us([call] * 64, 20, torch), 3)
+    res["cold_us_untraced"] = round(graph_time_us(cold, 5, torch), 3)
+    buf = torch.zeros(16384 * pa.PA_TRACE_WORDS, dtype=torch.int64, device="cuda")
+    pa.pa_trace_set(buf)
+    try:
+        res["warm_us_traced"] = round(graph_time_us([call] * 64, 20, torch), 3)
+        torch.cuda.synchronize()
+        rec_w = buf.view(-1, pa.PA_TRACE_WORDS).cpu().numpy().astype(np.uint64)
+        buf.zero_()
+        res["cold_us_traced"] = round(graph_time_us(cold, 5, torch), 3)
+        torch.cuda.synchronize()
+        rec_c = buf.view(-1, pa.PA_TRACE_WORDS).cpu().numpy().astype(np.uint64)
+    finally:
+        pa.pa_trace_set(None)
+    kernel, _, launch = launch_info(pa.pa_get_stats())
+    res["kernel"] = kernel
+    res["launch"] = launch
+    res["warm"] = timeline_summary(rec_w, khz, lens, w.head_dim, 2)
+    res["cold"] = timeline_summary(rec_c, khz, lens, w.head_dim, 2)
+    return res
+
+
 def _median_time(fn, runs):
     ts = []
     for _ in range(runs):
@@ -550,6 +648,11 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_prefill:
         print(json.dumps(prefill_line(pa, torch, wl)), flush=True)
+        return
+    if args.timeline:
+        knobs = dict(variant=args.variant, partition_tokens=args.partition_tokens,
+                     schedule=args.schedule, shares=args.shares, merge=args.merge)
+        print(json.dumps(timeline_line(pa, torch, wl, args.timeline, knobs)), flush=True)
         return
     w = wl.WORKLOADS[args.workload]
     t_gen = time.perf_counter()

@@ -414,6 +414,27 @@ typedef struct pa_stats {
 int  pa_get_stats(pa_stats* stats);   /* PA_EINVAL if stats is NULL            */
 void pa_reset_stats(void);
 
+/* Per-workgroup timeline of the matrix-core decode on fixed or fitted
+ * partitions (a measurement aid, for instance to see start-up, streaming,
+ * wave merge and in-kernel merge per CU).  While a buffer is set, every
+ * launch of that kernel writes PA_TRACE_WORDS uint64 per workgroup for the
+ * first bytes / (8 * PA_TRACE_WORDS) workgroups: [0] entry, [1] prologue done
+ * (lengths, page ids, Q), [2] wave 0's streaming done, [3] wave merge and
+ * stores done, [4] exit, in s_memrealtime ticks (pa_trace_clock_khz; [1]..[3] are 0 for
+ * a workgroup with no partition to run); [5] HW_ID | XCC_ID << 32; [6]
+ * sequence | query block << 16 | partition << 32; [7] partition tokens |
+ * flags << 32 (1: no partition to run, 2: merged its group in the kernel).
+ * Each launch overwrites the records; graphs captured while a buffer is set
+ * keep writing to it.  buf: device memory owned by the caller, 16-byte
+ * aligned; NULL (or bytes < 64) stops tracing.  Process-wide, like the
+ * counters.  Returns PA_OK, or PA_EINVAL for a misaligned buffer. */
+#define PA_TRACE_WORDS 8
+int  pa_trace_set(void* buf, size_t bytes);
+/* Frequency of the records' clock on the current device, in kHz (the HIP
+ * wall-clock rate).  PA_EINVAL if khz is NULL, PA_ENODEV / PA_EHIP if the
+ * runtime cannot tell. */
+int  pa_trace_clock_khz(int* khz);
+
 /* Static text for an error code; never NULL. */
 const char* pa_strerror(int code);
 

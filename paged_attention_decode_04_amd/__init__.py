@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     PaError, PaOpts, PaStats, PaTensor, cache_append, decode, last_error, make_opts, pa_cache_append,
     pa_check_args, pa_decode, pa_decode_noalloc, pa_prefill, release_workspaces, pa_prefill_workspace_bytes, prefill,
     pa_decode_ex, pa_decode_workspace_bytes, pa_get_stats, pa_release, pa_reset_stats, strerror,
+    PA_TRACE_WORDS, pa_trace_clock_khz, pa_trace_set,
     tensor_desc, version,
 )
 

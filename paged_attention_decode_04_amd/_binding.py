@@ -81,6 +81,10 @@ def _load() -> ctypes.CDLL:
     lib.pa_get_stats.restype = ctypes.c_int
     lib.pa_reset_stats.argtypes = []
     lib.pa_reset_stats.restype = None
+    lib.pa_trace_set.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.pa_trace_set.restype = ctypes.c_int
+    lib.pa_trace_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    lib.pa_trace_clock_khz.restype = ctypes.c_int
     lib.pa_strerror.argtypes = [ctypes.c_int]
     lib.pa_strerror.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
@@ -370,6 +374,27 @@ def pa_get_stats() -> dict:
 
 def pa_reset_stats() -> None:
     LIB.pa_reset_stats()
+
+
+PA_TRACE_WORDS = 8
+
+
+def pa_trace_set(buf) -> None:
+    """Per-workgroup timeline records of the partitioned MFMA decode into the
+    contiguous device tensor ``buf`` (PA_TRACE_WORDS uint64 per workgroup),
+    or stop with ``None``.  A measurement aid; see ``pa_trace_set`` in the
+    header for the record layout."""
+    if buf is None:
+        _check(LIB.pa_trace_set(None, 0), "pa_trace_set")
+    else:
+        _check(LIB.pa_trace_set(buf.data_ptr(), buf.numel() * buf.element_size()), "pa_trace_set")
+
+
+def pa_trace_clock_khz() -> int:
+    """Frequency of the timeline records' clock on the current device (kHz)."""
+    v = ctypes.c_int(0)
+    _check(LIB.pa_trace_clock_khz(ctypes.byref(v)), "pa_trace_clock_khz")
+    return int(v.value)
 
 
 def pa_release() -> None:

@@ -42,6 +42,10 @@ struct Counters {
     std::atomic<uint64_t> last_t{0}, last_np{0}, last_variant{0}, last_schedule{0};
 } g_stats;
 
+// Timeline buffer of the partitioned MFMA decode (pa_trace_set), or null.
+std::atomic<uint64_t*> g_trace{nullptr};
+std::atomic<int> g_trace_wgs{0};
+
 // Validated call geometry.
 struct Geometry {
     int64_t B, Hq, Hkv, D, P, NP, max_blk;
@@ -526,6 +530,8 @@ int launch(const pa_tensor* q, const pa_tensor* k, const pa_tensor* v, const pa_
         p.n_wg = (int)std::max<int64_t>(pl.fit_grid, p.fit_target);
     }
     if (pl.fuse) p.fuse_ctr = reinterpret_cast<int*>(static_cast<char*>(ws) + pa::kFuseCounterOffset);
+    p.trace = g_trace.load();
+    p.trace_wgs = p.trace ? g_trace_wgs.load() : 0;
     if (pl.variant == PA_VARIANT_MFMA) {
         e = pa::launch_mfma(p, (int)g.D, g.kv_dtype, pl.qw, pl.split, s);
         if (e != hipSuccess) return fail(PA_EHIP, "decode (mfma) launch: %s", hipGetErrorString(e));
@@ -1094,6 +1100,27 @@ int pa_get_stats(pa_stats* s) {
     s->prefill_launches = g_stats.prefill;
     s->last_schedule = g_stats.last_schedule;
     s->fused_calls = g_stats.fused;
+    return PA_OK;
+}
+
+int pa_trace_set(void* buf, size_t bytes) {
+    static_assert(PA_TRACE_WORDS == pa::kTraceWords, "trace record size");
+    if (buf && (reinterpret_cast<uintptr_t>(buf) & 15u))
+        return fail(PA_EINVAL, "pa_trace_set: the buffer must be 16-byte aligned");
+    const size_t rec = sizeof(uint64_t) * PA_TRACE_WORDS;
+    const size_t wgs = buf ? std::min<size_t>(bytes / rec, INT32_MAX) : 0;
+    g_trace_wgs = (int)wgs;
+    g_trace = wgs ? static_cast<uint64_t*>(buf) : nullptr;
+    return PA_OK;
+}
+
+int pa_trace_clock_khz(int* khz) {
+    if (!khz) return fail(PA_EINVAL, "pa_trace_clock_khz: khz is NULL");
+    int dev = 0, n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n < 1) return fail(PA_ENODEV, "no HIP device");
+    if (hipGetDevice(&dev) != hipSuccess) return fail(PA_EHIP, "hipGetDevice failed");
+    const hipError_t e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return fail(PA_EHIP, "hipDeviceGetAttribute(WallClockRate): %s", hipGetErrorString(e));
     return PA_OK;
 }
 

@@ -46,7 +46,38 @@ struct DecodeParams {
                                                             // arrival counter per (sequence, query block),
                                                             // zero between calls; null = separate merge kernel
     float scale_log2;                                       // scale * log2(e)
+    uint64_t* trace;                                        // measurement: kTraceWords stamps per workgroup
+                                                            // of the partitioned MFMA decode, or null
+    int   trace_wgs;                                        // workgroups the trace buffer holds
 };
+
+// Workgroup barrier that orders LDS only.  The plain barrier's release fence
+// waits for every vector memory operation in flight (loads included); this one
+// waits for the wave's LDS operations alone, so global loads issued before it
+// (Q rows, the next tile) stay in flight across it.  For exchanges through LDS
+// only: global memory written before it is not made visible to the workgroup.
+// s_waitcnt operand that waits for every vector memory operation of the wave
+// (vmcnt 0) and for nothing else (expcnt 7, lgkmcnt 15: their maxima).
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Per-workgroup timeline record of the partitioned matrix-core decode (a
+// measurement aid): [0] entry, [1] prologue done (lengths, page ids, Q), [2]
+// wave 0's streaming done, [3] wave merge and stores done, [4] exit, in
+// s_memrealtime ticks (the device's wall-clock rate); [5] HW_ID | XCC_ID << 32; [6] sequence |
+// query block << 16 | partition << 32; [7] partition tokens | flags << 32
+// (flag 1: no partition to run, 2: merged its group in the kernel).
+constexpr int kTraceWords = 8;
+__device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint64_t trace_where() {
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);     // HW_REG_HW_ID, 32 bits
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // HW_REG_XCC_ID, 32 bits
+    return (uint64_t)hw | ((uint64_t)xcc << 32);
+}
 
 // KV-cache append: newest token of each sequence into its page slot.  Byte
 // pointers and byte strides: the copy does not depend on the element type.

@@ -83,8 +83,17 @@ __device__ __forceinline__ void fit_lengths(const DecodeParams& p, int (&len)[kF
     }
 }
 
-__device__ __forceinline__ bool fit_locate(const DecodeParams& p, int x, int (&len)[kFitChunks], int& b, int& qb,
-                                           int& part, int& T, int& L) {
+// The (sequence, query block, partition) triple of fitted-partition
+// workgroup x and the partition size T, from the lengths of the batch: the
+// smallest multiple of 64 in [fit_lo, part_tokens] that gives at most
+// fit_target triples (else part_tokens), with the triples of partition j of
+// all sequences ahead of those of partition j + 1.  When `hinted`, b, qb, part
+// and T hold the previous call's answer on entry (decode lengths grow by one
+// token per call, so it seldom changes): one round of three independent
+// reductions confirms it, and only a miss runs the searches.  Returns false
+// past the last triple (T is set either way).
+__device__ __forceinline__ bool fit_locate(const DecodeParams& p, int x, int (&len)[kFitChunks], bool hinted, int& b,
+                                           int& qb, int& part, int& T, int& L) {
     constexpr int NC = kFitChunks;
     const int lane = threadIdx.x & 63;
     const int n_qb = p.Hq / p.qw;
@@ -93,63 +102,109 @@ __device__ __forceinline__ bool fit_locate(const DecodeParams& p, int x, int (&l
 #pragma unroll
     for (int c = 0; c < NC; ++c) len[c] = clampi(len[c], 0, cap);
     // ceil(len / t) for 0 <= len < 2^24 (the host bounds the block tables
-    // so), 64 <= t: a float estimate off by at most one, made exact by two
-    // integer corrections
+    // so), 64 <= t: len times the hardware reciprocal of t (relative error
+    // near 2^-22, so under 0.1 on a quotient below 2^18) is off by at most
+    // one after truncation, made exact by two integer corrections
     auto ceil_div = [](int len, int t, float rcp) {
         int d = (int)((float)len * rcp);
         d -= d * t > len ? 1 : 0;
         d += (d + 1) * t <= len ? 1 : 0;        // d = floor(len / t)
         return d + (d * t < len ? 1 : 0);
     };
-    auto count = [&](int t) {
-        const float rcp = 1.f / (float)t;
+    // wave-wide total times n_qb: uniform by construction; saying so keeps
+    // the searches on scalar branches, so every reduction runs with the whole
+    // wave active
+    auto total = [&](int s) { return __builtin_amdgcn_readfirstlane(wave_sum_i(s) * n_qb); };
+    auto count = [&](int t) {                   // triples with partitions of t tokens
+        const float rcp = __builtin_amdgcn_rcpf((float)t);
         int s = 0;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             if (c < nc) s += ceil_div(len[c], t, rcp);
-        // uniform by construction; saying so keeps the search on scalar
-        // branches, so every reduction runs with the whole wave active
-        return __builtin_amdgcn_readfirstlane(wave_sum_i(s) * n_qb);
+        return total(s);
     };
-    int lo = p.fit_lo >> 6, hi = p.part_tokens >> 6;   // sizes in units of 64 tokens
-    // The count only falls as the size grows: when one step below the
-    // largest size is already too many partitions, the largest is the answer
-    // (the common case for batches of even lengths: one probe, no search).
-    if (lo < hi && count((hi - 1) << 6) > p.fit_target) lo = hi;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (count(mid << 6) <= p.fit_target) hi = mid; else lo = mid + 1;
-    }
-    T = __builtin_amdgcn_readfirstlane(lo << 6);
-    if (x == 0 && threadIdx.x == 0) *p.fit_part = T;
-    // n_b partitions per sequence; before(j) = n_qb * sum_b min(n_b, j) live
-    // triples precede partition index j
+    const int lo0 = p.fit_lo >> 6, hi0 = p.part_tokens >> 6;   // sizes in units of 64 tokens
+    // n_b partitions per sequence at size T; before(j) = n_qb * sum_b min(n_b, j)
+    // live triples precede partition index j
     int nb[NC];
-    int top = 0, tot = 0;
-    const float rcp = 1.f / (float)T;
+    int n_all = -1;                             // count(T) once T is known
+    int n_before = -1;                          // before(part) of the hinted part, when T is the hinted size
+    if (hinted) {
+        // The count only falls as the size grows, so the hinted size is the
+        // answer exactly when it gives few enough triples (or is the largest
+        // size) and one step below gives too many (or it is the smallest).
+        const int th = T >> 6, tl = max(th - 1, 1);
+        const float r_at = __builtin_amdgcn_rcpf((float)(th << 6)), r_bl = __builtin_amdgcn_rcpf((float)(tl << 6));
+        int s_at = 0, s_bl = 0, s_bp = 0;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        nb[c] = c < nc ? ceil_div(len[c], T, rcp) : 0;
-        top = max(top, nb[c]);
-        tot += nb[c];
+        for (int c = 0; c < NC; ++c) {
+            nb[c] = 0;
+            if (c < nc) {
+                nb[c] = ceil_div(len[c], th << 6, r_at);
+                s_at += nb[c];
+                s_bl += ceil_div(len[c], tl << 6, r_bl);
+                s_bp += min(nb[c], part);
+            }
+        }
+        const int c_at = total(s_at), c_bl = total(s_bl), bp = total(s_bp);
+        if ((th == hi0 || c_at <= p.fit_target) && (th == lo0 || c_bl > p.fit_target)) {
+            n_all = c_at;
+            n_before = bp;
+        }
     }
-    if (x >= __builtin_amdgcn_readfirstlane(wave_sum_i(tot) * n_qb)) return false;   // past the last live triple
-    top = __builtin_amdgcn_readfirstlane(wave_max_i(top));
+    if (n_all < 0) {
+        int lo = lo0, hi = hi0;
+        // When one step below the largest size is already too many triples,
+        // the largest is the answer (the common case for batches of even
+        // lengths: one probe, no search).
+        if (lo < hi && count((hi - 1) << 6) > p.fit_target) lo = hi;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (count(mid << 6) <= p.fit_target) hi = mid; else lo = mid + 1;
+        }
+        T = __builtin_amdgcn_readfirstlane(lo << 6);
+        const float rcp = __builtin_amdgcn_rcpf((float)T);
+        int tot = 0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            nb[c] = c < nc ? ceil_div(len[c], T, rcp) : 0;
+            tot += nb[c];
+        }
+        n_all = total(tot);
+    }
+    if (x >= n_all) return false;               // past the last live triple
     auto before = [&](int j) {
         int s = 0;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             if (c < nc) s += min(nb[c], j);
-        return __builtin_amdgcn_readfirstlane(wave_sum_i(s) * n_qb);
+        return total(s);
     };
-    // partition index: the largest j < top with before(j) <= x
-    int a = 0, z = top - 1;
-    while (a < z) {
-        const int mid = (a + z + 1) >> 1;
-        if (before(mid) <= x) a = mid; else z = mid - 1;
+    // partition index: the largest j with before(j) <= x.  The hinted part is
+    // it when before(part) <= x < before(part + 1), the step between the two
+    // being n_qb times the sequences with more than part partitions.
+    int bx = -1;                                // before(part)
+    if (n_before >= 0 && n_before <= x) {
+        int more = 0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (c < nc) more += __builtin_popcountll(__ballot(nb[c] > part));
+        if (x < n_before + n_qb * more) bx = n_before;
     }
-    part = a;
-    const int y = x - before(part);
+    if (bx < 0) {
+        int top = 0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) top = max(top, nb[c]);
+        top = __builtin_amdgcn_readfirstlane(wave_max_i(top));
+        int a = 0, z = top - 1;
+        while (a < z) {
+            const int mid = (a + z + 1) >> 1;
+            if (before(mid) <= x) a = mid; else z = mid - 1;
+        }
+        part = a;
+        bx = before(part);
+    }
+    const int y = x - bx;
     qb = y % n_qb;
     int k = y / n_qb;                           // the k-th sequence (from 0) with n_b > part
 #pragma unroll
@@ -180,13 +235,21 @@ template <int D, bool SPLIT, bool PAGE16, bool HALF, int NBUF, typename KV>
 __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p) {
     constexpr int KK = TileFrag<D>::KK;
     constexpr int NO = D / 16;                  // O^T accumulator tiles
+    const bool tracing = p.trace && (int)blockIdx.x < p.trace_wgs;   // measurement only
+    uint64_t tr[4] = {tracing ? trace_clock() : 0, 0, 0, 0};
     const int qw = p.qw;                        // query heads of this workgroup (<= 16)
     const int n_qb = p.Hq / qw;
     int qb = blockIdx.x % n_qb;
     int b = (blockIdx.x / n_qb) % p.B;
     int part = blockIdx.x / n_qb / p.B;
     int T = p.part_tokens;                      // tokens per partition
+    const int wave0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    // Fitted partitions: wave 0 reads all lengths (to locate this workgroup's
+    // triple) before the hint, so both reads are in flight together.
+    int len[kFitChunks];
+    bool hinted = false;                        // b, qb, part, T come from a valid hint
     if (p.fit_part) {
+        if (wave0 == 0) fit_lengths(p, len);
         // Fitted partitions: start from the triple this workgroup took in the
         // previous call when it is a valid one (decode lengths grow by a token
         // per step, so the plan seldom changes); else the fixed-grid slot.
@@ -199,12 +262,40 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
             qb = hq;
             part = hp;
             T = ht;
+            hinted = true;
         }
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wave = wave0;                     // wave-uniform
     const int n = lane & 15, q = lane >> 4;
+    auto trace_out = [&](uint32_t flags) {
+        if (tracing && tid == 0) {
+            uint64_t* r = p.trace + (int64_t)blockIdx.x * kTraceWords;
+            r[0] = tr[0];
+            r[1] = tr[1];
+            r[2] = tr[2];
+            r[3] = tr[3];
+            r[4] = trace_clock();
+            r[5] = trace_where();
+            r[6] = (uint64_t)(uint32_t)b | ((uint64_t)(uint32_t)qb << 16) | ((uint64_t)(uint32_t)part << 32);
+            r[7] = (uint64_t)(uint32_t)T | ((uint64_t)flags << 32);
+        }
+    };
+
+    // Fitted partitions: the next call's hint (this workgroup's triple, or an
+    // invalid one when it has none) and, from workgroup 0, the size chosen
+    // (read by the merge kernel).  Stored once the workgroup has passed its
+    // last barrier before streaming: a barrier waits for the workgroup's
+    // outstanding stores, and nothing in this call reads them.
+    __shared__ int s_fit[6];                    // b, qb, part, T, L, state
+    auto fit_record = [&](bool none) {
+        if (p.fit_part && tid == 0) {
+            *reinterpret_cast<int4*>(p.fit_hint + 4 * (int64_t)blockIdx.x) =
+                none ? make_int4(-1, -1, -1, -1) : make_int4(s_fit[0], s_fit[1], s_fit[2], s_fit[3]);
+            if (blockIdx.x == 0) *p.fit_part = s_fit[3];
+        }
+    };
 
     // Page ids of the partition's token range are fetched without waiting for
     // the sequence length (entries past the sequence's end are never used),
@@ -218,33 +309,35 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     }
     extern __shared__ int s_pages[];
     u32x4 qop[KK];
-    int len[kFitChunks];
-    if (p.fit_part && wave == 0) fit_lengths(p, len);
     int ts, pg0;
+    // With fitted partitions wave 0 locates the triple while the page ids are
+    // read, so the page-id loop starts at wave 1 (wave 0 takes entries only
+    // past the other three waves' share).
+    const int ftid = p.fit_part ? (tid + kMBlock - 64) % kMBlock : tid;
     auto fetch = [&]() {
         ts = t_base + part * T;
         int lp_hi, unused;
         page_slot(p, ts, pg0, unused);
         page_slot(p, ts + T - 1, lp_hi, unused);
-        fetch_pages(p, b, pg0, lp_hi, s_pages, tid);
-        // Q does not depend on the length either: its load goes out with the
-        // others (a partition past the end drops it).
+        // Q does not depend on the length either: its loads go out first, so
+        // they are in flight while the page ids are read and written to LDS
+        // (a partition past the end drops them).
         load_q<D, HALF, KV>(p, b, qb * qw, qw, n, q, qop);
+        fetch_pages(p, b, pg0, lp_hi, s_pages, ftid);
     };
     fetch();
     if (p.fit_part) {
-        // Fitted partitions (never with a window).  The fetch above took the
+        // Fitted partitions (never with a window).  The fetch takes the
         // hinted triple or the fixed-partition slot; when that is the triple
         // this workgroup is given, nothing is fetched again, else the fetch
-        // is made again (each thread
-        // rewrites the page-id entries it wrote, so no barrier is needed
-        // before the one that precedes their use).  Wave 0 alone reads the
-        // lengths and locates the triple (one read of the lengths per
-        // workgroup); the others take it from LDS.
-        __shared__ int s_fit[6];                // b, qb, part, T, L, state
+        // is made again (each thread rewrites the page-id entries it wrote,
+        // so no barrier is needed before the one that precedes their use).
+        // Wave 0 alone reads the lengths and locates the triple (one read of
+        // the lengths per workgroup) while its Q reads are in flight; the
+        // others take the triple from LDS.
         if (wave == 0) {
-            int fb = 0, fqb = 0, fpart = 0, fT = T, fL = 0;
-            const bool live = fit_locate(p, (int)blockIdx.x, len, fb, fqb, fpart, fT, fL);
+            int fb = b, fqb = qb, fpart = part, fT = T, fL = 0;
+            const bool live = fit_locate(p, (int)blockIdx.x, len, hinted, fb, fqb, fpart, fT, fL);
             if (p.fuse_ctr && blockIdx.x == 0) {
                 // Merged in this kernel, a sequence with no tokens has no
                 // partition and no merge to write its zero rows: this wave
@@ -270,14 +363,15 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
                 s_fit[4] = fL;
                 // 0: past the last triple, 1: the slot fetched, 2: another one
                 s_fit[5] = !live ? 0 : (fb == b && fqb == qb && fpart == part && fT == T) ? 1 : 2;
-                // the next call's hint (no triple: an invalid one)
-                *reinterpret_cast<int4*>(p.fit_hint + 4 * (int64_t)blockIdx.x) =
-                    live ? make_int4(fb, fqb, fpart, fT) : make_int4(-1, -1, -1, -1);
             }
         }
-        __syncthreads();
+        lds_barrier();
         const int state = __builtin_amdgcn_readfirstlane(s_fit[5]);
-        if (state == 0) return;                 // the whole workgroup
+        if (state == 0) {                       // the whole workgroup
+            fit_record(true);
+            trace_out(1);
+            return;
+        }
         L = __builtin_amdgcn_readfirstlane(s_fit[4]);
         if (state == 2) {
             b = __builtin_amdgcn_readfirstlane(s_fit[0]);
@@ -289,7 +383,11 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     } else if (p.window <= 0) {
         L = clampi(p.ctx[b], 0, p.max_blk * p.P);
     }
-    if (ts >= L && part > 0) return;
+    if (ts >= L && part > 0) {
+        fit_record(false);
+        trace_out(1);
+        return;
+    }
     const int h0 = qb * qw;
     const int g = h0 / (p.Hq / p.Hkv);
     const int te = min(L, ts + T);
@@ -300,7 +398,12 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     // the last of them to arrive merges them.
     const int n_used = SPLIT && p.fuse_ctr ? max(1, (L - t_base + T - 1) / T) : 0;
     const bool direct = !SPLIT || n_used == 1;
-    __syncthreads();
+    lds_barrier();
+    // Q has been in flight since the fetch (the barriers above order LDS
+    // only); waiting for it here, once, keeps the wait out of the tile loop.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (tracing) tr[1] = trace_clock();
+    fit_record(false);
 
     f32x4 o[NO];
 #pragma unroll
@@ -313,6 +416,7 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
     run_tiles<D, PAGE16, HALF, NBUF, KV>(p, s_pages, pg0, g, n, q, wave, lo, qop, col_live, ts, te, t_begin,
                                          t_begin, te, o, m_run, l_run);
     l_run = xsum32(xsum16(l_run));              // row sums over the four 16-lane rows
+    if (tracing) tr[2] = trace_clock();
 
     __shared__ MergeLds<D> lds;
     merge_waves<D>(lds, o, m_run, l_run, qw, n, q, wave, tid,
@@ -332,6 +436,8 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
             }
         }
     });
+    if (tracing) tr[3] = trace_clock();
+    uint32_t trace_flags = 0;
     if constexpr (SPLIT) {
         if (p.fuse_ctr && n_used > 1) {
             // Count this partition in once all its partial stores are
@@ -354,9 +460,11 @@ __global__ __launch_bounds__(kMBlock) void pa_decode_mfma_kernel(DecodeParams p)
                     merge_partials<D, true>(p, ((int64_t)b * p.Hq + h) * p.n_part, 1, n_used,
                                             (int64_t)b * p.o_sb + (int64_t)h * p.o_sh);
                 }
+                trace_flags = 2;
             }
         }
     }
+    trace_out(trace_flags);
 }
 
 // ---------------------------------------------------------------------------

@@ -233,32 +233,36 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const TileFrag<
 
 // Q^T as the B operand of query heads h0 .. h0 + qw - 1 of sequence b (same
 // k <-> dim map as the K rows of the layout), in the KV element type: a Q
-// stored in another type is converted (round to nearest even).  Columns
-// past qw are zero.
+// stored in another type is converted (round to nearest even).  Lanes of
+// columns past qw load head h0 instead and are not cleared: an output column
+// depends only on its own column of Q^T and those columns' logits are masked
+// out, and a clear would make the wave wait for the reads right here.  In the
+// split layout the operands past the loaded ones are zero.
 template <int D, bool HALF, typename KV>
 __device__ __forceinline__ void load_q(const DecodeParams& p, int b, int h0, int qw, int n, int q,
                                        u32x4 (&qop)[D / 32]) {
     const int qcol = HALF ? (n & 7) : n;
     const bool live = qcol < qw;
     const int64_t qr = (int64_t)b * p.q_sb + (int64_t)(h0 + (live ? qcol : 0)) * p.q_sh;
+    constexpr int NL = HALF ? D / 64 : D / 32;          // loads; the split layout leaves the rest unused
+    u32x4 w[NL];
+    // The type test stays outside the loops, so all the loads are in flight
+    // together (a test per load would make each wait for the one before).
+    if (p.q_dtype == KV::code) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-        if (HALF && kk >= D / 64) {
-            qop[kk] = u32x4{0u, 0u, 0u, 0u};            // unused in the split layout
-            continue;
-        }
-        const int64_t off = qr + k_col<D, HALF>(kk, n, q);
-        u32x4 w;
-        if (p.q_dtype == KV::code) {
-            w = load16(static_cast<const uint16_t*>(p.q) + off);
-        } else {
+        for (int kk = 0; kk < NL; ++kk) w[kk] = load16(static_cast<const uint16_t*>(p.q) + qr + k_col<D, HALF>(kk, n, q));
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < NL; ++kk) {
             float f[8];
-            load8f(p.q, p.q_dtype, off, f);
+            load8f(p.q, p.q_dtype, qr + k_col<D, HALF>(kk, n, q), f);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = KV::pack2(f[2 * i], f[2 * i + 1]);
+            for (int i = 0; i < 4; ++i) w[kk][i] = KV::pack2(f[2 * i], f[2 * i + 1]);
         }
-        qop[kk] = live ? w : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        qop[kk] = kk < NL ? w[kk < NL ? kk : 0] : u32x4{0u, 0u, 0u, 0u};
 }
 
 // This wave's share of the tokens [ts, te): tiles ts + 16 (wave + 4k), rows

@@ -29,6 +29,19 @@ def test_header_declares_the_entry_points():
         assert must in names
 
 
+def test_trace_set_arguments():
+    lib = _binding.LIB
+    assert lib.pa_trace_set(None, 0) == pa.PA_OK                  # stop (also when never started)
+    assert lib.pa_trace_set(ctypes.c_void_p(0x1008), 4096) == pa.PA_EINVAL   # not 16-byte aligned
+    assert "aligned" in pa.last_error()
+    assert lib.pa_trace_set(None, 4096) == pa.PA_OK
+    assert pa.PA_TRACE_WORDS == 8
+    assert lib.pa_trace_clock_khz(None) == pa.PA_EINVAL
+    if not torch.cuda.is_available():
+        v = ctypes.c_int(0)
+        assert lib.pa_trace_clock_khz(ctypes.byref(v)) in (pa.PA_ENODEV, pa.PA_EHIP)
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(pa.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(lib, n)]

@@ -531,6 +531,54 @@ def test_fitted_many_sequences_ragged(B, Hq, Hkv, D):
         assert_parity(y, ref, f"B={B} D={D} target={n}")
 
 
+@pytest.mark.parametrize("variant", ["mfma-fit", "mfma-fit-fused", "mfma"])
+def test_trace_records(variant):
+    """The timeline records (pa_trace_set) of the partitioned MFMA decode on
+    the head_dim-256 workload: the output is unchanged, every workgroup that
+    ran a partition stamps its phases in order, and the (sequence, query
+    block, partition) triples of the records cover each group's tokens once;
+    with the merge in the kernel, one workgroup per split group merges it."""
+    inp = make_inputs("hd256_gqa4", seed=0)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    buf = torch.zeros(4096 * pa.PA_TRACE_WORDS, dtype=torch.int64, device="cuda")
+    pa.pa_trace_set(buf)
+    try:
+        y, s = gpu_run(d, variant=variant)
+    finally:
+        pa.pa_trace_set(None)
+    assert_parity(y, ref, f"hd256_gqa4/{variant} traced")
+    rec = buf.view(-1, pa.PA_TRACE_WORDS).cpu().numpy().astype(np.uint64)
+    rec = rec[rec[:, 4] != 0]                            # workgroups that wrote a record
+    assert len(rec) > 0
+    flags = (rec[:, 7] >> np.uint64(32)).astype(np.int64)
+    T = (rec[:, 7] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+    ran = rec[flags != 1]
+    t = ran[:, :5].astype(np.int64)
+    assert (t > 0).all() and (np.diff(t, axis=1) >= 0).all(), "phase stamps out of order"
+    lens = inp.context_lens
+    b = (ran[:, 6] & np.uint64(0xFFFF)).astype(np.int64)
+    qb = ((ran[:, 6] >> np.uint64(16)) & np.uint64(0xFFFF)).astype(np.int64)
+    part = (ran[:, 6] >> np.uint64(32)).astype(np.int64)
+    Tr = T[flags != 1]
+    assert len(set(Tr.tolist())) == 1, "one partition size per call"
+    Tc = int(Tr[0])
+    groups = {}
+    for bi, qi, pi in zip(b.tolist(), qb.tolist(), part.tolist()):
+        groups.setdefault((bi, qi), []).append(pi)
+    n_qb = max(qb.tolist()) + 1
+    for bi in range(len(lens)):
+        need = max(1, -(-int(lens[bi]) // Tc))
+        for qi in range(n_qb):
+            assert sorted(groups.get((bi, qi), [])) == list(range(need)), (bi, qi, groups.get((bi, qi)))
+    merged = int((flags == 2).sum())
+    split_groups = sum(1 for bi in range(len(lens)) if -(-int(lens[bi]) // Tc) > 1) * n_qb
+    if _MERGE.get(variant) == "fused":
+        assert merged == split_groups, (merged, split_groups)
+    else:
+        assert merged == 0
+
+
 def test_fitted_workspace_garbage_and_foreign_hints():
     """Fitted partitions keep each workgroup's last partition in the workspace
     as the next call's guess.  Any content there must give the same result:
@@ -568,6 +616,56 @@ def test_fitted_workspace_garbage_and_foreign_hints():
                 first[i] = y
             else:
                 assert np.array_equal(y, first[i]), f"fitted case {i} round {rnd}: result depends on the hints"
+
+
+def test_fitted_stale_hints():
+    """Each call's hints (the previous call's size and triples) are checked
+    against the current lengths and target before use.  A run of calls on one
+    workspace whose lengths shrink, empty out and come back, and whose
+    triple target changes, must match bit for bit a run on a fresh workspace
+    (no usable hint, full search) and, for two of them, the oracle."""
+    B, P = 32, 32
+    rng = np.random.default_rng(31)
+    base = rng.integers(1, 4097, B)
+    w = custom(batch=B, num_q_heads=8, num_kv_heads=2, head_dim=256, page_size=P, ctx=tuple(int(x) for x in base))
+    inp = make_inputs(w, seed=31)
+    d = to_device(inp)
+    q, k, v = d.call(0)
+    cut = base.copy()
+    cut[::3] = np.maximum(cut[::3] // 2, 1)
+    empty = base.copy()
+    empty[1::5] = 0
+    series = [(base, 0), (base - 1, 0), (cut, 0), (empty, 0), (base, 0), (base, 64), (base, 300), (cut, 1000),
+              (base, 0), (base, 0)]
+    opts_n = max(pa.pa_decode_workspace_bytes(B, 8, 2, 256, d.block_tables.shape[1], P,
+                                              pa.make_opts("mfma", 0, "fitted", shares=sh)) for _, sh in series)
+
+    def workspace():
+        raw = torch.zeros(opts_n + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 256
+        return raw[off:off + opts_n]
+
+    def run(lens, shares, ws):
+        ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        out = torch.full_like(q, float("nan"))
+        pa.pa_reset_stats()
+        pa.decode(q, k, v, d.block_tables, ctx, inp.w.scale, out=out, variant="mfma", schedule="fitted",
+                  shares=shares, workspace=ws)
+        torch.cuda.synchronize()
+        st = pa.pa_get_stats()
+        assert st["last_schedule"] == pa.PA_SCHEDULE_FITTED, st
+        return bits(out)
+
+    kept = workspace()
+    for i, (lens, shares) in enumerate(series):
+        y = run(lens, shares, kept)
+        fresh = run(lens, shares, workspace())
+        assert np.array_equal(y, fresh), f"call {i} (shares {shares}): result depends on the hints"
+        if i in (1, 3):
+            qh, kh, vh = inp.call(0)
+            ref = oracle.attention(qh, kh, vh, inp.block_tables, np.asarray(lens, dtype=np.int32), inp.w.scale,
+                                   inp.w.num_kv_heads)
+            assert_parity(y, ref, f"fitted stale hints, call {i}")
 
 
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 8), (256, 32, 4), (128, 64, 4)])
