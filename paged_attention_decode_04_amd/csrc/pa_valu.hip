@@ -281,9 +281,11 @@ __global__ __launch_bounds__(kBlock) void pa_decode_valu_kernel(DecodeParams p) 
 
 // Log-sum-exp merge of the split-KV partials: one 64-thread group per (h, b).
 // Partials read before the row's count is known: 32 at head_dim 128 (5
-// registers each), 16 above.
+// registers each), 8 above, where a slot is 1-2 KB: slots past the row's
+// count are read for nothing, and at 16 those bytes cost more than the
+// second round trip that rows of more than 8 partitions take.
 template <int D>
-constexpr int kMergeEager = D == 128 ? 32 : 16;
+constexpr int kMergeEager = D == 128 ? 32 : 8;
 template <int D>
 __global__ __launch_bounds__(64) void pa_lse_merge_kernel(DecodeParams p) {
     const int h = blockIdx.x, b = blockIdx.y;
