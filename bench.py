@@ -95,7 +95,7 @@ def parse():
                          "for rocprofv3 runs over its kernel")
     ap.add_argument("--timeline", metavar="WORKLOAD", default=None,
                     help="per-workgroup phase timeline (pa_trace_set) of one call of WORKLOAD on the "
-                         "partitioned MFMA decode, warm and MALL-cold, printed as a markdown summary")
+                         "partitioned MFMA decode, warm and MALL-cold, summarised per phase as one JSON line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a plain device copy of this many MiB (HBM reference and the "
                          "calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -459,6 +459,22 @@ def timeline_summary(rec, khz, lens, D, elem):
     stat("stream_GBps_per_wg", gbs)
     if (flags == 2).any():
         stat("kernel_merge_us", (t[flags == 2, 4] - t[flags == 2, 3]) * us)
+    # Workgroups whose partition is full (T tokens) stream the same bytes:
+    # their streaming time split by query block (which KV head they read)
+    # and by XCD.
+    qb = ((rec[run, 6] >> np.uint64(16)) & np.uint64(0xFFFF)).astype(np.int64)
+    xr = (rec[run, 5] >> np.uint64(32)).astype(np.int64)
+    full = tokens == Tr
+    out["full_partitions"] = int(full.sum())
+    def groups(keys):
+        res = {}
+        for k in sorted(set(keys[full].tolist())):
+            v = stream_us[full & (keys == k)]
+            res[str(k)] = {"n": int(len(v)), "p50": round(_pct(v, 50), 3), "max": round(float(v.max()), 3)}
+        return res
+    if full.any():
+        out["stream_full_by_query_block_us"] = groups(qb)
+        out["stream_full_by_xcd_us"] = groups(xr)
     last = {}
     for x, e in zip(xcc.tolist(), ((t[:, 4] - t0) * us).tolist()):
         last[x] = max(last.get(x, 0.0), e)
