@@ -668,6 +668,21 @@ def test_fitted_stale_hints():
             assert_parity(y, ref, f"fitted stale hints, call {i}")
 
 
+@pytest.mark.parametrize("P,ctx", [(1, (9000, 5000, 100, 0)), (2, (20000, 1, 16385, 700))])
+def test_balanced_multi_fill(P, ctx):
+    """The balanced schedule fetches a segment's page ids 4096 tokens at a
+    time: with pages of 1 and 2 tokens a fill holds 4098 and 2050 page ids,
+    and segments of up to 20000 tokens cross several fills, inside a share
+    and at its edges."""
+    w = custom(batch=len(ctx), num_q_heads=16, num_kv_heads=8, head_dim=128, page_size=P, ctx=ctx)
+    inp = make_inputs(w, seed=P + 40)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for n in (1, 7, 64):
+        y, _ = gpu_run(d, variant="mfma-bal", shares=n)
+        assert_parity(y, ref, f"balanced, page {P}, shares {n}")
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 8), (256, 32, 4), (128, 64, 4)])
 def test_balanced_share_sweep(D, Hq, Hkv):
     """Many share counts over a length mix with one long sequence: share
