@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--shares", type=int, default=0, help="balanced schedule: shares; fitted: workgroups to fill (0 = automatic)")
     ap.add_argument("--merge", default="auto", choices=["auto", "kernel", "fused"],
                     help="split partitions merged by a second kernel or inside the decode kernel")
+    ap.add_argument("--window", type=int, default=0,
+                    help="attend to each sequence's last WINDOW tokens only (the timed step; 0 = all)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "f16", "f32"],
+                    help="storage type of the K/V cache and Q of the timed step")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
@@ -672,16 +676,19 @@ def main():
         return
     w = wl.WORKLOADS[args.workload]
     t_gen = time.perf_counter()
+    dt = args.kv_dtype
     if w.name == "long_ctx_gqa8":
-        d = wl.device_inputs(w, seed=args.seed)
+        d = wl.device_inputs(w, seed=args.seed, dtype=dt)
     else:
-        d = wl.to_device(wl.make_inputs(w, seed=args.seed))
+        d = wl.to_device(wl.make_inputs(w, seed=args.seed, dtype=dt))
     torch.cuda.synchronize()
-    log(f"[bench] inputs for {w.name} ready in {time.perf_counter() - t_gen:.1f}s")
-    kvb_per_call = wl.kv_bytes(w, d.layout.context_lens)
+    log(f"[bench] inputs for {w.name} ({dt}) ready in {time.perf_counter() - t_gen:.1f}s")
+    kvb_per_call = wl.kv_bytes(w, d.layout.context_lens, args.window, ELEM_BYTES[dt])
     n_calls = w.calls
     knobs = dict(variant=args.variant, partition_tokens=args.partition_tokens,
                  schedule=args.schedule, shares=args.shares, merge=args.merge)
+    if args.window:
+        knobs["window"] = args.window
     ws = make_workspace(pa, d, knobs)
     calls = [make_call(pa, d, i, knobs, ws)[0] for i in range(n_calls)]
 
@@ -738,14 +745,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if variant == "mfma" else "f32",
-        "storage_dtype": "bf16",
+        "dtype": dt if variant == "mfma" else "f32",   # MFMA products in the cache's 16-bit type
+        "storage_dtype": dt,
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled block tables)",
         "config": {
             "workload": w.name, "desc": w.desc, "batch": w.batch,
             "sum_ctx": int(d.layout.context_lens.sum()), "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
             "calls_per_step": n_calls, "kv_bytes_per_call": kvb_per_call, **launch,
+            **({"window": args.window} if args.window else {}),
         },
         "launch_mode": "graph replay" if args.graph else "eager",
         "us_per_call": round(us_per_call_ev, 3),
@@ -753,7 +761,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": profiled_traffic(kernel, w.name, launch),
+            # the committed counter runs are of the bf16, unwindowed workloads
+            "traffic": profiled_traffic(kernel, w.name, launch) if dt == "bf16" and not args.window else None,
             "kernel": kernel + (f" + {merge}" if merge else ""),
             "duration_us": round(us_per_call_ev, 3),
             "note": "achieved = algorithmic KV bytes per call / HIP-event time per call over the "
