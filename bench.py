@@ -100,6 +100,8 @@ def parse():
     ap.add_argument("--timeline", metavar="WORKLOAD", default=None,
                     help="per-workgroup phase timeline (pa_trace_set) of one call of WORKLOAD on the "
                          "partitioned MFMA decode, warm and MALL-cold, summarised per phase as one JSON line")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="only the MFMA/VALU issue-rate probe, printed as one JSON line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a plain device copy of this many MiB (HBM reference and the "
                          "calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -525,6 +527,46 @@ def timeline_line(pa, torch, workloads_mod, name, knobs):
     return res
 
 
+def issue_probe_line(torch, rounds=4096):
+    """How MFMA and vector-ALU work share a SIMD (libpa_probe.so's issue-rate
+    probe): per mode, rounds of NM 16x16x32 bf16 MFMAs and NV independent fp32
+    FMAs, in every wave (mixed) or in separate MFMA-only and FMA-only waves,
+    at one and four waves per SIMD.  Times are turned into cycles per
+    wave-round with one clock calibration: the MFMA-only mode at four waves
+    per SIMD keeps the matrix pipe saturated at 16 cycles per MFMA.
+    References: serial = 16 NM + 4 NV cycles (the two pipes one after the
+    other), overlapped = max(16 NM, 4 NV); for split modes, per wave-round
+    over both kinds of wave, half of each."""
+    from paged_attention_decode_04_amd import probe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(4 * cus, dtype=torch.int32, device="cuda")
+    modes = probe.issue_modes()
+    times = {}
+    for wps in (1, 4):
+        n_wg = cus * wps                      # 4 waves per workgroup, 4 SIMDs per CU
+        for i in range(len(modes)):
+            f = (lambda i=i, n_wg=n_wg: probe.issue(i, n_wg, rounds, sink))
+            event_time_ms(f, 2, torch)
+            times[(wps, i)] = min(event_time_ms(f, 5, torch) / 5 for _ in range(3))
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    ref = next(i for i, m in enumerate(modes) if m == (1, 0, True))
+    hz = rounds * 4 * 16 / (times[(4, ref)] * 1e-3)      # cycles per second of the saturated MFMA run
+    rows = []
+    for (wps, i), ms in sorted(times.items()):
+        nm, nv, mixed = modes[i]
+        cyc = ms * 1e-3 * hz / (rounds * wps)
+        serial = 16 * nm + 4 * nv
+        over = max(16 * nm, 4 * nv)
+        if not mixed:
+            serial, over = serial / 2, over / 2
+        rows.append({"waves_per_simd": wps, "mfma_per_round": nm, "fma_per_round": nv,
+                     "waves": "mixed" if mixed else "split", "us_per_launch": round(ms * 1e3, 2),
+                     "cycles_per_wave_round": round(cyc, 1), "serial_cycles": serial, "overlapped_cycles": over})
+    return {"probe": "issue-rate (pa_probe_issue)", "cus": cus, "rounds": rounds,
+            "clock_GHz_from_mfma_rate": round(hz / 1e9, 3), "modes": rows}
+
+
 def _median_time(fn, runs):
     ts = []
     for _ in range(runs):
@@ -668,6 +710,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_prefill:
         print(json.dumps(prefill_line(pa, torch, wl)), flush=True)
+        return
+    if args.issue_probe:
+        print(json.dumps(issue_probe_line(torch)), flush=True)
         return
     if args.timeline:
         knobs = dict(variant=args.variant, partition_tokens=args.partition_tokens,

@@ -5,7 +5,7 @@
  *
  * Each probe only reads: it streams the bytes a decode call would read, with
  * no arithmetic, so its rate is what the memory system gives that access
- * pattern.  Two patterns:
+ * pattern.  Two patterns (and an issue-rate probe, below):
  *
  *  - contiguous: `bytes` bytes from `base`, 16 bytes per lane per load,
  *    grid-stride over n_wg workgroups of 256 threads;
@@ -57,6 +57,25 @@ typedef struct pa_probe_paged {
 
 /* n_wg: 1 .. 4096 workgroups. */
 int pa_probe_read_paged(const pa_probe_paged* d, int n_wg, void* sink, void* stream);
+
+/* Issue-rate probe of one CU's SIMDs (no memory traffic): how matrix-core
+ * products and vector-ALU work share a SIMD, the bound of the several-query
+ * kernel, whose 32-token pairs issue 26 MFMAs and about 64 other VALU
+ * instructions in dependent blocks.  Mode i of a fixed menu runs `rounds`
+ * rounds of NM 16x16x32 bf16 MFMAs and NV independent fp32 FMAs per wave,
+ * either interleaved in every wave (mixed = 1) or split between MFMA-only and
+ * FMA-only waves (mixed = 0); n_wg workgroups of 256 threads (on 256 CUs,
+ * 256 of them give one wave per SIMD and 1024 give four).  The caller times
+ * the launch.
+ *
+ * pa_probe_issue_modes(i, &nm, &nv, &mixed): describes mode i; returns the
+ * number of modes (also for i < 0, which writes nothing), -1 for i past the
+ * menu or a NULL output.
+ * pa_probe_issue: 0 on success, 1 on a bad argument (mode outside the menu,
+ * n_wg outside 1 .. 65536, rounds outside 1 .. 2^20, sink NULL; nothing
+ * enqueued), 2 when the launch failed.  sink: n_wg 32-bit words (device). */
+int pa_probe_issue_modes(int mode, int* nm, int* nv, int* mixed);
+int pa_probe_issue(int mode, int n_wg, int rounds, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

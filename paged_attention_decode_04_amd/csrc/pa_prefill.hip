@@ -237,22 +237,34 @@ __device__ __forceinline__ void vm_wait_barrier() {
 // 32 tokens tb .. tb + 31 from one stage buffer (rows 0 .. 31 of kl / vl),
 // in two steps so that a stage can issue the logits of all its pairs before
 // the first softmax (the matrix cores then overlap the vector work):
-// pair_logits: the logits of the two 16-token halves on MFMA;
+// stage_logits: the logits of the two 16-token halves of each pair on MFMA;
 // pair_update: one online-softmax update, and P.V as one 16x16x32 MFMA per
 // 16 dims whose contraction runs over both halves (lane q's eight k-slots:
 // tokens 4q .. 4q+3 of each half).  P enters P.V as the sum of two KV-type
 // values, hi = round(p) and lo = round(p - hi): the weights are then exact to
 // about 2^-17 relative, and the normaliser sums those same weights.
-template <int D, typename KV>
-__device__ __forceinline__ void pair_logits(const uint16_t* kl, const u32x4 (&qop)[D / 32], int n, int q,
-                                            f32x4& sa, f32x4& sb) {
-    sa = f32x4{0.f, 0.f, 0.f, 0.f};
-    sb = f32x4{0.f, 0.f, 0.f, 0.f};
+//
+// Products into one accumulator are spaced apart: with accumulators in
+// VGPRs, an MFMA that reads the previous one's result waits for it (a chain
+// of dependent 16x16x32 MFMAs runs at about a third of the issue rate).
+// The logits of all NPAIR pairs are accumulated k-step by k-step, 2 NPAIR
+// chains side by side.
+template <int D, int NPAIR, typename KV>
+__device__ __forceinline__ void stage_logits(const uint16_t* kl, const u32x4 (&qop)[D / 32], int n, int q,
+                                             f32x4 (&sa)[NPAIR], f32x4 (&sb)[NPAIR]) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-        sa = KV::mma_qk(lds16(kl + n * D + swz(n, 4 * kk + q)), qop[kk], sa);
-        sb = KV::mma_qk(lds16(kl + (16 + n) * D + swz(16 + n, 4 * kk + q)), qop[kk], sb);
+    for (int i = 0; i < NPAIR; ++i) {
+        sa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+        for (int i = 0; i < NPAIR; ++i) {
+            const uint16_t* kli = kl + 32 * i * D;
+            sa[i] = KV::mma_qk(lds16(kli + n * D + swz(n, 4 * kk + q)), qop[kk], sa[i]);
+            sb[i] = KV::mma_qk(lds16(kli + (16 + n) * D + swz(16 + n, 4 * kk + q)), qop[kk], sb[i]);
+        }
 }
 
 // Raise this wave's issue priority over a block of matrix-core work and
@@ -339,12 +351,17 @@ __device__ __forceinline__ void pair_softmax(const DecodeParams& p, const f32x4&
 // each column's weights (hi + lo, exactly the ones P.V uses) over all 32
 // tokens, in every row of the tile.
 template <typename KV>
-__device__ __forceinline__ void pair_norm(const u32x4& ph, const u32x4& pl, f32x4& l_acc) {
+__device__ __forceinline__ u32x4 ones_operand() {
     const uint32_t one2 = KV::pack2(1.f, 1.f);
-    const u32x4 ones = {one2, one2, one2, one2};
-    l_acc = KV::mma_qk(ones, ph, l_acc);
-    l_acc = KV::mma_qk(ones, pl, l_acc);
+    return u32x4{one2, one2, one2, one2};
 }
+
+// P.V output tiles taken G at a time: the G hi products, then the G lo
+// products, so that the two products into one accumulator are G MFMAs
+// apart.  4 at head_dim 256; 2 at 128, where 4 would take the kernel past
+// 128 VGPRs and cost the second workgroup per CU.
+template <int D>
+constexpr int kPvGroup = D == 128 ? 2 : 4;
 
 // V^T operands by transposing LDS reads (ds_read_b64_tr_b16): inside each
 // 16-lane group, lane j gets slot k from element j % 4 of the 8 bytes at
@@ -366,16 +383,24 @@ __device__ __forceinline__ void pair_update(const DecodeParams& p, const uint16_
                                             const f32x4& sb, int tb, bool mask, int mask_lo, int mask_hi, int n,
                                             int q, bool col_live, f32x4 (&o)[D / 16], float& m_run, f32x4& l_acc) {
     constexpr int NO = D / 16;
+    constexpr int G = kPvGroup<D>;
+    static_assert(NO % G == 0, "P.V groups");
     u32x4 ph, pl;
     pair_softmax<D, KV>(p, sa, sb, tb, mask, mask_lo, mask_hi, q, col_live, o, m_run, l_acc, ph, pl);
     mfma_prio<D, 1>();
-    pair_norm<KV>(ph, pl, l_acc);
+    const u32x4 ones = ones_operand<KV>();
+    l_acc = KV::mma_qk(ones, ph, l_acc);        // the normaliser's lo product comes after the P.V ones
 #pragma unroll
-    for (int t = 0; t < NO; ++t) {
-        const u32x4 vt = v_operand<D>(vl, n, q, t);
-        o[t] = KV::mma_qk(vt, ph, o[t]);
-        o[t] = KV::mma_qk(vt, pl, o[t]);
+    for (int t0 = 0; t0 < NO; t0 += G) {
+        u32x4 vt[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) vt[j] = v_operand<D>(vl, n, q, t0 + j);
+#pragma unroll
+        for (int j = 0; j < G; ++j) o[t0 + j] = KV::mma_qk(vt[j], ph, o[t0 + j]);
+#pragma unroll
+        for (int j = 0; j < G; ++j) o[t0 + j] = KV::mma_qk(vt[j], pl, o[t0 + j]);
     }
+    l_acc = KV::mma_qk(ones, pl, l_acc);
     mfma_prio<D, 0>();
 }
 
@@ -467,8 +492,7 @@ __device__ __forceinline__ void staged_stage(const DecodeParams& p, const uint16
     constexpr int NPAIR = C::ST / 32;
     f32x4 sa[NPAIR], sb[NPAIR];
     mfma_prio<D, 1>();
-#pragma unroll
-    for (int i = 0; i < NPAIR; ++i) pair_logits<D, KV>(kl + 32 * i * D, qop, n, q, sa[i], sb[i]);
+    stage_logits<D, NPAIR, KV>(kl, qop, n, q, sa, sb);
     mfma_prio<D, 0>();
 #pragma unroll
     for (int i = 0; i < NPAIR; ++i) {

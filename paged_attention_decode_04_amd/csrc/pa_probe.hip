@@ -144,6 +144,68 @@ __global__ __launch_bounds__(kProbeBlock) void pa_probe_paged_kernel(PagedProbe 
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Issue-rate probe: every round, NM matrix-core products (16x16x32 bf16, on
+// two accumulator chains) and NV independent fp32 FMAs (on eight chains).
+// MIXED: every wave issues both, interleaved in program order.  Otherwise
+// the waves of a workgroup alternate between MFMA only and FMA only (each
+// SIMD then holds waves of both kinds).  Nothing is read from memory; the
+// folded result goes to the sink only if it equals a fixed constant.
+typedef float pf32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 pbf16x8 __attribute__((ext_vector_type(8)));
+
+template <int NM, int NV, bool MIXED>
+__global__ __launch_bounds__(kProbeBlock) void pa_probe_issue_kernel(uint32_t* sink, float seed, int rounds) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    pbf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(seed * (float)(threadIdx.x + i));
+        b[i] = (__bf16)(seed - (float)i);
+    }
+    pf32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = seed * (float)i + (float)threadIdx.x;
+    auto mfmas = [&]() {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[m & 1], 0, 0, 0);
+    };
+    auto fmas = [&]() {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j & 7] = fmaf(v[j & 7], 1.0001f, 0.5f);
+    };
+    if constexpr (MIXED) {
+        for (int it = 0; it < rounds; ++it) {
+            mfmas();
+            fmas();
+        }
+    } else if ((wave + (int)blockIdx.x) & 1) {      // wave-uniform
+        for (int it = 0; it < rounds; ++it) mfmas();
+    } else {
+        for (int it = 0; it < rounds; ++it) fmas();
+    }
+    float s = acc[0][0] + acc[1][1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+    if (__float_as_uint(s) == kSinkMagic) sink[blockIdx.x] = kSinkMagic;
+}
+
+struct IssueMode {
+    int nm, nv, mixed;
+};
+// The menu of pa_probe_issue: one MFMA or four FMAs alone, one MFMA with 2,
+// 3, 4 and 8 FMAs, two MFMAs with 6, all in every wave; then MFMA-only
+// beside FMA-only waves.
+constexpr IssueMode kIssueModes[] = {{1, 0, 1}, {0, 4, 1}, {1, 2, 1}, {1, 3, 1}, {1, 4, 1},
+                                     {1, 8, 1}, {2, 6, 1}, {1, 4, 0}, {2, 6, 0}};
+constexpr int kIssueModeCount = sizeof(kIssueModes) / sizeof(kIssueModes[0]);
+
+template <int NM, int NV, bool MIXED>
+void launch_issue(int n_wg, int rounds, uint32_t* sink, hipStream_t s) {
+    hipLaunchKernelGGL((pa_probe_issue_kernel<NM, NV, MIXED>), dim3(n_wg), dim3(kProbeBlock), 0, s, sink, 1.0f,
+                       rounds);
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,6 +253,35 @@ int pa_probe_read_paged(const pa_probe_paged* d, int n_wg, void* sink, void* str
         hipLaunchKernelGGL((pa_probe_paged_kernel<16, 3>), dim3(n_wg), dim3(kProbeBlock), lds, s, pp);
     else
         hipLaunchKernelGGL((pa_probe_paged_kernel<32, 2>), dim3(n_wg), dim3(kProbeBlock), lds, s, pp);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int pa_probe_issue_modes(int mode, int* nm, int* nv, int* mixed) {
+    if (mode < 0) return kIssueModeCount;
+    if (mode >= kIssueModeCount || !nm || !nv || !mixed) return -1;
+    *nm = kIssueModes[mode].nm;
+    *nv = kIssueModes[mode].nv;
+    *mixed = kIssueModes[mode].mixed;
+    return kIssueModeCount;
+}
+
+int pa_probe_issue(int mode, int n_wg, int rounds, void* sink, void* stream) {
+    if (!sink || mode < 0 || mode >= kIssueModeCount || n_wg < 1 || n_wg > 65536 || rounds < 1 ||
+        rounds > (1 << 20))
+        return 1;
+    uint32_t* sk = static_cast<uint32_t*>(sink);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (mode) {
+        case 0: launch_issue<1, 0, true>(n_wg, rounds, sk, s); break;
+        case 1: launch_issue<0, 4, true>(n_wg, rounds, sk, s); break;
+        case 2: launch_issue<1, 2, true>(n_wg, rounds, sk, s); break;
+        case 3: launch_issue<1, 3, true>(n_wg, rounds, sk, s); break;
+        case 4: launch_issue<1, 4, true>(n_wg, rounds, sk, s); break;
+        case 5: launch_issue<1, 8, true>(n_wg, rounds, sk, s); break;
+        case 6: launch_issue<2, 6, true>(n_wg, rounds, sk, s); break;
+        case 7: launch_issue<1, 4, false>(n_wg, rounds, sk, s); break;
+        default: launch_issue<2, 6, false>(n_wg, rounds, sk, s); break;
+    }
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -35,6 +35,11 @@ def _load():
         lib.pa_probe_read_paged.argtypes = [ctypes.POINTER(PaProbePaged), ctypes.c_int, ctypes.c_void_p,
                                             ctypes.c_void_p]
         lib.pa_probe_read_paged.restype = ctypes.c_int
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.pa_probe_issue_modes.argtypes = [ctypes.c_int, ip, ip, ip]
+        lib.pa_probe_issue_modes.restype = ctypes.c_int
+        lib.pa_probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.pa_probe_issue.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -74,3 +79,23 @@ def read_paged(desc: PaProbePaged, n_wg: int, sink, stream=None) -> None:
     rc = _load().pa_probe_read_paged(ctypes.byref(desc), int(n_wg), sink.data_ptr(), _stream(stream))
     if rc:
         raise RuntimeError(f"pa_probe_read_paged returned {rc}")
+
+
+def issue_modes() -> list:
+    """The issue-rate probe's menu: (MFMAs, FMAs, mixed) per round, per mode."""
+    lib = _load()
+    n = lib.pa_probe_issue_modes(-1, None, None, None)
+    out = []
+    for i in range(n):
+        nm, nv, mixed = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        if lib.pa_probe_issue_modes(i, ctypes.byref(nm), ctypes.byref(nv), ctypes.byref(mixed)) != n:
+            raise RuntimeError(f"pa_probe_issue_modes({i}) failed")
+        out.append((nm.value, nv.value, bool(mixed.value)))
+    return out
+
+
+def issue(mode: int, n_wg: int, rounds: int, sink, stream=None) -> None:
+    """Run mode ``mode`` of the issue-rate probe (n_wg workgroups of 256 threads)."""
+    rc = _load().pa_probe_issue(int(mode), int(n_wg), int(rounds), sink.data_ptr(), _stream(stream))
+    if rc:
+        raise RuntimeError(f"pa_probe_issue returned {rc}")

@@ -52,14 +52,14 @@ PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "pa_probe.h")
 
 
 def test_probe_library_exports_and_validates():
-    """libpa_probe.so (the benchmark's streaming-read probes) exports every
-    function pa_probe.h declares and refuses bad arguments before any HIP
-    call."""
+    """libpa_probe.so (the benchmark's streaming-read and issue-rate probes)
+    exports every function pa_probe.h declares and refuses bad arguments
+    before any HIP call."""
     from paged_attention_decode_04_amd import probe
     lib = ctypes.CDLL(probe.PROBE_LIB_PATH)
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"^\s*int\s+(pa_probe_[a-z_]+)\s*\(", text, flags=re.M)))
-    assert names == ["pa_probe_read_contiguous", "pa_probe_read_paged"]
+    assert names == ["pa_probe_issue", "pa_probe_issue_modes", "pa_probe_read_contiguous", "pa_probe_read_paged"]
     assert all(hasattr(lib, n) for n in names)
     plib = probe._load()
     assert plib.pa_probe_read_contiguous(None, 16, 1, None, None) == 1
@@ -80,6 +80,16 @@ def test_probe_library_exports_and_validates():
     assert plib.pa_probe_read_paged(ctypes.byref(d), 256, 0x2000, None) == 1
     d.row_bytes = 256
     assert plib.pa_probe_read_paged(ctypes.byref(d), 0, 0x2000, None) == 1     # no workgroups
+    # the issue-rate probe: its menu, and arguments refused before any launch
+    assert probe.issue_modes()[0] == (1, 0, True)
+    n = len(probe.issue_modes())
+    assert plib.pa_probe_issue_modes(n, None, None, None) == -1
+    assert plib.pa_probe_issue(0, 256, 16, None, None) == 1                     # no sink
+    assert plib.pa_probe_issue(n, 256, 16, 0x2000, None) == 1                   # mode past the menu
+    assert plib.pa_probe_issue(-1, 256, 16, 0x2000, None) == 1
+    assert plib.pa_probe_issue(0, 0, 16, 0x2000, None) == 1                     # no workgroups
+    assert plib.pa_probe_issue(0, 256, 0, 0x2000, None) == 1                    # no rounds
+    assert plib.pa_probe_issue(0, 256, (1 << 20) + 1, 0x2000, None) == 1
 
 
 def test_version_and_strerror():

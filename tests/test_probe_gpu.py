@@ -33,3 +33,16 @@ def test_paged_probe_runs(name):
         probe.read_paged(desc, n_wg, sink)
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0
+
+
+def test_issue_probe_runs():
+    """Every mode of the issue-rate probe runs (few rounds, one and four waves
+    per SIMD); it writes nothing but by chance."""
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    modes = probe.issue_modes()
+    assert len(modes) >= 2 and all(nm + nv > 0 for nm, nv, _ in modes)
+    for i in range(len(modes)):
+        for n_wg in (256, 1024):
+            probe.issue(i, n_wg, 64, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
