@@ -911,6 +911,22 @@ def test_fp32_cache_on_mfma_is_enotsup(variant, D):
     assert bool(torch.all(out == 7.0))
 
 
+@pytest.mark.parametrize("kt", ["bf16", "f16"])
+@pytest.mark.parametrize("P", [8, 24])
+def test_head_dim_512_wide_groups_small_pages(kt, P):
+    """head_dim 512 with 16 query heads per KV head (the row = token layout)
+    on pages that are not a power of two of at least 16 tokens (per-row page
+    lookup): the MFMA kernel instantiation whose registers run out (it keeps
+    some in scratch), split and unsplit, against the oracle."""
+    w = custom(batch=3, num_q_heads=16, num_kv_heads=1, head_dim=512, page_size=P, ctx=(1, 77, 900))
+    inp = make_inputs(w, seed=P + 512, poison_unused=True, dtype=kt)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for T in (0, 64, 256):
+        y, _ = gpu_run(d, variant="mfma", partition_tokens=T)
+        assert_parity(y, ref, f"D=512 qg=16 P={P} kv {kt} T={T}")
+
+
 @pytest.mark.parametrize("kt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (16, 4), (16, 2)])
 def test_head_dim_512(kt, Hq, Hkv):
