@@ -122,7 +122,10 @@ typedef struct pa_tensor {
  * fits to the actual lengths (chosen automatically, without a window and
  * for at most 256 sequences, where fixed partitions would cut the tables
  * into 4 or more and the tables hold at least 192 MB of K/V); partial results are
- * merged with the log-sum-exp rule by a second kernel.  The library keeps a
+ * merged with the log-sum-exp rule by a second kernel or, where that is
+ * faster (fixed partitions, at most two per (sequence, query block), at
+ * most 256 workgroups; pa_opts.merge), inside the decode kernel by the last
+ * partition of each group to finish.  The library keeps a
  * per-device workspace for the partials, grown on demand with hipMalloc
  * (an outgrown buffer is kept until pa_release(), which frees them all);
  * calls that use it must not overlap in time on one device (callers that
