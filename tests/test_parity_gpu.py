@@ -216,6 +216,25 @@ def workloads_f32(b):
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 48), (128, 16, 8, 64), (128, 16, 8, 256),
+                                        (256, 8, 2, 128)])
+def test_large_pages_poisoned(D, Hq, Hkv, P, variant):
+    """Pages of several tiles, as long as a partition or longer (48 to 256
+    tokens): lengths on and off page and partition boundaries, with every
+    unread slot and page set to NaN."""
+    lens = (1, P - 1, P, P + 1, 1000, 4097, 9000)
+    w = custom(batch=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
+               ctx=lens, pool_pages=sum(-(-L // P) for L in lens) + 3)
+    inp = make_inputs(w, seed=P + D, poison_unused=True)
+    d = to_device(inp)
+    ref = oracle_run(inp)
+    for kn in knobs(variant, (0, 64, 320)):
+        y, _ = gpu_run(d, variant=variant, **kn)
+        assert np.all(np.isfinite(workloads_f32(y)))
+        assert_parity(y, ref, f"D={D} P={P} {kn}")
+
+
 # ------------------------------------------------------------------ exactness
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_ctx1_returns_v_row_bitwise(variant):
@@ -1021,7 +1040,8 @@ def oracle_queries(inp, q, qs, window=0):
 
 
 @pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 16), (128, 32, 2, 16), (256, 8, 2, 32),
-                                        (128, 16, 16, 16), (128, 16, 1, 7), (256, 16, 4, 1)])
+                                        (128, 16, 16, 16), (128, 16, 1, 7), (256, 16, 4, 1),
+                                        (128, 16, 8, 64), (128, 16, 8, 256), (256, 8, 2, 128)])
 def test_prefill_parity(D, Hq, Hkv, P):
     """A batch mixing whole-prompt prefill, chunked prefill and decode steps:
     every query row against the causal oracle, split and unsplit, with and
