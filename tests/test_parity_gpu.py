@@ -180,6 +180,44 @@ def test_long_context_all_rows(variant, long_ctx):
     assert_parity(y, long_ctx.ref(), f"long_ctx all rows {variant}")
 
 
+class SingleLong:
+    """One sequence of 200,003 tokens (Hq 64 / Hkv 8, d 128, page 16; 820 MB
+    of K/V): every schedule cuts each of its 8 query blocks into many
+    partitions or pieces (up to 3126 per row at 64-token partitions), so the
+    merges run far past the partials they read in their first round trip."""
+
+    def __init__(self):
+        w = custom("single_long", batch=1, num_q_heads=64, num_kv_heads=8, head_dim=128, page_size=16,
+                   ctx=(200003,))
+        self.inp = make_inputs(w, seed=21)
+        self.d = to_device(self.inp)
+        self._ref = None
+
+    def ref(self):
+        if self._ref is None:
+            self._ref = oracle_run(self.inp)
+        return self._ref
+
+
+@pytest.fixture(scope="module")
+def single_long(gpu):
+    sl = SingleLong()
+    yield sl
+    del sl.d
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_single_long_sequence(variant, single_long):
+    for kn in knobs(variant, (0, 64, 4096)):
+        y, s = gpu_run(single_long.d, variant=variant, **kn)
+        # a partition holds at most 8192 pages' tokens (131072 here), so even
+        # the largest size asked for splits this sequence
+        assert s["split_calls"] == 1, s
+        assert_parity(y, single_long.ref(),
+                      f"200003 tokens {variant} {kn} (x{s['last_num_partitions']}, T={s['last_partition_tokens']})")
+
+
 # ------------------------------------------------------------------ geometry
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("D", [128, 256])
