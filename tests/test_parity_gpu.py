@@ -221,7 +221,7 @@ def test_single_long_sequence(variant, single_long):
 # ------------------------------------------------------------------ geometry
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("D", [128, 256])
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (32, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (32, 2), (6, 6), (12, 3), (40, 5)])
 def test_head_geometries(D, Hq, Hkv, variant):
     w = custom(batch=3, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=16,
                ctx=(1, 257, 700))
