@@ -350,7 +350,7 @@ int pa_check_args(const pa_tensor* q,
  *                must be automatic or MFMA.  Schedules: PARTITIONS = one
  *                workgroup per query block (16 / qg query tokens times the
  *                qg heads of a KV head), long contexts split into partitions
- *                merged by log-sum-exp; STAGED = four consecutive query
+ *                merged by log-sum-exp; STAGED = eight consecutive query
  *                blocks per workgroup share each K/V stage (no split, no
  *                workspace; partition_tokens must be 0); AUTO takes STAGED
  *                when partition_tokens is 0, the call has at least two query

@@ -724,7 +724,7 @@ int validate_append(const pa_tensor* kn, const pa_tensor* vn, const pa_tensor* k
 
 // ---------------------------------------------------------------- several queries
 struct PrefillPlan {
-    bool staged;        // four query blocks per workgroup (no split)
+    bool staged;        // eight query blocks per workgroup (no split)
     int n_slots;        // query-block slots (an upper bound on the blocks); staged: workgroup slots
     int part_tokens;
     int n_part;

@@ -650,11 +650,33 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_staged_kernel(DecodeParams
     }
 }
 
+// LDS of the staged kernel beyond its dynamic part (page ids of one fill and
+// the B + 1 prefix sums of workgroup slots): the K/V stages, and a margin for
+// the few scalars the kernel shares (36 bytes now).  pa_prefill takes at most
+// 4096 sequences, so even pages of one token leave the whole within the CU's
+// 160 KB at both head dims.
+template <int D, int NW, int NB>
+constexpr size_t staged_static_lds() {
+    return sizeof(uint16_t) * NB * 2 * Staged<D, NW, NB>::STAGE + 1024;
+}
+template <int D, int NW, int NB>
+constexpr size_t staged_dynamic_lds(int page_size, int batch) {
+    return sizeof(int) * ((size_t)(Staged<D, NW, NB>::kFillTokens / page_size) + 2 + (size_t)batch + 1);
+}
+constexpr size_t kCuLdsBytes = 160 * 1024;
+static_assert(staged_static_lds<128, kStagedWaves, kStagedBuffers128>() +
+                  staged_dynamic_lds<128, kStagedWaves, kStagedBuffers128>(1, 4096) <= kCuLdsBytes,
+              "staged kernel LDS at head_dim 128");
+static_assert(staged_static_lds<256, kStagedWaves, kStagedBuffers256>() +
+                  staged_dynamic_lds<256, kStagedWaves, kStagedBuffers256>(1, 4096) <= kCuLdsBytes,
+              "staged kernel LDS at head_dim 256");
+
 template <int D, int NW, int NB, typename KV>
 static hipError_t launch_staged_d(DecodeParams p, hipStream_t s) {
     using C = Staged<D, NW, NB>;
     p.lean_page_slots = C::kFillTokens / p.P + 2;
     const size_t lds = sizeof(int) * (size_t)(p.lean_page_slots + p.B + 1);
+    if (staged_static_lds<D, NW, NB>() + lds > kCuLdsBytes) return hipErrorInvalidValue;
     dim3 grid((uint32_t)((int64_t)p.n_slots * p.Hkv));
     hipLaunchKernelGGL((pa_prefill_staged_kernel<D, NW, NB, KV>), grid, dim3(C::NT), lds, s, p);
     return hipGetLastError();

@@ -1068,7 +1068,7 @@ def prefill_run(d, q, qs, out_dtype=None, **kw):
 
 
 # (schedule, partition_tokens): the per-block kernel unsplit / split / one
-# partition, and four query blocks per workgroup sharing K/V stages in LDS
+# partition, and eight query blocks per workgroup sharing K/V stages in LDS
 PREFILL_SCHEDULES = [("partitions", 0), ("partitions", 64), ("partitions", 1 << 20), ("staged", 0)]
 
 
