@@ -154,12 +154,14 @@ int pa_decode(const pa_tensor* q,
  * the decode step, on the same NHD pool (page 1, issue "ROCm gfx1200:
  * PagedAttnOnline is 8.1x slower per call", section "Where to look").
  *
- *  k_new, v_new  [B, Hkv, D]        bf16, stride[2] == 1, 16-byte aligned rows.
- *  k_cache, v_cache [NP, P, Hkv, D] bf16 NHD pools, as in pa_decode; written.
+ *  k_new, v_new  [B, Hkv, D]        bf16, fp16 or fp32 (the caches' type),
+ *                                   stride[2] == 1, 16-byte aligned rows.
+ *  k_cache, v_cache [NP, P, Hkv, D] NHD pools of one element type, as in
+ *                pa_decode; written (the rows are copied bit for bit).
  *  block_tables  [B, MaxBlk] int32; context_lens [B] int32 -- lengths that
  *                already count the new token.
- *  num_kv_heads, head_dim, page_size must equal the shapes; head_dim is any
- *                multiple of 8.
+ *  num_kv_heads, head_dim, page_size must equal the shapes; a row of head_dim
+ *                elements must be whole 16-byte chunks (PA_ENOTSUP else).
  *
  * For each b with L = context_lens[b] >= 1 and t = L - 1, the rows
  * k_new[b][g][:] and v_new[b][g][:] of every KV head g are written to
@@ -194,7 +196,7 @@ int pa_cache_append(const pa_tensor* k_new,
                                       into one equal static share per
                                       workgroup plus small units taken from a
                                       counter as workgroups finish           */
-#define PA_SCHEDULE_STAGED      3  /* pa_prefill only: a workgroup takes four
+#define PA_SCHEDULE_STAGED      3  /* pa_prefill only: a workgroup takes eight
                                       query blocks of one sequence, which share
                                       every K/V stage through LDS; no split   */
 #define PA_SCHEDULE_FITTED      4  /* MFMA only, no window, at most 256
