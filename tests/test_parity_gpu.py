@@ -1079,7 +1079,8 @@ def oracle_queries(inp, q, qs, window=0):
 
 @pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 16), (128, 32, 2, 16), (256, 8, 2, 32),
                                         (128, 16, 16, 16), (128, 16, 1, 7), (256, 16, 4, 1),
-                                        (128, 16, 8, 64), (128, 16, 8, 256), (256, 8, 2, 128)])
+                                        (128, 16, 8, 64), (128, 16, 8, 256), (256, 8, 2, 128),
+                                        (128, 12, 3, 16), (256, 40, 5, 32)])
 def test_prefill_parity(D, Hq, Hkv, P):
     """A batch mixing whole-prompt prefill, chunked prefill and decode steps:
     every query row against the causal oracle, split and unsplit, with and
