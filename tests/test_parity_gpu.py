@@ -809,7 +809,7 @@ def poison_before_window(inp, W):
 
 @pytest.mark.parametrize("variant", VARIANTS_W)
 @pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 16), (256, 8, 2, 32), (128, 64, 8, 16),
-                                        (128, 16, 4, 7)])
+                                        (128, 16, 4, 7), (128, 16, 8, 64), (256, 8, 2, 256)])
 def test_window_parity_poisoned(variant, D, Hq, Hkv, P):
     """Windows of 1 token to beyond the longest sequence, every row before a
     window set to NaN, lengths on and off tile and page boundaries."""
