@@ -847,7 +847,7 @@ def test_window_long_context_all_rows(variant, long_ctx):
 
 
 # ------------------------------------------------------------------ KV-cache append
-@pytest.mark.parametrize("D,Hkv,P", [(128, 8, 16), (256, 2, 32), (128, 4, 7), (64, 8, 1)])
+@pytest.mark.parametrize("D,Hkv,P", [(128, 8, 16), (256, 2, 32), (128, 4, 7), (64, 8, 1), (128, 8, 256)])
 def test_append_matches_oracle_bitwise(D, Hkv, P):
     """The whole K and V pools after the append equal the oracle's, bit for
     bit: the newest token's rows land in their slots and nothing else moves.
