@@ -65,13 +65,14 @@ def knobs(variant, tokens):
     return [dict(partition_tokens=T) for T in tokens]
 
 
-def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0, out_dtype=None, workspace=None):
+def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0, out_dtype=None, workspace=None,
+            scale=None):
     kernel, schedule = _MODE[variant]
     merge = _MERGE.get(variant, "kernel")
     q, k, v = d.call(call)
     out = torch.full(q.shape, float("nan"), dtype=out_dtype or q.dtype, device=q.device)   # every row must be written
     pa.pa_reset_stats()
-    pa.decode(q, k, v, d.block_tables, d.context_lens, d.w.scale, out=out, variant=kernel,
+    pa.decode(q, k, v, d.block_tables, d.context_lens, d.w.scale if scale is None else scale, out=out, variant=kernel,
               partition_tokens=partition_tokens, schedule=schedule, shares=shares, window=window,
               merge=merge if kernel == "mfma" and schedule != "balanced" else "auto", workspace=workspace)
     torch.cuda.synchronize()
@@ -93,9 +94,9 @@ def gpu_run(d, call=0, variant="valu", partition_tokens=0, shares=0, window=0, o
     return host_out(out), s
 
 
-def oracle_run(inp, call=0, window=0):
+def oracle_run(inp, call=0, window=0, scale=None):
     q, k, v = inp.call(call)
-    return oracle.attention(q, k, v, inp.block_tables, inp.context_lens, inp.w.scale,
+    return oracle.attention(q, k, v, inp.block_tables, inp.context_lens, inp.w.scale if scale is None else scale,
                             inp.w.num_kv_heads, window=window)
 
 
@@ -274,6 +275,24 @@ def test_large_pages_poisoned(D, Hq, Hkv, P, variant):
 
 
 # ------------------------------------------------------------------ exactness
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_scale_sweep(variant):
+    """Logit scales from a nearly flat to a nearly one-hot softmax, and a
+    negative one, over keys with 2% of rows x4: the lazy rescale, the
+    weights' hi + lo split at weights far above 1, and merges of partitions
+    whose maxima lie far apart all stay within the bar."""
+    w = custom(batch=5, num_q_heads=16, num_kv_heads=8, head_dim=128, page_size=16,
+               ctx=(1, 100, 700, 2000, 5000), spike_frac=0.02)
+    inp = make_inputs(w, seed=33)
+    d = to_device(inp)
+    for f in (1e-3, 0.25, 4.0, 16.0, 64.0, -2.0):
+        sc = float(np.float32(w.scale * f))
+        ref = oracle_run(inp, scale=sc)
+        for kn in knobs(variant, (0, 64)):
+            y, _ = gpu_run(d, variant=variant, scale=sc, **kn)
+            assert_parity(y, ref, f"scale x{f} {kn}")
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_ctx1_returns_v_row_bitwise(variant):
     w = custom(batch=5, num_q_heads=16, num_kv_heads=8, head_dim=128, page_size=32,
