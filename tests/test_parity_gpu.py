@@ -1070,12 +1070,12 @@ def to_torch(a):
     return torch.from_numpy(a).cuda()
 
 
-def prefill_run(d, q, qs, out_dtype=None, **kw):
+def prefill_run(d, q, qs, out_dtype=None, scale=None, **kw):
     qd = to_torch(q)
     out = torch.full(qd.shape, float("nan"), dtype=out_dtype or qd.dtype, device="cuda")
     pa.pa_reset_stats()
     pa.prefill(qd, d.k[0], d.v[0], d.block_tables, d.context_lens, torch.from_numpy(qs).cuda(),
-               d.w.scale, out=out, **kw)
+               d.w.scale if scale is None else scale, out=out, **kw)
     torch.cuda.synchronize()
     s = pa.pa_get_stats()
     assert s["prefill_launches"] == 1, s
@@ -1091,9 +1091,9 @@ def prefill_run(d, q, qs, out_dtype=None, **kw):
 PREFILL_SCHEDULES = [("partitions", 0), ("partitions", 64), ("partitions", 1 << 20), ("staged", 0)]
 
 
-def oracle_queries(inp, q, qs, window=0):
+def oracle_queries(inp, q, qs, window=0, scale=None):
     return oracle.attention_queries(q, inp.k[0], inp.v[0], inp.block_tables, inp.context_lens, qs,
-                                    inp.w.scale, inp.w.num_kv_heads, window=window)
+                                    inp.w.scale if scale is None else scale, inp.w.num_kv_heads, window=window)
 
 
 @pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 16, 8, 16), (128, 32, 2, 16), (256, 8, 2, 32),
@@ -1114,6 +1114,22 @@ def test_prefill_parity(D, Hq, Hkv, P):
             y, s = prefill_run(d, q, qs, window=W, partition_tokens=T, schedule=sched)
             assert_parity(y, ref, f"prefill D={D} Hq={Hq} Hkv={Hkv} P={P} W={W} {sched} T={T} "
                                   f"(x{s['last_num_partitions']})")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_scale_sweep(D):
+    """Several queries per sequence over logit scales from nearly flat to
+    nearly one-hot, and a negative one: the staged kernel's lazy rescale and
+    weight split, and the per-block kernel's, split and unsplit."""
+    Hq, Hkv = (16, 8) if D == 128 else (8, 2)
+    inp, q, qs = queries_case((1, 17, 300, 1000, 2500), (1, 17, 64, 100, 200), Hq, Hkv, D, 16, seed=D + 5)
+    d = to_device(inp)
+    for f in (1e-3, 4.0, 16.0, 64.0, -2.0):
+        sc = float(np.float32(inp.w.scale * f))
+        ref = oracle_queries(inp, q, qs, scale=sc)
+        for sched, T in PREFILL_SCHEDULES:
+            y, _ = prefill_run(d, q, qs, scale=sc, partition_tokens=T, schedule=sched)
+            assert_parity(y, ref, f"prefill D={D} scale x{f} {sched} T={T}")
 
 
 @pytest.mark.parametrize("Hq,Hkv,P,kt", [(8, 2, 16, "bf16"), (16, 16, 32, "bf16"), (16, 1, 7, "bf16"),
